@@ -1,0 +1,86 @@
+"""Newton-Schulz orthogonalisation with NVFP4 operands (oracle; test
+infrastructure only).
+
+[FS4 §2.3]: the Root/Muon optimizer's Newton-Schulz matrix products run
+directly on NVFP4 operands rather than on a mixed-precision path.  The pages
+tune (a, b, c) per aspect ratio and clip at the 99th percentile but print
+neither; this oracle takes the fixed quintic used by Muon,
+(a, b, c) = (3.4445, -4.7750, 2.0315), and no clipping.
+
+Iteration on X [m, n], m <= n:
+
+    X_0     = G / (||G||_F + eps)                   (eps = 1e-7)
+    A       = Q(X) Q(X)^T                           X row-wise (blocks along n)
+    B       = b A + c Q(A) Q(A^T)^T                 A row- and column-wise
+    X_next  = a X + Q(B) Q(X^T)^T                   B row-wise, X column-wise
+
+Reading: the state X and the products A, B are float32 tensors (they are the
+operands the quantizer sees); every GEMM is exact in float64 over the
+dequantized operands and then rounded to float32; only GEMM operands are
+quantized (b A and a X use the float32 values).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .linear import gemm_nt, gemm_nt_abs
+from .quantize import quantize
+
+MUON_ABC = (3.4445, -4.7750, 2.0315)
+NS_EPS = 1e-7
+
+
+def ns_normalize(g, eps: float = NS_EPS):
+    """X_0 = G / (||G||_F + eps), Frobenius norm in float64, X_0 rounded to
+    float32.  Returns (X_0 float32, X_0 float64)."""
+    g64 = np.asarray(g, dtype=np.float64)
+    x64 = g64 / (np.sqrt(np.sum(g64 * g64)) + eps)
+    return x64.astype(np.float32), x64
+
+
+def ns_step(x, a: float, b: float, c: float):
+    """One quantized Newton-Schulz step from float32 X.
+
+    Returns dict: A, B, X (float32 results), A64, B64, X64 (float64 before
+    rounding) and the error normalisers A_D, B_D, X_D.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    x_row, x_col, _ = quantize(x, rowwise=True, colwise=True)
+    a64 = gemm_nt(x_row, x_row)
+    a_d = gemm_nt_abs(x_row, x_row)
+    a32 = a64.astype(np.float32)
+    a_row, a_col, _ = quantize(a32, rowwise=True, colwise=True)
+    aa = gemm_nt(a_row, a_col)
+    b64 = b * a32.astype(np.float64) + c * aa
+    b_d = abs(b) * np.abs(a32.astype(np.float64)) + abs(c) * gemm_nt_abs(a_row, a_col)
+    b32 = b64.astype(np.float32)
+    b_row, _, _ = quantize(b32, rowwise=True, colwise=False)
+    bx = gemm_nt(b_row, x_col)
+    x64 = a * x.astype(np.float64) + bx
+    x_d = abs(a) * np.abs(x.astype(np.float64)) + gemm_nt_abs(b_row, x_col)
+    return {"A": a32, "A64": a64, "A_D": a_d, "B": b32, "B64": b64, "B_D": b_d,
+            "X": x64.astype(np.float32), "X64": x64, "X_D": x_d}
+
+
+def newton_schulz(g, steps: int = 5, abc=MUON_ABC, eps: float = NS_EPS, normalize: bool = True):
+    """Quantized NS from G.  Returns the list of float32 iterates X_0..X_steps
+    and the list of per-step dicts from ``ns_step``."""
+    a, b, c = abc
+    x0 = ns_normalize(g, eps)[0] if normalize else np.asarray(g, dtype=np.float32)
+    xs, steps_out = [x0], []
+    for _ in range(steps):
+        st = ns_step(xs[-1], a, b, c)
+        steps_out.append(st)
+        xs.append(st["X"])
+    return xs, steps_out
+
+
+def newton_schulz_fp64(g, steps: int = 5, abc=MUON_ABC, eps: float = NS_EPS):
+    """The same iteration without quantization, all in float64."""
+    a, b, c = abc
+    x = ns_normalize(g, eps)[1]
+    for _ in range(steps):
+        am = x @ x.T
+        bm = b * am + c * (am @ am)
+        x = a * x + bm @ x
+    return x

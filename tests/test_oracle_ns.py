@@ -1,0 +1,131 @@
+"""Pins for the oracle's Newton-Schulz iteration."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import exact as X
+from oracle.newton_schulz import MUON_ABC
+
+
+def _p(s, abc=MUON_ABC):
+    a, b, c = abc
+    return a * s + b * s ** 3 + c * s ** 5
+
+
+def test_unquantized_ns_matches_svd_closed_form():
+    rng = np.random.default_rng(0)
+    g = rng.standard_normal((48, 128))
+    uu, s, vt = np.linalg.svd(g / (np.linalg.norm(g) + 1e-7), full_matrices=False)
+    for steps in (1, 3, 5):
+        sig = s.copy()
+        for _ in range(steps):
+            sig = _p(sig)
+        want = (uu * sig) @ vt
+        got = oracle.newton_schulz_fp64(g, steps)
+        np.testing.assert_allclose(got, want, atol=1e-12 * np.abs(want).max())
+
+
+def test_quintic_band_for_the_normalised_gaussian_spectrum():
+    # A 3072 x 8192 Gaussian matrix divided by its Frobenius norm has singular
+    # values near [1/sqrt(m) - 1/sqrt(n), 1/sqrt(m) + 1/sqrt(n)] (Marchenko-
+    # Pastur edges); five quintic steps map that range (with finite-size slack)
+    # into about [0.68, 1.17].
+    m, n = 3072, 8192
+    lo, hi = 1 / np.sqrt(m) - 1 / np.sqrt(n), 1 / np.sqrt(m) + 1 / np.sqrt(n)
+    s = np.linspace(lo * 0.7, hi * 1.2, 20001)
+    for _ in range(5):
+        s = _p(s)
+    assert s.min() > 0.68 and s.max() < 1.17
+
+
+def test_unquantized_ns_spectrum_lands_in_band_at_reduced_size():
+    # same aspect ratio as the workload, smaller: check the fp64 oracle's
+    # iterate against the polynomial image of its own starting spectrum
+    g = synth.bf16_to_f32(synth.ns_input(seed=5, m=384, n=1024)).astype(np.float64)
+    s0 = np.linalg.svd(g / (np.linalg.norm(g) + 1e-7), compute_uv=False)
+    x5 = oracle.newton_schulz_fp64(g, 5)
+    s5 = np.sort(np.linalg.svd(x5, compute_uv=False))
+    want = np.sort(_p(_p(_p(_p(_p(s0))))))
+    np.testing.assert_allclose(s5, want, rtol=1e-10)
+
+
+def _exact_quantized_values(x):
+    """Exact rational values of the row-wise and column-wise quantization."""
+    rc, rs, cc, cs, s_t = X.quantize_exact(x)
+
+    def vals(codes, scales):
+        out = np.empty(codes.shape, dtype=object)
+        for r in range(codes.shape[0]):
+            for k in range(codes.shape[1]):
+                c = int(codes[r, k])
+                mag = X.E2M1_MAGS[c & 7] * X.E4M3_FINITE[int(scales[r, k // 16])] * s_t
+                out[r, k] = -mag if c & 8 else mag
+        return out
+
+    return vals(rc, rs), vals(cc, cs)
+
+
+def _mm_nt(a, b):
+    out = np.empty((a.shape[0], b.shape[0]), dtype=object)
+    for i in range(a.shape[0]):
+        for j in range(b.shape[0]):
+            out[i, j] = sum((a[i, t] * b[j, t] for t in range(a.shape[1])), Fraction(0))
+    return out
+
+
+def _to_f32(arr):
+    return np.array([[float(X.round_to_f32(abs(v))) * (1 if v >= 0 else -1) for v in row] for row in arr],
+                    dtype=np.float32)
+
+
+def test_quantized_ns_step_matches_rational_brute_force():
+    a, b, c = MUON_ABC
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((16, 32)) * 0.05).astype(np.float32)
+    st = oracle.ns_step(x, a, b, c)
+    xr, xc = _exact_quantized_values(x)
+    A = _mm_nt(xr, xr)                                   # Q(X) Q(X)^T
+    A32 = _to_f32(A)
+    np.testing.assert_array_equal(st["A"], A32)
+    ar, ac = _exact_quantized_values(A32)
+    AA = _mm_nt(ar, ac)                                   # Q(A) Q(A^T)^T
+    fb, fc = Fraction(b), Fraction(c)
+    B = np.array([[fb * Fraction(float(A32[i, j])) + fc * AA[i, j] for j in range(16)] for i in range(16)],
+                 dtype=object)
+    B32 = _to_f32(B)
+    np.testing.assert_array_equal(st["B"], B32)
+    br, _ = _exact_quantized_values(B32)
+    BX = _mm_nt(br, xc)                                   # Q(B) Q(X^T)^T
+    fa = Fraction(a)
+    Xn = np.array([[fa * Fraction(float(x[i, j])) + BX[i, j] for j in range(32)] for i in range(16)],
+                  dtype=object)
+    np.testing.assert_array_equal(st["X"], _to_f32(Xn))
+
+
+def test_quantized_ns_step_noise_is_quantization_sized():
+    # One quantized step from a given iterate differs from the exact step by
+    # the NVFP4 noise of its three products (~7-10% per product, Frobenius).
+    # While |aX| dominates |BX| (the first steps of a Gaussian start) that noise
+    # is diluted; later steps cancel aX against BX and amplify it, which is the
+    # error growth the pages attribute to naive NVFP4 Newton-Schulz.
+    a, b, c = MUON_ABC
+    g = synth.bf16_to_f32(synth.ns_input(seed=5, m=384, n=1024))
+    xs, steps = oracle.newton_schulz(g, 2)
+    for k, bound in ((0, 0.005), (1, 0.03)):
+        x = xs[k].astype(np.float64)
+        am = x @ x.T
+        want = a * x + (b * am + c * am @ am) @ x
+        rel = np.linalg.norm(steps[k]["X64"] - want) / np.linalg.norm(want)
+        assert rel < bound, (k, rel)
+        rel_a = np.linalg.norm(steps[k]["A64"] - am) / np.linalg.norm(am)
+        assert 0.01 < rel_a < 0.15
+    assert np.linalg.norm(xs[0].astype(np.float64) - oracle.ns_normalize(g)[1]) < 1e-6
+
+
+def test_ns_normalize():
+    g = np.array([[3.0, 4.0]], dtype=np.float32)
+    x32, x64 = oracle.ns_normalize(g, eps=0.0)
+    np.testing.assert_allclose(x64, [[0.6, 0.8]], rtol=1e-15)
