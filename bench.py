@@ -1,0 +1,231 @@
+"""Benchmark of the NVFP4 linear-projection hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+
+One step is one pass of the whole hot path over one batch of synthetic input
+at the 3B-shape projection (X 8192 x 3072 bf16, W 8192 x 3072 with a rank-32
+BF16 LoRA-SVD part, dY 8192 x 8192 bf16):
+
+    quantize R (row- and column-wise)               weights change every step
+    forward:  quantize X, T = X V^T, Y = Q(X) Q(R)^T + T U^T
+    backward: quantize dY, P = dY U, dX = Q(dY) Q(R^T)^T + P V,
+              dW = Q(dY^T) Q(X^T)^T, dU = dY^T T, dV = P^T X
+
+Work counted per step: 1254.67 GFLOP (three 8192 x 8192 x 3072 block-scaled
+products plus the rank-32 products), the algorithmic count; quantization is
+timed but credited no FLOPs.  ``value`` is that work / measured step time, in
+TFLOP/s, with every input resident in HBM before the timed region.
+
+Extra fields: the dominant kernel's roofline (the block-scaled GEMM, timed
+with HIP events around its own launches at the three step shapes), the
+quantizer's HBM GB/s on the 4096 x 4096 workload (both layouts, inputs rotated
+through 12 copies so every call reads from HBM), the 5-step NVFP4
+Newton-Schulz on 3072 x 8192, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 linear fwd+bwd TFLOP/s and quantizer GB/s at 3B shapes, % of roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+M, K, N, R_RANK = 8192, 3072, 8192, 32
+
+
+def step_flops(m=M, k=K, n=N, r=R_RANK):
+    main = 3 * 2.0 * m * n * k
+    low = 2.0 * (m * k * r + m * r * n + m * n * r + m * r * k + n * m * r + r * m * k)
+    return main + low
+
+
+def quantizer_bytes(rows, cols, in_bytes=2):
+    # one read of the input, both layouts' codes and scales, the tensor scale
+    return rows * cols * in_bytes + 2 * (rows * cols // 2 + rows * cols // 16) + 4
+
+
+def ns_flops(m=3072, n=8192, steps=5):
+    per = 2.0 * m * m * n + 2.0 * m * m * m + 2.0 * m * m * n
+    return steps * per
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="skip the quantizer/NS/roofline legs")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def cpu_baseline():
+    """The oracle as it stands, on a bounded sample of the same workload: the
+    fwd+bwd of the 3B-shape projection restricted to the first 256 tokens
+    (X 256 x 3072, dY 256 x 8192, full W), TFLOP/s over the same algorithmic
+    FLOP count for that token count."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:   # pragma: no cover
+        threads = os.cpu_count()
+    d = synth.linear3b()
+    dy = synth.linear3b_dy()
+    ms = 256
+    x = synth.bf16_to_f32(d["X"][:ms])
+    u, v = synth.bf16_to_f32(d["U"]), synth.bf16_to_f32(d["V"])
+    t0 = time.perf_counter()
+    r_row, r_col, _ = oracle.quantize(d["R"])
+    fwd = oracle.linear_fwd(x, r_row, u, v)
+    oracle.linear_bwd(synth.bf16_to_f32(dy[:ms]), x, r_col, u, v, fwd["T64"], x_col=fwd["X_col"])
+    dt = time.perf_counter() - t0
+    fl = step_flops(m=ms)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "fwd+bwd of the 3B-shape projection on the first %d of 8192 tokens "
+                      "(full 8192x3072 weight quantized both ways), %.1f s" % (ms, dt)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU; this build has no multi-GPU path (--gpus %d requested)" % a.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import precision_pretraining_amd as fs4
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    d = synth.linear3b()
+    X, U, V = to_bf16(d["X"]), to_bf16(d["U"]), to_bf16(d["V"])
+    Rw = torch.from_numpy(d["R"]).to(dev)
+    dY = to_bf16(synth.linear3b_dy())
+    r = U.shape[1]
+
+    # preallocated views/outputs so the step allocates nothing
+    R_row = fs4.NVFP4.empty(N, K, dev)
+    R_col = fs4.NVFP4.empty(K, N, dev, R_row.tscale)
+
+    def step():
+        fs4.quantize(Rw, out_row=R_row, out_col=R_col)
+        f = fs4.linear_fwd(X, R_row, U, V)
+        b = fs4.linear_bwd(dY, X, f.X_col, R_col, U, V, f.T)
+        return f, b
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(a.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / a.steps
+    value = step_flops() / (ms_step * 1e-3) / 1e12
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "3B-shape NVFP4 LoRA-SVD linear fwd+bwd: X 8192x3072 bf16, "
+                                  "W 8192x3072 (rank-32 bf16 factors + NVFP4 residual), dY 8192x8192 bf16",
+                      "tokens": M, "in_features": K, "out_features": N, "rank": r,
+                      "step_gflop": round(step_flops() / 1e9, 2)},
+           "step_frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)}
+
+    if not a.no_extra:
+        # ---- dominant kernel: block-scaled GEMM at the three step shapes ----
+        X_row, X_col = fs4.quantize(X)
+        dY_row, dY_col = fs4.quantize(dY)
+        shapes = [(X_row, R_row), (dY_row, R_col), (dY_col, X_col)]
+        Cs = [torch.empty((A.rows, B.rows), dtype=torch.float32, device=dev) for A, B in shapes]
+        for (A, B), C in zip(shapes, Cs):
+            fs4.gemm_nt(A, B, out=C)
+        torch.cuda.synchronize()
+        reps = max(3, a.steps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * 3)]
+        i = 0
+        for _ in range(reps):
+            for (A, B), C in zip(shapes, Cs):
+                ev[i][0].record(stream)
+                fs4.gemm_nt(A, B, out=C)
+                ev[i][1].record(stream)
+                i += 1
+        torch.cuda.synchronize()
+        durs = [s.elapsed_time(e) for s, e in ev]
+        gemm_ms = float(np.mean(durs))
+        gemm_flop = 2.0 * M * N * K
+        ach = gemm_flop / (gemm_ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": "gemm_nt_kernel (block-scaled NVFP4 NT GEMM)",
+                           "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "per_launch": "8192x8192x3072 = %.1f GFLOP" % (gemm_flop / 1e9),
+                           "avg_launch_ms": round(gemm_ms, 4)}
+
+        # ---- quantizer on the 4096 x 4096 workload ---------------------------
+        qb = synth.quantizer_input()
+        copies = [to_bf16(qb) for _ in range(12)]
+        rows_q, cols_q = qb.shape
+        qrow = fs4.NVFP4.empty(rows_q, cols_q, dev)
+        qcol = fs4.NVFP4.empty(cols_q, rows_q, dev, qrow.tscale)
+        for c in copies[:3]:
+            fs4.quantize(c, out_row=qrow, out_col=qcol)
+        torch.cuda.synchronize()
+        qreps = 48
+        qe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(qreps)]
+        for j in range(qreps):
+            qe[j][0].record(stream)
+            fs4.quantize(copies[j % len(copies)], out_row=qrow, out_col=qcol)
+            qe[j][1].record(stream)
+        torch.cuda.synchronize()
+        q_ms = float(np.mean([s.elapsed_time(e) for s, e in qe]))
+        q_gbs = quantizer_bytes(rows_q, cols_q) / (q_ms * 1e-3) / 1e9
+        out["quantizer"] = {"workload": "4096x4096 bf16 ~N(0,1), 0.1% x50; row+col layouts",
+                            "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(q_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(q_ms * 1e3, 2),
+                            "bytes_per_call": quantizer_bytes(rows_q, cols_q)}
+        del copies
+
+        # ---- NVFP4 Newton-Schulz, 3072 x 8192, 5 steps ------------------------
+        G = to_bf16(synth.ns_input())
+        Xns = torch.empty((3072, 8192), dtype=torch.float32, device=dev)
+        fs4.newton_schulz(G, steps=5, out=Xns)
+        torch.cuda.synchronize()
+        nreps = 5
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(nreps):
+            fs4.newton_schulz(G, steps=5, out=Xns)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        ns_ms = s0.elapsed_time(s1) / nreps
+        ns_tf = ns_flops() / (ns_ms * 1e-3) / 1e12
+        out["newton_schulz"] = {"workload": "G 3072x8192 bf16 ~N(0,1), 5 quintic steps, all GEMM operands NVFP4",
+                                "achieved": round(ns_tf, 2), "unit": "TFLOP/s",
+                                "frac": round(ns_tf / PEAK_BF16_TFLOPS, 4), "ms_per_call": round(ns_ms, 4)}
+
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

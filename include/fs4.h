@@ -1,0 +1,187 @@
+/*
+ * fs4.h — C ABI of libfs4: the NVFP4-quantized linear projection of
+ * Full-Stack FP4 on AMD MI355X (gfx950).
+ *
+ * Citation key: [FS4 §n] = "Full-Stack FP4: Stable LLM Pretraining with
+ * Quantized Projections, Optimizers, and Attention" (arXiv 2607.04422),
+ * technical summary on gist.science (Spanish and French editions), section n.
+ *
+ * The pages name NVFP4 without defining it; this library implements the
+ * two-level block format:
+ *   - E2M1 element codes, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}, bit 3 = sign;
+ *   - one E4M3 (FN) decode scale per 16 consecutive elements along the
+ *     contraction dimension;
+ *   - one FP32 decode scale per tensor, s_t = RNE_fp32(amax / 2688);
+ *   - s_b = E4M3 round-to-nearest-even (satfinite) of amax_b / (6 s_t);
+ *   - code = sign | E2M1 round-to-nearest-even of |x| / (s_b s_t), the
+ *     division exact, ties to the even code; the signed zero when s_b s_t = 0;
+ *   - x_hat = e2m1(code) * e4m3(s_b) * s_t.
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless a comment says otherwise; the caller
+ *     owns every buffer.  The library never allocates, frees, synchronises or
+ *     copies to the host; every call is asynchronous on `stream` (a
+ *     hipStream_t; NULL = the null stream).
+ *   - All arguments are validated on the host BEFORE anything is launched; on
+ *     an error status nothing was launched and no output was touched.  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Dimensions are element counts.  Every dimension that is blocked in some
+ *     quantized view must be a positive multiple of 16 (FS4_ERR_SHAPE).
+ *     Device pointers must be 16-byte aligned (FS4_ERR_ALIGN).
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified outputs.
+ *   - `ws` is a caller-provided device workspace of at least the size the
+ *     matching fs4_*_workspace_bytes() call returns (256-byte aligned).
+ *   - Calls are reentrant; calls that share a workspace or an output buffer
+ *     must be ordered on one stream.
+ */
+#ifndef FS4_H
+#define FS4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FS4_OK = 0,
+  FS4_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  FS4_ERR_SHAPE = 2,     /* a dimension is negative, not a multiple of 16, or
+                            views/buffers disagree on a dimension                */
+  FS4_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned            */
+  FS4_ERR_DTYPE = 4,     /* unknown fs4_dtype                                  */
+  FS4_ERR_RANK = 5,      /* low-rank r outside [0, 64], or U/V NULL with r > 0  */
+  FS4_ERR_WORKSPACE = 6, /* ws_bytes smaller than required                     */
+  FS4_ERR_HIP = 7,       /* a kernel launch failed                              */
+  FS4_ERR_ARG = 8        /* another argument is out of range (e.g. steps < 0)  */
+} fs4_status;
+
+typedef enum { FS4_BF16 = 0, FS4_FP32 = 1 } fs4_dtype;
+
+/* One NVFP4 view of a [rows][cols] tensor; cols is the blocked (contraction)
+ * dimension and is contiguous.
+ *   codes  [rows][cols/2]   byte j of a row = code[2j] | code[2j+1] << 4
+ *   scales [rows][cols/16]  raw E4M3FN block decode scales
+ *   tscale 1 float          the FP32 tensor decode scale (on the device)
+ * A "row-wise" view of x[R][C] has rows = R, cols = C.  A "column-wise" view
+ * of x has rows = C, cols = R: the row-wise quantization of x^T (different
+ * blocks, so a different quantization) with the same tensor scale. */
+typedef struct {
+  uint8_t *codes;
+  uint8_t *scales;
+  float *tscale;
+  int64_t rows;
+  int64_t cols;
+} fs4_nvfp4;
+
+/* ---------------------------------------------------------------------------
+ * fs4_quantize — two-level NVFP4 quantization of x[rows][cols] (bf16 or fp32,
+ * row-major), emitting the row-wise view, the column-wise view, or both, with
+ * one shared tensor scale.  [FS4 §2.1] (residual held in NVFP4), [FS4 §2.3]
+ * (Newton-Schulz operands in NVFP4).
+ *   rowwise:  rows = rows, cols = cols (cols % 16 == 0), or NULL
+ *   colwise:  rows = cols, cols = rows (rows % 16 == 0), or NULL
+ * At least one view must be given.  Both views' tscale receive s_t (they may
+ * point to the same float).  rows == 0 or cols == 0 writes s_t = 0 only.
+ * Codes and scales are bit-exact with the definition in the file header.
+ */
+size_t fs4_quantize_workspace_bytes(int64_t rows, int64_t cols);
+fs4_status fs4_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
+                        const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * fs4_gemm_nt — C[M][N] = alpha * s_tA * s_tB * sum_k A_hat[m,k] B_hat[n,k]
+ *                         + beta_e * E[M][N]            (E nullable)
+ * The block-scaled NT product that every linear and Newton-Schulz product
+ * reduces to.  A: view with rows = M, cols = K; B: view with rows = N,
+ * cols = K.  C, E fp32 row-major (leading dimension N); C may equal E.
+ * Products of the expanded operands are exact and accumulate in fp32.
+ */
+size_t fs4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+fs4_status fs4_gemm_nt(const fs4_nvfp4 *A, const fs4_nvfp4 *B, float alpha,
+                       const float *E, float beta_e, float *C,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * fs4_linear_fwd — LoRA-SVD projection forward, [FS4 §2.1]: the weight is
+ * W = R + beta U V with U = L2 [N][r], V = L1 [r][K] kept in BF16 and the
+ * residual R held in NVFP4:
+ *     Y = Q(X) Q(R)^T + beta (X V^T) U^T
+ *   X       bf16 [M][K] (M, K multiples of 16)
+ *   R_row   NVFP4 view of R: rows = N, cols = K (from fs4_quantize)
+ *   U       bf16 [N][r];  V  bf16 [r][K];  0 <= r <= 64 (r = 0: plain NVFP4)
+ *   Y       fp32 [M][N]
+ *   T_save  fp32 [M][r] receives X V^T (needed by the backward), nullable
+ *   X_col_save  column-wise view of X (rows = K, cols = M) for the backward,
+ *           nullable; its tscale receives X's tensor scale.
+ * The low-rank term uses the unquantized BF16 X.
+ */
+size_t fs4_linear_fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int r);
+fs4_status fs4_linear_fwd(const void *X, int64_t M, int64_t K, const fs4_nvfp4 *R_row,
+                          const void *U, const void *V, int r, float beta,
+                          float *Y, float *T_save, const fs4_nvfp4 *X_col_save,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * fs4_linear_bwd — LoRA-SVD projection backward, [FS4 §2.1], each product
+ * re-quantized along its own contraction dimension:
+ *     dX = Q(dY) Q(R^T)^T + beta (dY U) V     dY blocked along N
+ *     dW = Q(dY^T) Q(X^T)^T                   both blocked along M
+ *     dU = beta dY^T T,  dV = beta (dY U)^T X
+ *   dY      bf16 [M][N]
+ *   X       bf16 [M][K]        (for dV; may be NULL when dV is NULL or r = 0)
+ *   X_col   column-wise view of X: rows = K, cols = M (from the forward)
+ *   R_col   column-wise view of R: rows = K, cols = N (from fs4_quantize)
+ *   U, V, r, beta as in the forward;  T fp32 [M][r] = X V^T (forward's T_save)
+ *   dX fp32 [M][K];  dW fp32 [N][K] (gradient of the full weight; the update
+ *   of the NVFP4 residual);  dU fp32 [N][r], dV fp32 [r][K] (nullable).
+ * The pages' Cholesky-QR constraint on the low-rank update is not applied.
+ */
+size_t fs4_linear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
+fs4_status fs4_linear_bwd(const void *dY, int64_t M, int64_t N, int64_t K,
+                          const void *X, const fs4_nvfp4 *X_col, const fs4_nvfp4 *R_col,
+                          const void *U, const void *V, int r, float beta, const float *T,
+                          float *dX, float *dW, float *dU, float *dV,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * fs4_newton_schulz — Newton-Schulz orthogonalisation with every GEMM operand
+ * in NVFP4, [FS4 §2.3]:
+ *     X_0 = G / (||G||_F + eps)          (normalize != 0; else X_0 = G)
+ *     repeat `steps` times:
+ *       A = Q(X) Q(X)^T;  B = b A + c Q(A) Q(A^T)^T;  X <- a X + Q(B) Q(X^T)^T
+ *   G       [m][n], bf16 or fp32 (dt), m <= n, both multiples of 16
+ *   X_out   fp32 [m][n]: X_steps
+ *   trace_X fp32 [steps+1][m][n]: X_0..X_steps, nullable
+ *   trace_A, trace_B fp32 [steps][m][m]: each step's A and B, nullable
+ * The Frobenius norm is accumulated in fp64.  steps >= 0.
+ */
+size_t fs4_newton_schulz_workspace_bytes(int64_t m, int64_t n);
+fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, int steps,
+                             float a, float b, float c, int normalize, float eps,
+                             float *X_out, float *trace_X, float *trace_A, float *trace_B,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace size for any of the calls above, dispatched on the operation:
+ *   FS4_OP_QUANTIZE   d0 = rows, d1 = cols
+ *   FS4_OP_GEMM       d0 = M, d1 = N, d2 = K
+ *   FS4_OP_LINEAR_FWD d0 = M, d1 = K, d2 = N, r
+ *   FS4_OP_LINEAR_BWD d0 = M, d1 = N, d2 = K, r
+ *   FS4_OP_NS         d0 = m, d1 = n
+ * Returns 0 for an unknown op. */
+typedef enum { FS4_OP_QUANTIZE = 0, FS4_OP_GEMM = 1, FS4_OP_LINEAR_FWD = 2,
+               FS4_OP_LINEAR_BWD = 3, FS4_OP_NS = 4 } fs4_op;
+size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r);
+
+/* Human-readable name of a status code (static storage). */
+const char *fs4_status_str(fs4_status s);
+
+/* Library version string, e.g. "fs4 0.1 gfx950" (static storage). */
+const char *fs4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FS4_H */

@@ -1,0 +1,277 @@
+"""Python binding of libfs4, the MI355X (gfx950) NVFP4 linear-projection
+library of Full-Stack FP4.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libfs4.so.  PyTorch provides device memory and the current stream.  The
+library must have been built (``python -m precision_pretraining_amd.build``);
+importing this package without it raises ImportError.
+
+Names follow the C ABI in include/fs4.h:
+
+    quantize(x, rowwise=True, colwise=True)   -> (row view, col view)
+    gemm_nt(A, B, alpha, E, beta_e)           -> C
+    linear_fwd(X, R_row, U, V, beta)          -> LinearFwd(Y, T, X_col)
+    linear_bwd(dY, X, X_col, R_col, U, V, T)  -> LinearBwd(dX, dW, dU, dV)
+    newton_schulz(G, steps, abc, ...)         -> X (and traces)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfs4.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libfs4.so is not built; run `python -m precision_pretraining_amd.build` "
+                      "(expected at %s)" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+FS4_BF16, FS4_FP32 = 0, 1
+FS4_OP_QUANTIZE, FS4_OP_GEMM, FS4_OP_LINEAR_FWD, FS4_OP_LINEAR_BWD, FS4_OP_NS = range(5)
+MUON_ABC = (3.4445, -4.7750, 2.0315)
+
+EXPORTS = [
+    "fs4_quantize_workspace_bytes", "fs4_quantize", "fs4_gemm_workspace_bytes", "fs4_gemm_nt",
+    "fs4_linear_fwd_workspace_bytes", "fs4_linear_fwd", "fs4_linear_bwd_workspace_bytes",
+    "fs4_linear_bwd", "fs4_newton_schulz_workspace_bytes", "fs4_newton_schulz",
+    "fs4_workspace_bytes", "fs4_status_str", "fs4_version",
+]
+
+
+class _View(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tscale", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_VP = ctypes.POINTER(_View)
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_sig("fs4_status_str", ctypes.c_char_p, [ctypes.c_int])
+_sig("fs4_version", ctypes.c_char_p, [])
+_sig("fs4_workspace_bytes", _SZ, [ctypes.c_int, _I64, _I64, _I64, ctypes.c_int])
+_sig("fs4_quantize_workspace_bytes", _SZ, [_I64, _I64])
+_sig("fs4_quantize", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _VP, _VP, _P, _SZ, _P])
+_sig("fs4_gemm_workspace_bytes", _SZ, [_I64, _I64, _I64])
+_sig("fs4_gemm_nt", ctypes.c_int, [_VP, _VP, _F, _P, _F, _P, _P, _SZ, _P])
+_sig("fs4_linear_fwd_workspace_bytes", _SZ, [_I64, _I64, _I64, ctypes.c_int])
+_sig("fs4_linear_fwd", ctypes.c_int, [_P, _I64, _I64, _VP, _P, _P, ctypes.c_int, _F, _P, _P, _VP,
+                                      _P, _SZ, _P])
+_sig("fs4_linear_bwd_workspace_bytes", _SZ, [_I64, _I64, _I64, ctypes.c_int])
+_sig("fs4_linear_bwd", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _VP, _VP, _P, _P, ctypes.c_int, _F,
+                                      _P, _P, _P, _P, _P, _P, _SZ, _P])
+_sig("fs4_newton_schulz_workspace_bytes", _SZ, [_I64, _I64])
+_sig("fs4_newton_schulz", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_int, _F, _F, _F,
+                                         ctypes.c_int, _F, _P, _P, _P, _P, _P, _SZ, _P])
+
+
+class FS4Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__("%s: %s" % (call, _lib.fs4_status_str(status).decode()))
+
+
+def _check(st: int, call: str):
+    if st != 0:
+        raise FS4Error(st, call)
+
+
+def version() -> str:
+    return _lib.fs4_version().decode()
+
+
+def status_str(st: int) -> str:
+    return _lib.fs4_status_str(st).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_WS = {}
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    """A cached device workspace (reused by calls ordered on one stream)."""
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+@dataclass
+class NVFP4:
+    """One NVFP4 view on the device: codes [rows, cols/2] uint8, scales
+    [rows, cols/16] uint8 (E4M3FN), tscale [1] float32; cols is the blocked
+    (contraction) dimension."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tscale: torch.Tensor
+    rows: int
+    cols: int
+
+    @staticmethod
+    def empty(rows: int, cols: int, device, tscale: Optional[torch.Tensor] = None) -> "NVFP4":
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=device)
+        ts = tscale if tscale is not None else torch.empty(1, dtype=torch.float32, device=device)
+        return NVFP4(codes, scales, ts, rows, cols)
+
+    def c(self) -> _View:
+        return _View(self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr(),
+                     self.rows, self.cols)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FS4_BF16
+    if t.dtype == torch.float32:
+        return FS4_FP32
+    raise TypeError("fs4 takes bfloat16 or float32 tensors, got %s" % t.dtype)
+
+
+def quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, out_row: Optional[NVFP4] = None,
+             out_col: Optional[NVFP4] = None):
+    """NVFP4-quantize a 2-D bf16/fp32 CUDA tensor; returns (row view, col view)
+    (None for a layout not asked for).  Both views share one tscale tensor."""
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("quantize takes a contiguous 2-D tensor")
+    rows, cols = x.shape
+    dev = x.device
+    ts = None
+    if rowwise and out_row is None:
+        out_row = NVFP4.empty(rows, cols, dev)
+        ts = out_row.tscale
+    if colwise and out_col is None:
+        out_col = NVFP4.empty(cols, rows, dev, ts)
+    rv = out_row.c() if rowwise else None
+    cv = out_col.c() if colwise else None
+    nbytes = _lib.fs4_quantize_workspace_bytes(rows, cols)
+    ws = _workspace(nbytes, dev)
+    _check(_lib.fs4_quantize(x.data_ptr(), _dtype_code(x), rows, cols,
+                             ctypes.byref(rv) if rv is not None else None,
+                             ctypes.byref(cv) if cv is not None else None,
+                             ws.data_ptr(), ws.numel(), _stream(dev)), "fs4_quantize")
+    return (out_row if rowwise else None), (out_col if colwise else None)
+
+
+def gemm_nt(A: NVFP4, B: NVFP4, alpha: float = 1.0, E: Optional[torch.Tensor] = None, beta_e: float = 0.0,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = alpha s_tA s_tB A_hat B_hat^T + beta_e E (fp32 [A.rows, B.rows])."""
+    dev = A.codes.device
+    C = out if out is not None else torch.empty((A.rows, B.rows), dtype=torch.float32, device=dev)
+    av, bv = A.c(), B.c()
+    _check(_lib.fs4_gemm_nt(ctypes.byref(av), ctypes.byref(bv), alpha, _ptr(E), beta_e, C.data_ptr(),
+                            None, 0, _stream(dev)), "fs4_gemm_nt")
+    return C
+
+
+@dataclass
+class LinearFwd:
+    Y: torch.Tensor
+    T: Optional[torch.Tensor]
+    X_col: Optional[NVFP4]
+
+
+def linear_fwd(X: torch.Tensor, R_row: NVFP4, U: Optional[torch.Tensor], V: Optional[torch.Tensor],
+               beta: float = 1.0, save_for_backward: bool = True, out: Optional[torch.Tensor] = None) -> LinearFwd:
+    """Y = Q(X) Q(R)^T + beta (X V^T) U^T.  X bf16 [M, K]; U bf16 [N, r]; V bf16 [r, K]."""
+    M, K = X.shape
+    N = R_row.rows
+    r = 0 if U is None else U.shape[1]
+    dev = X.device
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    T = torch.empty((M, r), dtype=torch.float32, device=dev) if (save_for_backward and r > 0) else None
+    X_col = NVFP4.empty(K, M, dev) if save_for_backward else None
+    rv = R_row.c()
+    xc = X_col.c() if X_col is not None else None
+    nbytes = _lib.fs4_linear_fwd_workspace_bytes(M, K, N, r)
+    ws = _workspace(nbytes, dev)
+    _check(_lib.fs4_linear_fwd(X.data_ptr(), M, K, ctypes.byref(rv), _ptr(U), _ptr(V), r, beta,
+                               Y.data_ptr(), _ptr(T), ctypes.byref(xc) if xc is not None else None,
+                               ws.data_ptr(), ws.numel(), _stream(dev)), "fs4_linear_fwd")
+    return LinearFwd(Y, T, X_col)
+
+
+@dataclass
+class LinearBwd:
+    dX: torch.Tensor
+    dW: torch.Tensor
+    dU: Optional[torch.Tensor]
+    dV: Optional[torch.Tensor]
+
+
+def linear_bwd(dY: torch.Tensor, X: Optional[torch.Tensor], X_col: NVFP4, R_col: NVFP4,
+               U: Optional[torch.Tensor], V: Optional[torch.Tensor], T: Optional[torch.Tensor],
+               beta: float = 1.0, need_factor_grads: bool = True) -> LinearBwd:
+    """dX = Q(dY) Q(R^T)^T + beta (dY U) V; dW = Q(dY^T) Q(X^T)^T;
+    dU = beta dY^T T; dV = beta (dY U)^T X."""
+    M, N = dY.shape
+    K = X_col.rows
+    r = 0 if U is None else U.shape[1]
+    dev = dY.device
+    dX = torch.empty((M, K), dtype=torch.float32, device=dev)
+    dW = torch.empty((N, K), dtype=torch.float32, device=dev)
+    dU = torch.empty((N, r), dtype=torch.float32, device=dev) if (need_factor_grads and r > 0) else None
+    dV = torch.empty((r, K), dtype=torch.float32, device=dev) if (need_factor_grads and r > 0) else None
+    xc, rc = X_col.c(), R_col.c()
+    nbytes = _lib.fs4_linear_bwd_workspace_bytes(M, N, K, r)
+    ws = _workspace(nbytes, dev)
+    _check(_lib.fs4_linear_bwd(dY.data_ptr(), M, N, K, _ptr(X), ctypes.byref(xc), ctypes.byref(rc),
+                               _ptr(U), _ptr(V), r, beta, _ptr(T), dX.data_ptr(), dW.data_ptr(),
+                               _ptr(dU), _ptr(dV), ws.data_ptr(), ws.numel(), _stream(dev)),
+           "fs4_linear_bwd")
+    return LinearBwd(dX, dW, dU, dV)
+
+
+def newton_schulz(G: torch.Tensor, steps: int = 5, abc=MUON_ABC, normalize: bool = True, eps: float = 1e-7,
+                  trace: bool = False, out: Optional[torch.Tensor] = None):
+    """NVFP4 Newton-Schulz on G [m, n] (m <= n).  Returns X, or with
+    trace=True (X, trace_X [steps+1, m, n], trace_A [steps, m, m],
+    trace_B [steps, m, m])."""
+    m, n = G.shape
+    dev = G.device
+    X = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    tX = torch.empty((steps + 1, m, n), dtype=torch.float32, device=dev) if trace else None
+    tA = torch.empty((max(steps, 1), m, m), dtype=torch.float32, device=dev) if trace else None
+    tB = torch.empty((max(steps, 1), m, m), dtype=torch.float32, device=dev) if trace else None
+    a, b, c = abc
+    nbytes = _lib.fs4_newton_schulz_workspace_bytes(m, n)
+    ws = _workspace(nbytes, dev)
+    _check(_lib.fs4_newton_schulz(G.data_ptr(), _dtype_code(G), m, n, steps, a, b, c, int(normalize), eps,
+                                  X.data_ptr(), _ptr(tX), _ptr(tA), _ptr(tB), ws.data_ptr(), ws.numel(),
+                                  _stream(dev)), "fs4_newton_schulz")
+    if trace:
+        return X, tX, tA, tB
+    return X
+
+
+def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> int:
+    return _lib.fs4_workspace_bytes(op, d0, d1, d2, r)
+
+
+__all__ = ["NVFP4", "quantize", "gemm_nt", "linear_fwd", "LinearFwd", "linear_bwd", "LinearBwd",
+           "newton_schulz", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
+           "EXPORTS", "MUON_ABC"]

@@ -1,0 +1,346 @@
+// libfs4 C ABI: argument validation and orchestration of the HIP kernels.
+// Every check runs on the host before anything is launched.
+#include "fs4_common.h"
+
+using namespace fs4;
+
+namespace {
+
+inline hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+bool dim_ok(int64_t d) { return d > 0 && d % kBlock == 0; }
+
+fs4_status check_ptr(const void *p) {
+  if (!p) return FS4_ERR_NULL;
+  if (!aligned16(p)) return FS4_ERR_ALIGN;
+  return FS4_OK;
+}
+
+#define FS4_TRY(x)                      \
+  do {                                  \
+    fs4_status _st = (x);               \
+    if (_st != FS4_OK) return _st;      \
+  } while (0)
+
+// A view used as an input (must be fully valid) or an output of given shape.
+fs4_status check_view(const fs4_nvfp4 *v, int64_t rows, int64_t cols) {
+  if (!v) return FS4_ERR_NULL;
+  if (!v->codes || !v->scales || !v->tscale) return FS4_ERR_NULL;
+  if (!aligned16(v->codes) || !aligned16(v->scales) || ((uintptr_t)v->tscale & 3u))
+    return FS4_ERR_ALIGN;
+  if (v->rows != rows || v->cols != cols) return FS4_ERR_SHAPE;
+  if (cols % kBlock) return FS4_ERR_SHAPE;
+  return FS4_OK;
+}
+
+fs4_status check_ws(void *ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need) return FS4_ERR_WORKSPACE;
+  if (need > 0) {
+    if (!ws) return FS4_ERR_NULL;
+    if ((uintptr_t)ws & 255u) return FS4_ERR_ALIGN;
+  }
+  return FS4_OK;
+}
+
+// ---- workspace layouts -------------------------------------------------------
+struct FwdWs {
+  fs4_nvfp4 x_row;
+  uint32_t *qws;
+  float *T;
+  float *partials;
+};
+FwdWs carve_fwd(void *ws, int64_t M, int64_t K, int r, size_t *total) {
+  Carver c(ws);
+  FwdWs w;
+  w.x_row = carve_view(c, M, K);
+  w.qws = (uint32_t *)c.take(quantize_ws_bytes());
+  w.T = (float *)c.take((size_t)(M * (r > 0 ? r : 1)) * sizeof(float));
+  w.partials = (float *)c.take(small_gemm_partials_bytes(M, r > 0 ? r : 1, K));
+  if (total) *total = c.off;
+  return w;
+}
+
+struct BwdWs {
+  fs4_nvfp4 dy_row, dy_col;
+  uint32_t *qws;
+  float *P;
+  float *partials;
+};
+BwdWs carve_bwd(void *ws, int64_t M, int64_t N, int64_t K, int r, size_t *total) {
+  Carver c(ws);
+  BwdWs w;
+  w.dy_row = carve_view(c, M, N);
+  w.dy_col = carve_view(c, N, M);
+  w.qws = (uint32_t *)c.take(quantize_ws_bytes());
+  const int rr = r > 0 ? r : 1;
+  w.P = (float *)c.take((size_t)(M * rr) * sizeof(float));
+  size_t pb = small_gemm_partials_bytes(M, rr, N);
+  size_t p2 = small_gemm_partials_bytes(N, rr, M);
+  size_t p3 = small_gemm_partials_bytes(rr, K, M);
+  if (p2 > pb) pb = p2;
+  if (p3 > pb) pb = p3;
+  w.partials = (float *)c.take(pb);
+  if (total) *total = c.off;
+  return w;
+}
+
+struct NsWs {
+  float *X, *A, *B;
+  fs4_nvfp4 x_row, x_col, a_row, a_col, b_row;
+  uint32_t *qws;
+  void *nws;
+};
+NsWs carve_ns(void *ws, int64_t m, int64_t n, size_t *total) {
+  Carver c(ws);
+  NsWs w;
+  w.X = (float *)c.take((size_t)(m * n) * sizeof(float));
+  w.A = (float *)c.take((size_t)(m * m) * sizeof(float));
+  w.B = (float *)c.take((size_t)(m * m) * sizeof(float));
+  w.x_row = carve_view(c, m, n);
+  w.x_col = carve_view(c, n, m);
+  w.a_row = carve_view(c, m, m);
+  w.a_col = carve_view(c, m, m);
+  w.b_row = carve_view(c, m, m);
+  w.qws = (uint32_t *)c.take(quantize_ws_bytes());
+  w.nws = c.take(normalize_ws_bytes());
+  if (total) *total = c.off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *fs4_status_str(fs4_status s) {
+  switch (s) {
+    case FS4_OK: return "FS4_OK";
+    case FS4_ERR_NULL: return "FS4_ERR_NULL: a required pointer is NULL";
+    case FS4_ERR_SHAPE: return "FS4_ERR_SHAPE: bad or inconsistent dimension";
+    case FS4_ERR_ALIGN: return "FS4_ERR_ALIGN: device pointer not 16-byte aligned";
+    case FS4_ERR_DTYPE: return "FS4_ERR_DTYPE: unknown dtype";
+    case FS4_ERR_RANK: return "FS4_ERR_RANK: low-rank r out of range or factors missing";
+    case FS4_ERR_WORKSPACE: return "FS4_ERR_WORKSPACE: workspace too small";
+    case FS4_ERR_HIP: return "FS4_ERR_HIP: kernel launch failed";
+    case FS4_ERR_ARG: return "FS4_ERR_ARG: argument out of range";
+  }
+  return "FS4: unknown status";
+}
+
+const char *fs4_version(void) { return "fs4 0.1 gfx950"; }
+
+size_t fs4_quantize_workspace_bytes(int64_t, int64_t) { return quantize_ws_bytes(); }
+
+fs4_status fs4_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
+                        const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise, void *ws,
+                        size_t ws_bytes, void *stream) {
+  if (dt != FS4_BF16 && dt != FS4_FP32) return FS4_ERR_DTYPE;
+  if (rows < 0 || cols < 0) return FS4_ERR_SHAPE;
+  if (!rowwise && !colwise) return FS4_ERR_NULL;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty) FS4_TRY(check_ptr(x));
+  if (rowwise) {
+    if (empty) {
+      if (!rowwise->tscale) return FS4_ERR_NULL;
+    } else {
+      FS4_TRY(check_view(rowwise, rows, cols));
+    }
+  }
+  if (colwise) {
+    if (empty) {
+      if (!colwise->tscale) return FS4_ERR_NULL;
+    } else {
+      FS4_TRY(check_view(colwise, cols, rows));
+    }
+  }
+  FS4_TRY(check_ws(ws, ws_bytes, quantize_ws_bytes()));
+  return launch_quantize(x, dt, rows, cols, rowwise, colwise, ws, as_stream(stream));
+}
+
+size_t fs4_gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+fs4_status fs4_gemm_nt(const fs4_nvfp4 *A, const fs4_nvfp4 *B, float alpha, const float *E,
+                       float beta_e, float *C, void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!A || !B) return FS4_ERR_NULL;
+  if (A->rows < 0 || B->rows < 0 || A->cols < 0) return FS4_ERR_SHAPE;
+  if (A->cols != B->cols || A->cols % kBlock) return FS4_ERR_SHAPE;
+  FS4_TRY(check_view(A, A->rows, A->cols));
+  FS4_TRY(check_view(B, B->rows, B->cols));
+  FS4_TRY(check_ptr(C));
+  if (E && !aligned16(E)) return FS4_ERR_ALIGN;
+  return launch_gemm_nt(*A, *B, alpha, E, beta_e, C, LowRankEpilogue(), as_stream(stream));
+}
+
+size_t fs4_linear_fwd_workspace_bytes(int64_t M, int64_t K, int64_t, int r) {
+  size_t total = 0;
+  carve_fwd(nullptr, M, K, r, &total);
+  return total;
+}
+
+fs4_status fs4_linear_fwd(const void *X, int64_t M, int64_t K, const fs4_nvfp4 *R_row,
+                          const void *U, const void *V, int r, float beta, float *Y,
+                          float *T_save, const fs4_nvfp4 *X_col_save, void *ws, size_t ws_bytes,
+                          void *stream) {
+  if (!dim_ok(M) || !dim_ok(K)) return FS4_ERR_SHAPE;
+  FS4_TRY(check_ptr(X));
+  if (!R_row) return FS4_ERR_NULL;
+  const int64_t N = R_row->rows;
+  if (N <= 0) return FS4_ERR_SHAPE;
+  FS4_TRY(check_view(R_row, N, K));
+  if (r < 0 || r > kMaxRank) return FS4_ERR_RANK;
+  if (r > 0) {
+    if (!U || !V) return FS4_ERR_RANK;
+    FS4_TRY(check_ptr(U));
+    FS4_TRY(check_ptr(V));
+    if (T_save) FS4_TRY(check_ptr(T_save));
+  }
+  FS4_TRY(check_ptr(Y));
+  if (X_col_save) FS4_TRY(check_view(X_col_save, K, M));
+  size_t need = 0;
+  carve_fwd(nullptr, M, K, r, &need);
+  FS4_TRY(check_ws(ws, ws_bytes, need));
+
+  hipStream_t s = as_stream(stream);
+  FwdWs w = carve_fwd(ws, M, K, r, nullptr);
+  FS4_TRY(launch_quantize(X, FS4_BF16, M, K, &w.x_row, X_col_save, w.qws, s));
+  LowRankEpilogue lr;
+  if (r > 0) {
+    float *T = T_save ? T_save : w.T;
+    // T[m][j] = sum_k X[m][k] V[j][k]
+    FS4_TRY(launch_small_gemm(X, false, K, 1, V, false, K, 1, M, r, K, 1.0f, T, false,
+                              w.partials, s));
+    lr.L = T;
+    lr.R = (const uint16_t *)U;
+    lr.r = r;
+    lr.r_sn = r;
+    lr.r_sj = 1;
+    lr.l_scale = beta;
+  }
+  return launch_gemm_nt(w.x_row, *R_row, 1.0f, nullptr, 0.0f, Y, lr, s);
+}
+
+size_t fs4_linear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
+  size_t total = 0;
+  carve_bwd(nullptr, M, N, K, r, &total);
+  return total;
+}
+
+fs4_status fs4_linear_bwd(const void *dY, int64_t M, int64_t N, int64_t K, const void *X,
+                          const fs4_nvfp4 *X_col, const fs4_nvfp4 *R_col, const void *U,
+                          const void *V, int r, float beta, const float *T, float *dX, float *dW,
+                          float *dU, float *dV, void *ws, size_t ws_bytes, void *stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return FS4_ERR_SHAPE;
+  FS4_TRY(check_ptr(dY));
+  FS4_TRY(check_view(X_col, K, M));
+  FS4_TRY(check_view(R_col, K, N));
+  if (r < 0 || r > kMaxRank) return FS4_ERR_RANK;
+  if (r > 0) {
+    if (!U || !V || !T) return FS4_ERR_RANK;
+    FS4_TRY(check_ptr(U));
+    FS4_TRY(check_ptr(V));
+    FS4_TRY(check_ptr(T));
+    if (dU) FS4_TRY(check_ptr(dU));
+    if (dV) {
+      FS4_TRY(check_ptr(dV));
+      FS4_TRY(check_ptr(X));
+    }
+  }
+  FS4_TRY(check_ptr(dX));
+  FS4_TRY(check_ptr(dW));
+  size_t need = 0;
+  carve_bwd(nullptr, M, N, K, r, &need);
+  FS4_TRY(check_ws(ws, ws_bytes, need));
+
+  hipStream_t s = as_stream(stream);
+  BwdWs w = carve_bwd(ws, M, N, K, r, nullptr);
+  FS4_TRY(launch_quantize(dY, FS4_BF16, M, N, &w.dy_row, &w.dy_col, w.qws, s));
+  LowRankEpilogue lr;
+  if (r > 0) {
+    // P[m][j] = sum_n dY[m][n] U[n][j]
+    FS4_TRY(launch_small_gemm(dY, false, N, 1, U, false, 1, r, M, r, N, 1.0f, w.P, false,
+                              w.partials, s));
+    lr.L = w.P;
+    lr.R = (const uint16_t *)V;   // R(k, j) = V[j][k]
+    lr.r = r;
+    lr.r_sn = 1;
+    lr.r_sj = K;
+    lr.l_scale = beta;
+  }
+  FS4_TRY(launch_gemm_nt(w.dy_row, *R_col, 1.0f, nullptr, 0.0f, dX, lr, s));
+  FS4_TRY(launch_gemm_nt(w.dy_col, *X_col, 1.0f, nullptr, 0.0f, dW, LowRankEpilogue(), s));
+  if (r > 0 && dU) {
+    // dU[n][j] = beta sum_m dY[m][n] T[m][j]
+    FS4_TRY(launch_small_gemm(dY, false, 1, N, T, true, 1, r, N, r, M, beta, dU, false,
+                              w.partials, s));
+  }
+  if (r > 0 && dV) {
+    // dV[j][k] = beta sum_m P[m][j] X[m][k]
+    FS4_TRY(launch_small_gemm(w.P, true, 1, r, X, false, 1, K, r, K, M, beta, dV, false,
+                              w.partials, s));
+  }
+  return FS4_OK;
+}
+
+size_t fs4_newton_schulz_workspace_bytes(int64_t m, int64_t n) {
+  size_t total = 0;
+  carve_ns(nullptr, m, n, &total);
+  return total;
+}
+
+fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, int steps, float a,
+                             float b, float c, int normalize, float eps, float *X_out,
+                             float *trace_X, float *trace_A, float *trace_B, void *ws,
+                             size_t ws_bytes, void *stream) {
+  if (dt != FS4_BF16 && dt != FS4_FP32) return FS4_ERR_DTYPE;
+  if (!dim_ok(m) || !dim_ok(n) || m > n) return FS4_ERR_SHAPE;
+  if (steps < 0) return FS4_ERR_ARG;
+  FS4_TRY(check_ptr(G));
+  FS4_TRY(check_ptr(X_out));
+  if (trace_X) FS4_TRY(check_ptr(trace_X));
+  if (trace_A) FS4_TRY(check_ptr(trace_A));
+  if (trace_B) FS4_TRY(check_ptr(trace_B));
+  size_t need = 0;
+  carve_ns(nullptr, m, n, &need);
+  FS4_TRY(check_ws(ws, ws_bytes, need));
+
+  hipStream_t s = as_stream(stream);
+  NsWs w = carve_ns(ws, m, n, nullptr);
+  const int64_t mn = m * n, mm = m * m;
+  // iterate k lives in trace_X[k] when tracing, else alternates between X_out
+  // and the workspace so that the last one lands in X_out
+  auto slot = [&](int k) -> float * {
+    if (trace_X) return trace_X + (int64_t)k * mn;
+    return ((steps - k) % 2 == 0) ? X_out : w.X;
+  };
+  float *cur = slot(0);
+  if (normalize) FS4_TRY(launch_normalize(G, dt, mn, eps, cur, w.nws, s));
+  else FS4_TRY(launch_copy_f32(G, dt, mn, cur, s));
+  for (int k = 0; k < steps; ++k) {
+    float *A = trace_A ? trace_A + (int64_t)k * mm : w.A;
+    float *B = trace_B ? trace_B + (int64_t)k * mm : w.B;
+    float *next = slot(k + 1);
+    FS4_TRY(launch_quantize(cur, FS4_FP32, m, n, &w.x_row, &w.x_col, w.qws, s));
+    FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s));
+    FS4_TRY(launch_quantize(A, FS4_FP32, m, m, &w.a_row, &w.a_col, w.qws, s));
+    FS4_TRY(launch_gemm_nt(w.a_row, w.a_col, c, A, b, B, LowRankEpilogue(), s));
+    FS4_TRY(launch_quantize(B, FS4_FP32, m, m, &w.b_row, nullptr, w.qws, s));
+    FS4_TRY(launch_gemm_nt(w.b_row, w.x_col, 1.0f, cur, a, next, LowRankEpilogue(), s));
+    cur = next;
+  }
+  if (trace_X) FS4_TRY(launch_copy_f32(cur, FS4_FP32, mn, X_out, s));
+  return FS4_OK;
+}
+
+size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r) {
+  switch (op) {
+    case FS4_OP_QUANTIZE: return fs4_quantize_workspace_bytes(d0, d1);
+    case FS4_OP_GEMM: return fs4_gemm_workspace_bytes(d0, d1, d2);
+    case FS4_OP_LINEAR_FWD: return fs4_linear_fwd_workspace_bytes(d0, d1, d2, r);
+    case FS4_OP_LINEAR_BWD: return fs4_linear_bwd_workspace_bytes(d0, d1, d2, r);
+    case FS4_OP_NS: return fs4_newton_schulz_workspace_bytes(d0, d1);
+  }
+  return 0;
+}
+
+}  // extern "C"

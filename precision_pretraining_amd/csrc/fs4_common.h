@@ -1,0 +1,126 @@
+// Internal helpers shared by the libfs4 kernels (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fs4.h"
+
+namespace fs4 {
+
+constexpr int kBlock = 16;              // elements per E4M3 block scale
+constexpr double kTensorDiv = 2688.0;   // 6 (largest E2M1) * 448 (largest E4M3)
+constexpr int kMaxRank = 64;
+
+// ----------------------------------------------------------------------------
+// E4M3FN decode: exponent field 0 is subnormal (m * 2^-9), else
+// 2^(e-7) * (1 + m/8).  Only the finite codes 0..0x7E occur as block scales.
+__device__ __host__ inline float e4m3_to_float(uint32_t byte) {
+  const uint32_t e = (byte >> 3) & 0xFu, m = byte & 7u;
+  if (e == 0) return (float)m * 0.001953125f;            // m * 2^-9, exact
+  return __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+}
+
+// Round-to-nearest-even of q >= 0 onto the finite E4M3FN values, values from
+// 448 up saturating to 448 (code 0x7E).  q is an fp64 value whose side of
+// every E4M3 midpoint is the exact one (see the quantizer).
+__device__ inline uint32_t e4m3_rne_satfinite(double q) {
+  if (q >= 448.0) return 0x7Eu;
+  if (q < 0.015625) {                                    // below 2^-6: subnormal grid 2^-9
+    return (uint32_t)__builtin_rint(q * 512.0);          // 0..8; 8 is 2^-6 (code 0x08)
+  }
+  int e;
+  const double mant = __builtin_frexp(q, &e);            // q = mant * 2^e, mant in [0.5, 1)
+  // q = 2^(e-1) * (2 mant), 2 mant in [1, 2); mantissa field = round((2 mant - 1) * 8)
+  uint32_t m = (uint32_t)__builtin_rint((2.0 * mant - 1.0) * 8.0);
+  int eb = e - 1 + 7;                                    // biased exponent, 1..15
+  if (m == 8u) { m = 0u; ++eb; }
+  uint32_t code = ((uint32_t)eb << 3) | m;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// fp64 -> fp32 with directed rounding (x > 0 finite, within fp32 range).
+// The nearest-even conversion is off by at most one fp32 step, and for
+// non-negative floats the next representable value is the next bit pattern.
+__device__ inline float f32_round_up(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f) + 1u);
+  return f;
+}
+__device__ inline float f32_round_down(double x) {
+  float f = (float)x;
+  if ((double)f > x) f = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f) - 1u);
+  return f;
+}
+
+// bf16 raw bits <-> fp32
+__device__ inline float bf16_bits_to_float(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+__device__ inline uint32_t float_to_bf16_rne_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ----------------------------------------------------------------------------
+// Host-side helpers
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Carves 256-byte aligned sub-buffers out of a workspace (or just sizes them
+// when base == nullptr).
+struct Carver {
+  uint8_t *base;
+  size_t off = 0;
+  explicit Carver(void *b) : base((uint8_t *)b) {}
+  void *take(size_t bytes) {
+    void *p = base ? base + off : nullptr;
+    off += round_up(bytes ? bytes : 1, 256);
+    return p;
+  }
+};
+
+// An NVFP4 view living in a workspace.
+inline fs4_nvfp4 carve_view(Carver &c, int64_t rows, int64_t cols) {
+  fs4_nvfp4 v;
+  v.rows = rows;
+  v.cols = cols;
+  v.codes = (uint8_t *)c.take((size_t)(rows * cols / 2));
+  v.scales = (uint8_t *)c.take((size_t)(rows * cols / kBlock));
+  v.tscale = (float *)c.take(sizeof(float));
+  return v;
+}
+
+// ----------------------------------------------------------------------------
+// Launchers (defined in the .hip files)
+constexpr int kAmaxPartials = 1024;      // max partial maxima written by the amax pass
+size_t quantize_ws_bytes();
+fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
+                           const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
+                           void *ws, hipStream_t s);
+
+struct LowRankEpilogue {
+  const float *L = nullptr;     // fp32 [M][r], scaled by l_scale before use
+  const uint16_t *R = nullptr;  // bf16, element (n, j) at R[n * r_sn + j * r_sj]
+  int r = 0;
+  int64_t r_sn = 0, r_sj = 1;
+  float l_scale = 1.0f;
+};
+fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
+                          float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s);
+
+// out[a][b] = scale * sum_k P(a, k) Q(b, k) with P(a, k) = P[a*p_sa + k*p_sk],
+// Q(b, k) = Q[b*q_sb + k*q_sk]; each operand bf16 or fp32 (p_f32 / q_f32);
+// Kc a multiple of 16.  Written row-major [Na][Nb], or [Nb][Na] when
+// transpose_out.  `partials` needs small_gemm_partials_bytes(Na, Nb, Kc).
+size_t small_gemm_partials_bytes(int64_t Na, int64_t Nb, int64_t Kc);
+fs4_status launch_small_gemm(const void *P, bool p_f32, int64_t p_sa, int64_t p_sk, const void *Q,
+                             bool q_f32, int64_t q_sb, int64_t q_sk, int64_t Na, int64_t Nb,
+                             int64_t Kc, float scale, float *out, bool transpose_out,
+                             float *partials, hipStream_t s);
+// Frobenius normalisation X = G / (||G||_F + eps), fp64 accumulation
+size_t normalize_ws_bytes();
+fs4_status launch_normalize(const void *G, fs4_dtype dt, int64_t n, float eps, float *X,
+                            void *ws, hipStream_t s);
+fs4_status launch_copy_f32(const void *src, fs4_dtype dt, int64_t n, float *dst, hipStream_t s);
+
+}  // namespace fs4

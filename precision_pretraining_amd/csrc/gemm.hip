@@ -1,0 +1,368 @@
+// Block-scaled NVFP4 NT GEMM for gfx950 with a fused epilogue.
+//
+//   C[m][n] = alpha * s_tA * s_tB * sum_k A_hat[m][k] B_hat[n][k]
+//             + sum_j (l_scale * L[m][j]) R(n, j)            (low-rank term)
+//             + beta_e * E[m][n]
+//
+// A_hat = e2m1(code) * e4m3(s_b).  An E2M1 magnitude has <= 2 significant
+// bits and an E4M3 scale <= 4, so their product has <= 6 significant bits and
+// lies in [2^-10, 2688]: it is exact in FP16.  Packed codes are staged in LDS
+// as they sit in memory (4 bits per element) and expanded in registers right
+// before FP16 MFMA with fp32 accumulation:
+//   - write the scale as 2^E * F with F in [1, 2) (3 mantissa bits);
+//   - v_cvt_scalef32_pk_f16_fp4 turns two codes into two FP16 values times a
+//     power-of-two scale (the instruction takes only the exponent of its fp32
+//     scale operand, so 2^E is passed);
+//   - one packed FP16 multiply by F completes code * s_b, exactly.
+//
+// Full-Stack FP4 [FS4 §2.1] runs the projection GEMMs on NVFP4 operands while
+// the rank-r term stays in BF16: L = X V^T arrives in fp32, is split into BF16
+// hi + lo parts and runs as extra BF16 MFMA k-steps into the accumulators
+// after they have been scaled by alpha s_tA s_tB.
+//
+// Tiling: a workgroup of WM x WN waves computes (WM*TM*32) x (WN*TN*32) of C,
+// each wave TM x TN accumulators of v_mfma_f32_32x32x16_f16.  The k-tile is
+// 128 elements (64 code bytes and 8 scale bytes per row), double-buffered in
+// LDS with the next tile prefetched into registers while the current one is
+// multiplied.  Within a k-tile, lanes 0-31 of a wave take elements [0, 64)
+// and lanes 32-63 take [64, 128): MFMA k-step s uses elements 64h + 8s .. +8
+// for lane half h on both operands, so every step pairs equal k (the order of
+// summation over k is permuted, the set is not).
+//
+// Workgroups are ordered XCD-aware: the hardware deals workgroup ids round-
+// robin over the 8 XCDs, so ids are remapped to give each XCD a contiguous
+// run of tiles, walked in groups of rows so that concurrently running tiles
+// share A and B panels in that XCD's L2.
+#include <type_traits>
+
+#include "fs4_common.h"
+
+namespace fs4 {
+namespace {
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBK = 128;          // k-tile in elements
+constexpr int kRowBytes = 64;     // code bytes per row per k-tile
+constexpr int kLdsStride = 80;    // padded LDS row stride (conflict-free 16-byte reads)
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+struct GemmArgs {
+  const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
+  const float *a_ts, *b_ts;
+  int64_t M, N, K;
+  float alpha, beta_e, l_scale;
+  const float *E;
+  float *C;
+  const float *L;
+  const uint16_t *R;
+  int64_t r_sn, r_sj;
+  int r;
+};
+
+// E4M3 block scale -> (2^E as fp32, F as a pair of FP16) with s_b = 2^E F.
+struct ScalePair {
+  float pow2;
+  f16x2_t mant;
+};
+__device__ inline ScalePair split_scale(uint32_t byte) {
+  const uint32_t fb = __builtin_bit_cast(uint32_t, e4m3_to_float(byte));
+  ScalePair s;
+  s.pow2 = __builtin_bit_cast(float, fb & 0x7F800000u);    // 0 for a zero scale
+  const uint32_t h = 0x3C00u | (((fb >> 20) & 7u) << 7);    // FP16 1 + m/8
+  s.mant = __builtin_bit_cast(f16x2_t, h | (h << 16));
+  return s;
+}
+
+// Fills a 256-entry LDS table: entry b = {bits of 2^E, FP16 pair F} for the
+// E4M3 byte b (only 0..0x7E occur; the rest decode to something finite).
+__device__ inline void fill_scale_lut(uint2 *lut) {
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) {
+    const ScalePair p = split_scale((uint32_t)b & 0x7Fu);
+    lut[b] = make_uint2(__builtin_bit_cast(uint32_t, p.pow2), __builtin_bit_cast(uint32_t, p.mant));
+  }
+}
+__device__ inline ScalePair lut_scale(const uint2 *lut, uint32_t byte) {
+  const uint2 v = lut[byte];
+  ScalePair p;
+  p.pow2 = __builtin_bit_cast(float, v.x);
+  p.mant = __builtin_bit_cast(f16x2_t, v.y);
+  return p;
+}
+
+__device__ inline f16x8_t expand8(uint32_t codes8, const ScalePair &s) {
+  const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.pow2, 0) * s.mant;
+  const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.pow2, 1) * s.mant;
+  const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.pow2, 2) * s.mant;
+  const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, s.pow2, 3) * s.mant;
+  f16x8_t f;
+  f[0] = p0[0]; f[1] = p0[1]; f[2] = p1[0]; f[3] = p1[1];
+  f[4] = p2[0]; f[5] = p2[1]; f[6] = p3[0]; f[7] = p3[1];
+  return f;
+}
+
+__device__ inline bf16x8_t bits_to_bf16x8(const uint32_t *b) {
+  bf16x8_t f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = __builtin_bit_cast(__bf16, (uint16_t)b[i]);
+  return f;
+}
+
+// tile id -> (tile_m, tile_n): XCD-contiguous runs, grouped by kGroupM rows
+__device__ inline void tile_coords(int64_t bid, int64_t tiles_m, int64_t tiles_n, int64_t *tm,
+                                   int64_t *tn) {
+  const int64_t T = tiles_m * tiles_n;
+  int64_t L = bid;
+  if (T % kXcds == 0) L = (bid % kXcds) * (T / kXcds) + bid / kXcds;
+  const int64_t per_group = kGroupM * tiles_n;
+  const int64_t group = L / per_group;
+  const int64_t first_m = group * kGroupM;
+  const int64_t gsz = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int64_t in_group = L - group * per_group;
+  *tm = first_m + in_group % gsz;
+  *tn = in_group / gsz;
+}
+
+// KFAST: K % 128 == 0 (16-byte code chunks, 8-byte scale chunks, no k tail);
+// otherwise K % 16 == 0 with 8-byte code chunks and byte-wise scales.
+template <int WM, int WN, int TM, int TN, bool KFAST>
+__global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int A_BYTES = BM * kLdsStride, B_BYTES = BN * kLdsStride;
+  constexpr int STAGE = A_BYTES + B_BYTES + BM * 8 + BN * 8;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  __shared__ uint2 scale_lut[256];
+
+  const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  int64_t tile_m, tile_n;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, &tile_m, &tile_n);
+  const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t K = g.K, kb = K / 2, ks = K / kBlock;
+  const int nk = (int)((K + kBK - 1) / kBK);
+
+  // ---- global -> register staging ----------------------------------------
+  constexpr int CH = KFAST ? 16 : 8;
+  constexpr int PER_ROW = kRowBytes / CH;
+  constexpr int A_CH = BM * PER_ROW / NT, B_CH = BN * PER_ROW / NT;
+  constexpr int SCH = KFAST ? 8 : 1;                       // scale bytes per load
+  constexpr int SA_N = BM * 8 / SCH, SB_N = BN * 8 / SCH;  // scale chunks per tile
+  constexpr int SA_CH = (SA_N + NT - 1) / NT, SB_CH = (SB_N + NT - 1) / NT;
+  static_assert(A_CH >= 1 && B_CH >= 1 && SA_CH >= 1 && SB_CH >= 1, "tile too small");
+  static_assert(BM * PER_ROW % NT == 0 && BN * PER_ROW % NT == 0, "uneven staging");
+  typedef typename std::conditional<KFAST, uint4, uint2>::type chunk_t;
+  typedef typename std::conditional<KFAST, uint2, uint8_t>::type schunk_t;
+  chunk_t ra[A_CH], rb[B_CH];
+  schunk_t rsa[SA_CH], rsb[SB_CH];
+
+  auto load_global = [&](int kt) {
+    const int64_t kbyte0 = (int64_t)kt * kRowBytes, ksc0 = (int64_t)kt * 8;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / PER_ROW, seg = c % PER_ROW;
+      const int64_t gm = m0 + row, gb = kbyte0 + seg * CH;
+      chunk_t v = {};
+      if (gm < g.M && (KFAST || gb < kb)) v = *(const chunk_t *)(g.a_codes + gm * kb + gb);
+      ra[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / PER_ROW, seg = c % PER_ROW;
+      const int64_t gn = n0 + row, gb = kbyte0 + seg * CH;
+      chunk_t v = {};
+      if (gn < g.N && (KFAST || gb < kb)) v = *(const chunk_t *)(g.b_codes + gn * kb + gb);
+      rb[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < SA_CH; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / (8 / SCH), j = (c % (8 / SCH)) * SCH;
+      const int64_t gm = m0 + row, gs = ksc0 + j;
+      schunk_t v = {};
+      if (c < SA_N && gm < g.M && (KFAST || gs < ks)) v = *(const schunk_t *)(g.a_scales + gm * ks + gs);
+      rsa[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < SB_CH; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / (8 / SCH), j = (c % (8 / SCH)) * SCH;
+      const int64_t gn = n0 + row, gs = ksc0 + j;
+      schunk_t v = {};
+      if (c < SB_N && gn < g.N && (KFAST || gs < ks)) v = *(const schunk_t *)(g.b_scales + gn * ks + gs);
+      rsb[i] = v;
+    }
+  };
+  auto store_lds = [&](int stage) {
+    uint8_t *la = lds + stage * STAGE, *lb = la + A_BYTES, *lsa = lb + B_BYTES, *lsb = lsa + BM * 8;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NT;
+      *(chunk_t *)(la + (c / PER_ROW) * kLdsStride + (c % PER_ROW) * CH) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * NT;
+      *(chunk_t *)(lb + (c / PER_ROW) * kLdsStride + (c % PER_ROW) * CH) = rb[i];
+    }
+#pragma unroll
+    for (int i = 0; i < SA_CH; ++i)
+      if (tid + i * NT < SA_N) *(schunk_t *)(lsa + (tid + i * NT) * SCH) = rsa[i];
+#pragma unroll
+    for (int i = 0; i < SB_CH; ++i)
+      if (tid + i * NT < SB_N) *(schunk_t *)(lsb + (tid + i * NT) * SCH) = rsb[i];
+  };
+
+  floatx16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  fill_scale_lut(scale_lut);
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_global(kt + 1);
+    const uint8_t *la = lds + cur * STAGE, *lb = la + A_BYTES, *lsa = lb + B_BYTES, *lsb = lsa + BM * 8;
+    uint32_t sa4[TM], sb4[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      sa4[i] = *(const uint32_t *)(lsa + (wm * TM * 32 + i * 32 + l32) * 8 + h * 4);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      sb4[j] = *(const uint32_t *)(lsb + (wn * TN * 32 + j * 32 + l32) * 8 + h * 4);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      // one 16-element block per lane: 8 code bytes (two k-steps) per sub-tile
+      uint2 ca[TM], cb[TN];
+      ScalePair sa[TM], sb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        ca[i] = *(const uint2 *)(la + (wm * TM * 32 + i * 32 + l32) * kLdsStride + h * 32 + blk * 8);
+        sa[i] = lut_scale(scale_lut, (sa4[i] >> (8 * blk)) & 0xFFu);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        cb[j] = *(const uint2 *)(lb + (wn * TN * 32 + j * 32 + l32) * kLdsStride + h * 32 + blk * 8);
+        sb[j] = lut_scale(scale_lut, (sb4[j] >> (8 * blk)) & 0xFFu);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        f16x8_t av[TM], bv[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) av[i] = expand8(half ? ca[i].y : ca[i].x, sa[i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bv[j] = expand8(half ? cb[j].y : cb[j].x, sb[j]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        // keep each k-step's expansions next to its MFMAs (bounds live registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (kt + 1 < nk) store_lds(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue, one 32x32 tile at a time -----------------------------------
+  // C = alpha s_tA s_tB acc, then the rank-r term as BF16 MFMA k-steps on the
+  // hi/lo split of l_scale * L, then beta_e E; stored with bounds checks.
+  // 32x32 accumulator layout: register e of lane l holds row
+  // 8*(e/4) + 4*(l/32) + e%4, column l%32.
+  const float scale = g.alpha * (*g.a_ts) * (*g.b_ts);
+  const int nchunks = (g.r + 15) / 16;                    // <= 4 (r <= 64)
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m_frag = m0 + wm * TM * 32 + i * 32 + l32;
+    bf16x8_t lhi[4], llo[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t hb[8], lb[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int jj = c * 16 + 8 * h + q;
+        const float x = (c < nchunks && m_frag < g.M && jj < g.r) ? g.L[m_frag * g.r + jj] * g.l_scale : 0.0f;
+        hb[q] = float_to_bf16_rne_bits(x);
+        lb[q] = float_to_bf16_rne_bits(x - bf16_bits_to_float(hb[q]));
+      }
+      lhi[c] = bits_to_bf16x8(hb);
+      llo[c] = bits_to_bf16x8(lb);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = n0 + wn * TN * 32 + j * 32 + l32;
+      floatx16_t t = acc[i][j] * scale;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c < nchunks) {
+          uint32_t b[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int jj = c * 16 + 8 * h + q;
+            b[q] = (n < g.N && jj < g.r) ? (uint32_t)g.R[n * g.r_sn + jj * g.r_sj] : 0u;
+          }
+          const bf16x8_t rv = bits_to_bf16x8(b);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lhi[c], rv, t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(llo[c], rv, t, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < g.M && n < g.N) {
+          float v = t[e];
+          if (g.E) v += g.beta_e * g.E[m * g.N + n];
+          g.C[m * g.N + n] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int WM, int WN, int TM, int TN>
+fs4_status launch_cfg(const GemmArgs &g, hipStream_t s) {
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  if (g.K % kBK == 0)
+    gemm_nt_kernel<WM, WN, TM, TN, true><<<(unsigned)tiles, WM * WN * 64, 0, s>>>(g);
+  else
+    gemm_nt_kernel<WM, WN, TM, TN, false><<<(unsigned)tiles, WM * WN * 64, 0, s>>>(g);
+  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+}
+
+}  // namespace
+
+fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
+                          float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s) {
+  GemmArgs g;
+  g.a_codes = A.codes; g.a_scales = A.scales; g.a_ts = A.tscale;
+  g.b_codes = B.codes; g.b_scales = B.scales; g.b_ts = B.tscale;
+  g.M = A.rows; g.N = B.rows; g.K = A.cols;
+  g.alpha = alpha; g.beta_e = beta_e; g.E = E; g.C = C;
+  g.L = lr.L; g.R = lr.R; g.r = lr.L ? lr.r : 0; g.l_scale = lr.l_scale;
+  g.r_sn = lr.r_sn; g.r_sj = lr.r_sj;
+  if (g.M == 0 || g.N == 0) return FS4_OK;
+  // 256 x 256 tiles (4 waves of 128 x 128) once there are enough of them to
+  // fill the chip; 128 x 128 tiles otherwise.
+  const int64_t big_tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+  if (big_tiles >= 256) return launch_cfg<2, 2, 4, 4>(g, s);
+  return launch_cfg<2, 2, 2, 2>(g, s);
+}
+
+}  // namespace fs4

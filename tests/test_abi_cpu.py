@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/fs4.h, and rejects bad arguments on the host before
+launching anything (validation never touches the fake device pointers used
+here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fs4.h")
+
+fs4 = pytest.importorskip("precision_pretraining_amd", reason="libfs4.so not built")
+lib = fs4._lib
+
+OK, NULL, SHAPE, ALIGN, DTYPE, RANK, WORKSPACE, HIP, ARG = range(9)
+A16 = 0x10000          # fake 16-byte aligned "device" address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fs4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["fs4_quantize", "fs4_gemm_nt", "fs4_linear_fwd", "fs4_linear_bwd", "fs4_newton_schulz",
+                 "fs4_workspace_bytes", "fs4_status_str"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(fs4.EXPORTS) == declared_functions()
+
+
+def test_status_strings_and_version():
+    for st in range(9):
+        assert fs4.status_str(st).startswith("FS4")
+    assert "gfx950" in fs4.version()
+
+
+def view(rows, cols, codes=A16, scales=A16, tscale=A16):
+    return fs4._View(codes, scales, tscale, rows, cols)
+
+
+def q(x=A16, dt=0, rows=64, cols=64, rv="ok", cv="ok", ws=A16 * 16, wsb=1 << 20):
+    r = view(rows, cols) if rv == "ok" else rv
+    c = view(cols, rows) if cv == "ok" else cv
+    return lib.fs4_quantize(x, dt, rows, cols, ctypes.byref(r) if r is not None else None,
+                            ctypes.byref(c) if c is not None else None, ws, wsb, None)
+
+
+def test_quantize_validation():
+    assert q(dt=7) == DTYPE
+    assert q(rows=-16) == SHAPE
+    assert q(rv=None, cv=None) == NULL
+    assert q(x=None) == NULL
+    assert q(x=A16 + 4) == ALIGN
+    assert q(rv=view(64, 48)) == SHAPE                     # view shape disagrees
+    assert q(cols=40, rv=view(64, 40), cv=None) == SHAPE   # cols not a multiple of 16
+    assert q(rows=40, rv=None, cv=view(64, 40)) == SHAPE   # rows blocked in the column view
+    assert q(rv=view(64, 64, codes=None)) == NULL
+    assert q(rv=view(64, 64, scales=A16 + 8)) == ALIGN
+    assert q(wsb=16) == WORKSPACE
+    assert q(ws=None) == NULL
+    assert q(ws=A16 + 16) == ALIGN                         # workspace must be 256-byte aligned
+    assert lib.fs4_quantize_workspace_bytes(64, 64) > 0
+
+
+def test_gemm_validation():
+    a, b = view(64, 128), view(32, 128)
+    assert lib.fs4_gemm_nt(None, ctypes.byref(b), 1.0, None, 0.0, A16, None, 0, None) == NULL
+    bad = view(32, 96)
+    assert lib.fs4_gemm_nt(ctypes.byref(a), ctypes.byref(bad), 1.0, None, 0.0, A16, None, 0, None) == SHAPE
+    assert lib.fs4_gemm_nt(ctypes.byref(a), ctypes.byref(b), 1.0, None, 0.0, None, None, 0, None) == NULL
+    assert lib.fs4_gemm_nt(ctypes.byref(a), ctypes.byref(b), 1.0, A16 + 4, 0.0, A16, None, 0, None) == ALIGN
+    odd = view(64, 40)
+    assert lib.fs4_gemm_nt(ctypes.byref(odd), ctypes.byref(odd), 1.0, None, 0.0, A16, None, 0, None) == SHAPE
+
+
+def fwd(X=A16, M=64, K=128, R="ok", U=A16, V=A16, r=8, Y=A16, T=None, xc=None, wsb=1 << 30):
+    Rv = view(256, K) if R == "ok" else R
+    return lib.fs4_linear_fwd(X, M, K, ctypes.byref(Rv) if Rv is not None else None, U, V, r, 1.0, Y, T,
+                              ctypes.byref(xc) if xc is not None else None, A16 * 16, wsb, None)
+
+
+def test_linear_fwd_validation():
+    assert fwd(M=40) == SHAPE
+    assert fwd(K=0) == SHAPE
+    assert fwd(X=None) == NULL
+    assert fwd(R=None) == NULL
+    assert fwd(R=view(256, 64)) == SHAPE
+    assert fwd(r=65) == RANK
+    assert fwd(r=-1) == RANK
+    assert fwd(U=None) == RANK
+    assert fwd(Y=A16 + 8) == ALIGN
+    assert fwd(xc=view(64, 128)) == SHAPE                  # must be rows = K, cols = M
+    assert fwd(wsb=100) == WORKSPACE
+    need = lib.fs4_linear_fwd_workspace_bytes(64, 128, 256, 8)
+    assert need == lib.fs4_workspace_bytes(2, 64, 128, 256, 8)
+
+
+def bwd(dY=A16, M=64, N=256, K=128, X=A16, xc="ok", rc="ok", U=A16, V=A16, r=8, T=A16, dX=A16, dW=A16,
+        dU=A16, dV=A16, wsb=1 << 30):
+    xcv = view(K, M) if xc == "ok" else xc
+    rcv = view(K, N) if rc == "ok" else rc
+    return lib.fs4_linear_bwd(dY, M, N, K, X, ctypes.byref(xcv) if xcv is not None else None,
+                              ctypes.byref(rcv) if rcv is not None else None, U, V, r, 1.0, T, dX, dW, dU, dV,
+                              A16 * 16, wsb, None)
+
+
+def test_linear_bwd_validation():
+    assert bwd(N=100) == SHAPE
+    assert bwd(dY=None) == NULL
+    assert bwd(xc=view(M := 64, 128)) == SHAPE
+    assert bwd(rc=None) == NULL
+    assert bwd(T=None) == RANK
+    assert bwd(X=None) == NULL                             # dV requested needs X
+    assert bwd(dX=None) == NULL
+    assert bwd(dW=A16 + 4) == ALIGN
+    assert bwd(wsb=1) == WORKSPACE
+
+
+def ns(G=A16, dt=0, m=64, n=128, steps=5, X=A16, wsb=1 << 30):
+    return lib.fs4_newton_schulz(G, dt, m, n, steps, 3.4445, -4.775, 2.0315, 1, 1e-7, X, None, None, None,
+                                 A16 * 16, wsb, None)
+
+
+def test_newton_schulz_validation():
+    assert ns(dt=3) == DTYPE
+    assert ns(m=256, n=128) == SHAPE                       # m <= n required
+    assert ns(m=24) == SHAPE
+    assert ns(steps=-1) == ARG
+    assert ns(G=None) == NULL
+    assert ns(X=A16 + 2) == ALIGN
+    assert ns(wsb=1024) == WORKSPACE
+
+
+def test_workspace_sizes_grow_with_shape():
+    small = lib.fs4_linear_bwd_workspace_bytes(64, 64, 64, 8)
+    big = lib.fs4_linear_bwd_workspace_bytes(8192, 8192, 3072, 32)
+    assert big > small > 0
+    assert lib.fs4_newton_schulz_workspace_bytes(3072, 8192) > 3072 * 8192 * 4
+    assert lib.fs4_workspace_bytes(99, 1, 1, 1, 0) == 0

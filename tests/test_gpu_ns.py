@@ -1,0 +1,73 @@
+"""NVFP4 Newton-Schulz parity vs the oracle.
+
+The iteration amplifies NVFP4 noise once aX and BX start to cancel, so two
+correct implementations that differ only in fp32 summation order drift apart
+over several steps.  Parity is therefore checked one step at a time: the HIP
+path is started (normalize=0, steps=1) from the oracle's own iterate X_k and
+its A, B and X_{k+1} are compared with the oracle's step from the same X_k,
+normalised by sum |a||b| (+ |b A| and |a X| for the elementwise terms).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import need_gpu, dev_bf16, dev_f32, print_case, f32
+from oracle.newton_schulz import MUON_ABC
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def test_normalization():
+    fs4 = need_gpu()
+    print_case(test="ns_normalize")
+    g = synth.ns_input(seed=5, m=192, n=512)
+    X = fs4.newton_schulz(dev_bf16(g), steps=0).cpu().numpy()
+    _, ref = oracle.ns_normalize(f32(g))
+    # one fp32 rounding of an fp64 value on each side
+    assert np.max(np.abs(X - ref) / np.maximum(np.abs(ref), 1e-30)) <= 2.0 ** -23
+
+
+@pytest.mark.parametrize("m,n", [(192, 512), (768, 2048)])
+def test_per_step_parity(m, n):
+    fs4 = need_gpu()
+    print_case(test="ns_step", m=m, n=n)
+    g = synth.ns_input(seed=5, m=m, n=n)
+    xs, steps = oracle.newton_schulz(f32(g), 5)
+    a, b, c = MUON_ABC
+    for k in range(5):
+        X, tX, tA, tB = fs4.newton_schulz(dev_f32(xs[k]), steps=1, normalize=False, trace=True)
+        st = steps[k]
+        eA = oracle.rel_err(tA[0].cpu().numpy(), st["A64"], st["A_D"])
+        eB = oracle.rel_err(tB[0].cpu().numpy(), st["B64"], st["B_D"])
+        eX = oracle.rel_err(X.cpu().numpy(), st["X64"], st["X_D"])
+        print("step", k, "errA %.2e errB %.2e errX %.2e" % (eA, eB, eX), flush=True)
+        assert eA <= TOL and eB <= TOL and eX <= TOL, (k, eA, eB, eX)
+
+
+def test_full_size_first_product_sampled():
+    """3072 x 8192 momentum: normalisation in full and the first product
+    A = Q(X_0) Q(X_0)^T on sampled entries, plus the full 5-step run's
+    iterate staying in the band the quantized iteration reaches."""
+    fs4 = need_gpu()
+    print_case(test="ns_3072x8192")
+    g = synth.ns_input()
+    X, tX, tA, tB = fs4.newton_schulz(dev_bf16(g), steps=5, trace=True)
+    x0_ref32, x0_ref = oracle.ns_normalize(f32(g))
+    x0 = tX[0].cpu().numpy()
+    assert np.max(np.abs(x0 - x0_ref) / np.maximum(np.abs(x0_ref), 1e-30)) <= 2.0 ** -23
+    from oracle.quantize import quantize_rows, tensor_scale
+    s = tensor_scale(x0_ref32)
+    rng = np.random.default_rng(1)
+    A0 = tA[0]
+    for i, j in zip(rng.integers(0, 3072, 24), rng.integers(0, 3072, 24)):
+        qi = oracle.block_values(quantize_rows(x0_ref32[i:i + 1], s))[0]
+        qj = oracle.block_values(quantize_rows(x0_ref32[j:j + 1], s))[0]
+        ref = float(s) ** 2 * np.dot(qi, qj)
+        den = float(s) ** 2 * np.dot(np.abs(qi), np.abs(qj))
+        assert abs(A0[i, j].item() - ref) <= TOL * den
+    assert torch.equal(X, tX[5])
+    assert torch.isfinite(X).all()
