@@ -20,6 +20,12 @@
 // hi + lo parts and runs as extra BF16 MFMA k-steps into the accumulators
 // after they have been scaled by alpha s_tA s_tB.
 //
+// On gfx950 a wave's VALU work and its MFMAs do not overlap much (measured),
+// so the VALU count per MFMA bounds the kernel: expanding an A fragment once
+// serves TN MFMAs and a B fragment TM MFMAs.  Codes are read from LDS one
+// 16-element block per k-step pair, and the next step's operands are
+// expanded right before the current step's MFMAs are issued.
+//
 // Tiling: a workgroup of WM x WN waves computes (WM*TM*32) x (WN*TN*32) of C,
 // each wave TM x TN accumulators of v_mfma_f32_32x32x16_f16.  The k-tile is
 // 128 elements (64 code bytes and 8 scale bytes per row), double-buffered in
@@ -238,6 +244,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_global(kt + 1);
     const uint8_t *la = lds + cur * STAGE, *lb = la + A_BYTES, *lsa = lb + B_BYTES, *lsb = lsa + BM * 8;
+    // this lane's rows in the stage: codes at row*80 + h*32, scale bytes at row*8 + h*4
+    const uint8_t *pa = la + (wm * TM * 32 + l32) * kLdsStride + h * 32;
+    const uint8_t *pb = lb + (wn * TN * 32 + l32) * kLdsStride + h * 32;
     uint32_t sa4[TM], sb4[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -245,35 +254,58 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       sb4[j] = *(const uint32_t *)(lsb + (wn * TN * 32 + j * 32 + l32) * 8 + h * 4);
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      // one 16-element block per lane: 8 code bytes (two k-steps) per sub-tile
-      uint2 ca[TM], cb[TN];
-      ScalePair sa[TM], sb[TN];
+
+    // Software pipeline over the 8 k-steps of the tile: block b's codes and
+    // scale pairs are read one block ahead, and step s+1's operands are
+    // expanded while step s's MFMAs run.
+    uint2 ca[TM], cb[TN];
+    ScalePair sa[TM], sb[TN];
+    auto read_block = [&](int blk) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        ca[i] = *(const uint2 *)(la + (wm * TM * 32 + i * 32 + l32) * kLdsStride + h * 32 + blk * 8);
+        ca[i] = *(const uint2 *)(pa + i * 32 * kLdsStride + blk * 8);
         sa[i] = lut_scale(scale_lut, (sa4[i] >> (8 * blk)) & 0xFFu);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        cb[j] = *(const uint2 *)(lb + (wn * TN * 32 + j * 32 + l32) * kLdsStride + h * 32 + blk * 8);
+        cb[j] = *(const uint2 *)(pb + j * 32 * kLdsStride + blk * 8);
         sb[j] = lut_scale(scale_lut, (sb4[j] >> (8 * blk)) & 0xFFu);
       }
+    };
+    read_block(0);
+    f16x8_t av[TM], bv[TN];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        f16x8_t av[TM], bv[TN];
+    for (int i = 0; i < TM; ++i) av[i] = expand8(ca[i].x, sa[i]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) av[i] = expand8(half ? ca[i].y : ca[i].x, sa[i]);
+    for (int j = 0; j < TN; ++j) bv[j] = expand8(cb[j].x, sb[j]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bv[j] = expand8(half ? cb[j].y : cb[j].x, sb[j]);
+    for (int s = 0; s < 8; ++s) {
+      // next step's operands: the other half of this block, or the next block
+      f16x8_t an[TM], bn[TN];
+      if (s + 1 < 8) {
+        if ((s & 1) == 0) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+          for (int i = 0; i < TM; ++i) an[i] = expand8(ca[i].y, sa[i]);
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-        // keep each k-step's expansions next to its MFMAs (bounds live registers)
-        __builtin_amdgcn_sched_barrier(0);
+          for (int j = 0; j < TN; ++j) bn[j] = expand8(cb[j].y, sb[j]);
+        } else {
+          read_block((s + 1) >> 1);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) an[i] = expand8(ca[i].x, sa[i]);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bn[j] = expand8(cb[j].x, sb[j]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      if (s + 1 < 8) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) av[i] = an[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bv[j] = bn[j];
       }
     }
     if (kt + 1 < nk) store_lds(cur ^ 1);
@@ -358,10 +390,21 @@ fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, c
   g.L = lr.L; g.R = lr.R; g.r = lr.L ? lr.r : 0; g.l_scale = lr.l_scale;
   g.r_sn = lr.r_sn; g.r_sj = lr.r_sj;
   if (g.M == 0 || g.N == 0) return FS4_OK;
-  // 256 x 256 tiles (4 waves of 128 x 128) once there are enough of them to
-  // fill the chip; 128 x 128 tiles otherwise.
-  const int64_t big_tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
-  if (big_tiles >= 256) return launch_cfg<2, 2, 4, 4>(g, s);
+  // Tile shape: the one with the least estimated time, counted as rounds of
+  // workgroups over the 256 CUs times tile area over the configuration's
+  // relative MFMA throughput (measured on MI355X at the 3B shapes):
+  //   256 x 256, 8 waves of 128 x 64 (two per SIMD)   1.00
+  //   256 x 192, 4 waves of 128 x 96 (one per SIMD)   0.83
+  //   128 x 128, 4 waves of 64 x 64                   0.70
+  // Whole rounds matter: 384 tiles of 256 x 256 (an 8192 x 3072 output) leave
+  // half the chip idle in the second round, 512 tiles of 256 x 192 do not.
+  auto cost = [&](int64_t bm, int64_t bn, double rate) {
+    const int64_t tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
+    return (double)((tiles + 255) / 256) * (double)(bm * bn) / rate;
+  };
+  const double c256 = cost(256, 256, 1.0), c192 = cost(256, 192, 0.83), c128 = cost(128, 128, 0.70);
+  if (c256 <= c192 && c256 <= c128) return launch_cfg<2, 4, 4, 2>(g, s);
+  if (c192 <= c128) return launch_cfg<2, 2, 4, 3>(g, s);
   return launch_cfg<2, 2, 2, 2>(g, s);
 }
 

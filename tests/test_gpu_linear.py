@@ -216,3 +216,28 @@ def test_3b_linear_fwd_bwd_sampled():
     dV_ref = P.T @ x32.astype(np.float64)
     dV_den = (np.abs(dy64) @ np.abs(u32.astype(np.float64))).T @ np.abs(x32.astype(np.float64))
     assert _err(bwd.dV.cpu().numpy(), dV_ref, dV_den) <= TIGHT
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 1040), (8192, 3008, 1040)])
+def test_gemm_large_tiles_ragged_k_sampled(M, N, K):
+    """Shapes large enough for the wide tile configurations (4096 x 4096 takes
+    256 x 256 tiles; 8192 x 3008 takes 256 x 192 tiles with a ragged last
+    column of tiles), with K % 128 != 0 (the byte-wise staging path with a k
+    tail); sampled outputs against the oracle's rows."""
+    fs4 = need_gpu()
+    print_case(test="gemm_large_ragged_k", M=M, N=N, K=K)
+    rng = np.random.default_rng(21 + N)
+    a = synth.bf16_round(rng.standard_normal((M, K)))
+    b = (rng.standard_t(3, size=(N, K)) * 0.02).astype(np.float32)
+    ar, _ = fs4.quantize(dev_bf16(a), colwise=False)
+    br, _ = fs4.quantize(dev_f32(b), colwise=False)
+    C = fs4.gemm_nt(ar, br).cpu().numpy()
+    a32 = f32(a)
+    s_a, s_b = tensor_scale(a32), tensor_scale(b)
+    ms, ns_ = rng.integers(0, M, 64), rng.integers(0, N, 64)
+    ms[:4] = [0, M - 1, 255, 256]
+    ns_[:4] = [N - 1, 0, 192, 191]
+    qa = [quantize_rows(a32[m:m + 1], s_a) for m in ms]
+    qb = [quantize_rows(b[n:n + 1], s_b) for n in ns_]
+    e = _sampled_gemm_check(C, qa, qb, list(zip(ms, ns_)))
+    assert e <= TOL and e <= TIGHT, e
