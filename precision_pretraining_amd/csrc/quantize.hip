@@ -201,17 +201,22 @@ __device__ inline uint32_t scale_code(float amax, float inv6st, const Tables &t)
   return (uint32_t)c;
 }
 
-// Encodes 16 values; returns the scale code, packs the codes (element 2j in
-// the low nibble of byte j).
-__device__ inline uint32_t encode16(const float *v, float inv6st, const Tables &t, uint2 &packed) {
+// Encodes 16 values v[i] = src[i * estride] (LDS); returns the scale code and
+// packs the codes (element 2j in the low nibble of byte j).
+__device__ inline uint32_t encode16(const float *src, int estride, float inv6st, const Tables &t,
+                                    uint2 &packed) {
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = src[i * estride];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const uint32_t sb = scale_code(amax, inv6st, t);
   const float rl = t.rlo[sb], rh = t.rhi[sb];
-  uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
-  bool exact = rl < 0.0f;
-  if (!exact) {
+  const float *th = t.eth[sb];
+  uint32_t lo0 = 0, lo1 = 0;
+  if (rl >= 0.0f) {
+    uint32_t hi0 = 0, hi1 = 0;
 #define FS4_CVT(W, A, B, R, SEL) W = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(W, (A) * (R), (B) * (R), 1.0f, SEL)
     FS4_CVT(lo0, v[0], v[1], rl, 0); FS4_CVT(lo0, v[2], v[3], rl, 1);
     FS4_CVT(lo0, v[4], v[5], rl, 2); FS4_CVT(lo0, v[6], v[7], rl, 3);
@@ -222,12 +227,32 @@ __device__ inline uint32_t encode16(const float *v, float inv6st, const Tables &
     FS4_CVT(hi1, v[8], v[9], rh, 0); FS4_CVT(hi1, v[10], v[11], rh, 1);
     FS4_CVT(hi1, v[12], v[13], rh, 2); FS4_CVT(hi1, v[14], v[15], rh, 3);
 #undef FS4_CVT
-    exact = (lo0 != hi0) | (lo1 != hi1);
-  }
-  if (exact) {
-    // exact path: count the thresholds each |x| reaches
-    const float *th = t.eth[sb];
-    lo0 = lo1 = 0;
+    // An element whose two codes differ lies within the bracket of a
+    // midpoint; its code is the lower one, or the upper one when |x| reaches
+    // the exact threshold above the lower magnitude.  Rare (mostly exact
+    // rational ties of low-precision inputs, perturbed by the rounding of
+    // s_t), so lanes loop over such elements one at a time.
+    uint32_t d0 = lo0 ^ hi0, d1 = lo1 ^ hi1;
+    while (d0 | d1) {
+      const bool w1 = d0 == 0u;
+      const uint32_t d = w1 ? d1 : d0;
+      const uint32_t sh = (uint32_t)__builtin_ctz(d) & ~3u;
+      const uint32_t lo = w1 ? lo1 : lo0, hi = w1 ? hi1 : hi0;
+      const int e = (int)(sh >> 2) + (w1 ? 8 : 0);
+      const float a = fabsf(src[e * estride]);
+      const uint32_t c = a >= th[(lo >> sh) & 7u] ? (hi >> sh) & 15u : (lo >> sh) & 15u;
+      const uint32_t nl = (lo & ~(15u << sh)) | (c << sh);
+      if (w1) {
+        lo1 = nl;
+        d1 &= ~(15u << sh);
+      } else {
+        lo0 = nl;
+        d0 &= ~(15u << sh);
+      }
+    }
+  } else {
+    // 1/step beyond fp32's reach (tiny fp32 tensors): count the thresholds
+    // each |x| reaches
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float a = fabsf(v[i]);
@@ -243,55 +268,116 @@ __device__ inline uint32_t encode16(const float *v, float inv6st, const Tables &
   return sb;
 }
 
-// stage a 64 x 64 tile as fp32 in LDS (zeros outside the tensor)
+// One 64 x 64 tile in registers: bf16 takes two 16-byte words per lane, fp32
+// four (zeros outside the tensor).
 template <bool BF16>
-__device__ inline void load_tile(const void *x, int64_t rows, int64_t cols, int64_t r0, int64_t c0,
-                                 float (*tile)[kTile + 1]) {
-  if constexpr (BF16) {
-    const uint16_t *xb = (const uint16_t *)x;
-    uint4 v[2];
+struct TileRegs {
+  static constexpr int kVec = BF16 ? 2 : 4;
+  uint4 v[kVec];
+};
+
+// Loads are issued for every lane (addresses clamped into the tensor) and the
+// padding is zeroed when the tile is staged, so no lane-dependent branch
+// surrounds a load.
+// A workgroup past its last tile (valid == false) reads the tensor's first
+// 16 bytes instead, so the number of loads in flight never depends on the
+// data and the waits stay exact.
+template <bool BF16>
+__device__ inline void tile_gload(const void *x, int64_t rows, int64_t cols, int64_t r0, int64_t c0,
+                                  bool valid, TileRegs<BF16> &g) {
+  constexpr int kPerRow = BF16 ? 8 : 16;     // 16-byte words per 64-element tile row
+  constexpr int kElems = BF16 ? 8 : 4;       // elements per word
+  const char *xb = (const char *)x;
+  const int64_t esz = BF16 ? 2 : 4;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int idx = threadIdx.x + p * kThreads;
-      const int r = idx >> 3, ch = idx & 7;
-      const int64_t gr = r0 + r, gc = c0 + ch * 8;
-      v[p] = (gr < rows && gc < cols) ? *(const uint4 *)(xb + gr * cols + gc) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int idx = threadIdx.x + p * kThreads;
-      const int r = idx >> 3, ch = idx & 7;
-      const uint32_t wv[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        tile[r][ch * 8 + 2 * j] = bf16_bits_to_float(wv[j] & 0xFFFFu);
-        tile[r][ch * 8 + 2 * j + 1] = bf16_bits_to_float(wv[j] >> 16);
-      }
-    }
-  } else {
-    const float *xf = (const float *)x;
-    float4 v[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int idx = threadIdx.x + p * kThreads;
-      const int r = idx >> 4, ch = idx & 15;
-      const int64_t gr = r0 + r, gc = c0 + ch * 4;
-      v[p] = (gr < rows && gc < cols) ? *(const float4 *)(xf + gr * cols + gc)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int idx = threadIdx.x + p * kThreads;
-      const int r = idx >> 4, ch = idx & 15;
-      tile[r][ch * 4 + 0] = v[p].x;
-      tile[r][ch * 4 + 1] = v[p].y;
-      tile[r][ch * 4 + 2] = v[p].z;
-      tile[r][ch * 4 + 3] = v[p].w;
-    }
+  for (int p = 0; p < TileRegs<BF16>::kVec; ++p) {
+    const int idx = threadIdx.x + p * kThreads;
+    const int r = idx / kPerRow, ch = idx % kPerRow;
+    int64_t gr = r0 + r, gc = c0 + ch * kElems;
+    gr = gr < rows ? gr : rows - 1;
+    gc = gc < cols ? gc : cols - kElems;
+    const int64_t off = valid ? (gr * cols + gc) * esz : 0;
+    g.v[p] = *(const uint4 *)(xb + off);
   }
 }
 
 template <bool BF16>
+__device__ inline void tile_store(const TileRegs<BF16> &g, int64_t rows, int64_t cols, int64_t r0,
+                                  int64_t c0, float (*tile)[kTile + 1]) {
+  constexpr int kPerRow = BF16 ? 8 : 16;
+  constexpr int kElems = BF16 ? 8 : 4;
+#pragma unroll
+  for (int p = 0; p < TileRegs<BF16>::kVec; ++p) {
+    const int idx = threadIdx.x + p * kThreads;
+    const int r = idx / kPerRow, ch = idx % kPerRow;
+    const bool in = r0 + r < rows && c0 + ch * kElems < cols;
+    const uint32_t w[4] = {in ? g.v[p].x : 0u, in ? g.v[p].y : 0u, in ? g.v[p].z : 0u,
+                           in ? g.v[p].w : 0u};
+    if constexpr (BF16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        tile[r][ch * 8 + 2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu);
+        tile[r][ch * 8 + 2 * j + 1] = bf16_bits_to_float(w[j] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tile[r][ch * 4 + j] = __builtin_bit_cast(float, w[j]);
+    }
+  }
+}
+
+// Work order.  Tiles are grouped 4 x 4 into 256 x 256 super-tiles; the 16
+// tiles of a super-tile go to 16 workgroups of one XCD (consecutive
+// dispatches land on different XCDs, round robin over 8), so the partial
+// 128-byte lines of both code layouts that neighbouring tiles share are
+// completed in one L2.
+struct TileOrder {
+  // The grid size is a multiple of 16, so a workgroup keeps its position
+  // (sub_r, sub_c) inside the super-tile and its super-tile index advances
+  // by grid / 16 per step; all of it is wave-uniform 32-bit arithmetic.
+  int tiles_r, tiles_c, sct, n_st;   // tile grid, super-tile columns and count
+  int sub_r, sub_c;                  // this workgroup's tile inside a super-tile
+  int d_r, d_c;                      // per-step advance in super-tile rows / columns
+  __device__ TileOrder(int64_t rows, int64_t cols) {
+    tiles_r = (int)((rows + kTile - 1) / kTile);
+    tiles_c = (int)((cols + kTile - 1) / kTile);
+    sct = (tiles_c + 3) / 4;
+    n_st = ((tiles_r + 3) / 4) * sct;
+    const int g = (int)gridDim.x, b = (int)blockIdx.x;
+    const int v = (g % 8 == 0) ? (b % 8) * (g / 8) + b / 8 : b;   // XCD-major numbering
+    sub_r = (v & 15) >> 2;
+    sub_c = v & 3;
+    d_r = (g / 16) / sct;
+    d_c = (g / 16) % sct;
+  }
+  // Position: super-tile (sr, sc); returns whether a tile is left, moving
+  // (sr, sc) forward to the first super-tile whose sub-tile lies inside.
+  __device__ bool seek(int &sr, int &sc) const {
+    while (sr * sct + sc < n_st) {
+      if (sr * 4 + sub_r < tiles_r && sc * 4 + sub_c < tiles_c) return true;
+      advance(sr, sc);
+    }
+    return false;
+  }
+  __device__ void advance(int &sr, int &sc) const {
+    sr += d_r;
+    sc += d_c;
+    if (sc >= sct) {
+      sc -= sct;
+      ++sr;
+    }
+  }
+  __device__ void start(int &sr, int &sc) const {
+    const int g = (int)gridDim.x, b = (int)blockIdx.x;
+    const int v = (g % 8 == 0) ? (b % 8) * (g / 8) + b / 8 : b;
+    sr = (v >> 4) / sct;
+    sc = (v >> 4) % sct;
+  }
+  __device__ int64_t r0(int sr) const { return (int64_t)(sr * 4 + sub_r) * kTile; }
+  __device__ int64_t c0(int sc) const { return (int64_t)(sc * 4 + sub_c) * kTile; }
+};
+
+template <bool BF16, bool ROW, bool COL>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restrict__ x, int64_t rows,
                                                             int64_t cols,
                                                             const uint32_t *__restrict__ partials,
@@ -306,47 +392,68 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
   const float amax = __builtin_bit_cast(float, m);
   const float s_t = (float)((double)amax / kTensorDiv);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (rv.codes) *rv.tscale = s_t;
-    if (cv.codes) *cv.tscale = s_t;
+    if (ROW) *rv.tscale = s_t;
+    if (COL) *cv.tscale = s_t;
   }
+  // the first two tiles' loads overlap the table construction
+  const TileOrder order(rows, cols);
+  int sr, sc;
+  order.start(sr, sc);
+  int have = order.seek(sr, sc) ? 1 : 0;   // int flags stay in scalar registers
+  int sr1 = sr, sc1 = sc;
+  if (have) order.advance(sr1, sc1);
+  int have1 = (have && order.seek(sr1, sc1)) ? 1 : 0;
+  TileRegs<BF16> g0, g1;
+  tile_gload<BF16>(x, rows, cols, order.r0(sr), order.c0(sc), have != 0, g0);
+  tile_gload<BF16>(x, rows, cols, order.r0(sr1), order.c0(sc1), have1 != 0, g1);
   build_tables(tab, s_t);
   // 1/(6 s_t) only seeds the scale-code estimate; the tables make it exact
   const float inv6st = s_t > 0.0f ? (float)(1.0 / (6.0 * (double)s_t)) : 0.0f;   // may be inf
+  tile_store<BF16>(g0, rows, cols, order.r0(sr), order.c0(sc), tile);
   __syncthreads();
 
-  const int64_t tiles_c = (cols + kTile - 1) / kTile, tiles_r = (rows + kTile - 1) / kTile;
   const int t = threadIdx.x;
-  for (int64_t tile_id = blockIdx.x; tile_id < tiles_r * tiles_c; tile_id += gridDim.x) {
-    const int64_t r0 = (tile_id / tiles_c) * kTile, c0 = (tile_id % tiles_c) * kTile;
-    load_tile<BF16>(x, rows, cols, r0, c0, tile);
+  const int line = t >> 2, blk = t & 3;     // four lanes per row (or column) of the tile
+  // One step: the tile in LDS is (sr, sc); `nxt` holds the loads of the
+  // following tile (sr1, sc1); `ahead` is free and receives the tile after
+  // that.  The encode runs from LDS while both are in flight; after a barrier
+  // `nxt` replaces the tile in LDS (its wait leaves the loads just issued into
+  // `ahead` outstanding) and this tile's codes are stored.
+  auto step = [&](TileRegs<BF16> &ahead, const TileRegs<BF16> &nxt) {
+    const int64_t r0 = order.r0(sr), c0 = order.c0(sc);
+    int sr2 = sr1, sc2 = sc1;
+    if (have1) order.advance(sr2, sc2);
+    const int have2 = (have1 && order.seek(sr2, sc2)) ? 1 : 0;
+    tile_gload<BF16>(x, rows, cols, order.r0(sr2), order.c0(sc2), have2 != 0, ahead);
+    // zero padding outside the tensor encodes harmlessly; only stores are masked
+    uint2 pr = make_uint2(0, 0), pc = make_uint2(0, 0);
+    uint32_t sbr = 0, sbc = 0;
+    if (ROW) sbr = encode16(&tile[line][blk * kBlock], 1, inv6st, tab, pr);
+    if (COL) sbc = encode16(&tile[blk * kBlock][line], kTile + 1, inv6st, tab, pc);
     __syncthreads();
-    // four lanes per row (or column) write 32 contiguous code bytes
-    const int line = t >> 2, blk = t & 3;
-    if (rv.codes) {
+    tile_store<BF16>(nxt, rows, cols, order.r0(sr1), order.c0(sc1), tile);   // unread past the last tile
+    if (ROW) {
       const int64_t gr = r0 + line, gc = c0 + blk * kBlock;
       if (gr < rows && gc < cols) {
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = tile[line][blk * kBlock + i];
-        uint2 packed;
-        const uint32_t sb = encode16(v, inv6st, tab, packed);
-        *(uint2 *)(rv.codes + gr * (cols / 2) + gc / 2) = packed;
-        rv.scales[gr * (cols / kBlock) + gc / kBlock] = (uint8_t)sb;
+        *(uint2 *)(rv.codes + gr * (cols / 2) + gc / 2) = pr;
+        rv.scales[gr * (cols / kBlock) + gc / kBlock] = (uint8_t)sbr;
       }
     }
-    if (cv.codes) {
+    if (COL) {
       const int64_t gc = c0 + line, gr = r0 + blk * kBlock;
       if (gc < cols && gr < rows) {
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = tile[blk * kBlock + i][line];
-        uint2 packed;
-        const uint32_t sb = encode16(v, inv6st, tab, packed);
-        *(uint2 *)(cv.codes + gc * (rows / 2) + gr / 2) = packed;
-        cv.scales[gc * (rows / kBlock) + gr / kBlock] = (uint8_t)sb;
+        *(uint2 *)(cv.codes + gc * (rows / 2) + gr / 2) = pc;
+        cv.scales[gc * (rows / kBlock) + gr / kBlock] = (uint8_t)sbc;
       }
     }
     __syncthreads();
+    have = have1; sr = sr1; sc = sc1;
+    have1 = have2; sr1 = sr2; sc1 = sc2;
+  };
+  while (have) {
+    step(g0, g1);
+    if (!have) break;
+    step(g1, g0);
   }
 }
 
@@ -375,15 +482,24 @@ fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t co
   const int64_t g = (nvec + kThreads * kAmaxUnroll * 2 - 1) / (kThreads * kAmaxUnroll * 2);
   const int npart = (int)(g < 1 ? 1 : (g > kAmaxPartials ? kAmaxPartials : g));
   uint32_t *partials = (uint32_t *)ws;
-  const int64_t tiles = ((cols + kTile - 1) / kTile) * ((rows + kTile - 1) / kTile);
-  const unsigned grid = (unsigned)(tiles < kEncodeGrid ? tiles : kEncodeGrid);
+  // one workgroup per tile slot (4 x 4 tiles per super-tile), at most kEncodeGrid
+  const int64_t slots = ((rows + 4 * kTile - 1) / (4 * kTile)) * ((cols + 4 * kTile - 1) / (4 * kTile)) * 16;
+  const unsigned grid = (unsigned)(slots < kEncodeGrid ? slots : kEncodeGrid);   // multiple of 16
+  static_assert(kEncodeGrid % 16 == 0, "the tile walk needs a grid that is a multiple of 16");
+  const bool row = rv.codes != nullptr, col = cv.codes != nullptr;
+  if (bf16) amax_partial_kernel<true><<<npart, kThreads, 0, s>>>((const uint4 *)x, nvec, partials);
+  else amax_partial_kernel<false><<<npart, kThreads, 0, s>>>((const uint4 *)x, nvec, partials);
+#define FS4_QK(B, R, C) quantize_kernel<B, R, C><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv)
   if (bf16) {
-    amax_partial_kernel<true><<<npart, kThreads, 0, s>>>((const uint4 *)x, nvec, partials);
-    quantize_kernel<true><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv);
+    if (row && col) FS4_QK(true, true, true);
+    else if (row) FS4_QK(true, true, false);
+    else FS4_QK(true, false, true);
   } else {
-    amax_partial_kernel<false><<<npart, kThreads, 0, s>>>((const uint4 *)x, nvec, partials);
-    quantize_kernel<false><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv);
+    if (row && col) FS4_QK(false, true, true);
+    else if (row) FS4_QK(false, true, false);
+    else FS4_QK(false, false, true);
   }
+#undef FS4_QK
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 
