@@ -55,7 +55,9 @@ FwdWs carve_fwd(void *ws, int64_t M, int64_t K, int r, size_t *total) {
   w.x_row = carve_view(c, M, K);
   w.qws = (uint32_t *)c.take(quantize_ws_bytes());
   w.T = (float *)c.take((size_t)(M * (r > 0 ? r : 1)) * sizeof(float));
-  w.partials = (float *)c.take(small_gemm_partials_bytes(M, r > 0 ? r : 1, K));
+  size_t pb = small_gemm_partials_bytes(M, r > 0 ? r : 1, K);
+  const size_t p2 = rowred_partials_bytes(M, r > 0 ? r : 1, K);
+  w.partials = (float *)c.take(pb > p2 ? pb : p2);
   if (total) *total = c.off;
   return w;
 }
@@ -64,6 +66,7 @@ struct BwdWs {
   fs4_nvfp4 dy_row, dy_col;
   uint32_t *qws;
   float *P;
+  uint16_t *Ut, *bt;
   float *partials;
 };
 BwdWs carve_bwd(void *ws, int64_t M, int64_t N, int64_t K, int r, size_t *total) {
@@ -74,11 +77,13 @@ BwdWs carve_bwd(void *ws, int64_t M, int64_t N, int64_t K, int r, size_t *total)
   w.qws = (uint32_t *)c.take(quantize_ws_bytes());
   const int rr = r > 0 ? r : 1;
   w.P = (float *)c.take((size_t)(M * rr) * sizeof(float));
-  size_t pb = small_gemm_partials_bytes(M, rr, N);
-  size_t p2 = small_gemm_partials_bytes(N, rr, M);
-  size_t p3 = small_gemm_partials_bytes(rr, K, M);
-  if (p2 > pb) pb = p2;
-  if (p3 > pb) pb = p3;
+  w.Ut = (uint16_t *)c.take((size_t)(N * rr) * sizeof(uint16_t));
+  w.bt = (uint16_t *)c.take((size_t)(2 * M * rr) * sizeof(uint16_t));
+  size_t pb = 0;
+  for (size_t b : {small_gemm_partials_bytes(M, rr, N), small_gemm_partials_bytes(N, rr, M),
+                   small_gemm_partials_bytes(rr, K, M), rowred_partials_bytes(M, rr, N),
+                   colred_partials_bytes(M, N, rr), colred_partials_bytes(M, K, rr)})
+    pb = b > pb ? b : pb;
   w.partials = (float *)c.take(pb);
   if (total) *total = c.off;
   return w;
@@ -203,19 +208,27 @@ fs4_status fs4_linear_fwd(const void *X, int64_t M, int64_t K, const fs4_nvfp4 *
 
   hipStream_t s = as_stream(stream);
   FwdWs w = carve_fwd(ws, M, K, r, nullptr);
-  FS4_TRY(launch_quantize(X, FS4_BF16, M, K, &w.x_row, X_col_save, w.qws, s));
   LowRankEpilogue lr;
   if (r > 0) {
     float *T = T_save ? T_save : w.T;
-    // T[m][j] = sum_k X[m][k] V[j][k]
-    FS4_TRY(launch_small_gemm(X, false, K, 1, V, false, K, 1, M, r, K, 1.0f, T, false,
-                              w.partials, s));
+    // T[m][j] = sum_k X[m][k] V[j][k]; this pass reads all of X, so it also
+    // yields X's amax partials for the quantizer when they fit
+    const int64_t nwg = rowred_workgroups(M, K);
+    const bool fuse = nwg <= kAmaxPartials;
+    FS4_TRY(launch_rowred((const uint16_t *)X, (const uint16_t *)V, M, r, K, 1.0f, T, w.partials,
+                          fuse ? w.qws : nullptr, s));
+    if (fuse)
+      FS4_TRY(launch_quantize_encode(X, FS4_BF16, M, K, &w.x_row, X_col_save, w.qws, (int)nwg, s));
+    else
+      FS4_TRY(launch_quantize(X, FS4_BF16, M, K, &w.x_row, X_col_save, w.qws, s));
     lr.L = T;
     lr.R = (const uint16_t *)U;
     lr.r = r;
     lr.r_sn = r;
     lr.r_sj = 1;
     lr.l_scale = beta;
+  } else {
+    FS4_TRY(launch_quantize(X, FS4_BF16, M, K, &w.x_row, X_col_save, w.qws, s));
   }
   return launch_gemm_nt(w.x_row, *R_row, 1.0f, nullptr, 0.0f, Y, lr, s);
 }
@@ -254,30 +267,39 @@ fs4_status fs4_linear_bwd(const void *dY, int64_t M, int64_t N, int64_t K, const
 
   hipStream_t s = as_stream(stream);
   BwdWs w = carve_bwd(ws, M, N, K, r, nullptr);
-  FS4_TRY(launch_quantize(dY, FS4_BF16, M, N, &w.dy_row, &w.dy_col, w.qws, s));
   LowRankEpilogue lr;
   if (r > 0) {
-    // P[m][j] = sum_n dY[m][n] U[n][j]
-    FS4_TRY(launch_small_gemm(dY, false, N, 1, U, false, 1, r, M, r, N, 1.0f, w.P, false,
-                              w.partials, s));
+    // P[m][j] = sum_n dY[m][n] U[n][j] (U transposed once so both operands
+    // run along n); this pass reads all of dY, so it also yields dY's amax
+    // partials for the quantizer when they fit
+    FS4_TRY(launch_transpose_rank((const uint16_t *)U, N, r, w.Ut, s));
+    const int64_t nwg = rowred_workgroups(M, N);
+    const bool fuse = nwg <= kAmaxPartials;
+    FS4_TRY(launch_rowred((const uint16_t *)dY, w.Ut, M, r, N, 1.0f, w.P, w.partials,
+                          fuse ? w.qws : nullptr, s));
+    if (fuse)
+      FS4_TRY(launch_quantize_encode(dY, FS4_BF16, M, N, &w.dy_row, &w.dy_col, w.qws, (int)nwg, s));
+    else
+      FS4_TRY(launch_quantize(dY, FS4_BF16, M, N, &w.dy_row, &w.dy_col, w.qws, s));
     lr.L = w.P;
     lr.R = (const uint16_t *)V;   // R(k, j) = V[j][k]
     lr.r = r;
     lr.r_sn = 1;
     lr.r_sj = K;
     lr.l_scale = beta;
+  } else {
+    FS4_TRY(launch_quantize(dY, FS4_BF16, M, N, &w.dy_row, &w.dy_col, w.qws, s));
   }
   FS4_TRY(launch_gemm_nt(w.dy_row, *R_col, 1.0f, nullptr, 0.0f, dX, lr, s));
   FS4_TRY(launch_gemm_nt(w.dy_col, *X_col, 1.0f, nullptr, 0.0f, dW, LowRankEpilogue(), s));
+  // column contractions over the M tokens
   if (r > 0 && dU) {
     // dU[n][j] = beta sum_m dY[m][n] T[m][j]
-    FS4_TRY(launch_small_gemm(dY, false, 1, N, T, true, 1, r, N, r, M, beta, dU, false,
-                              w.partials, s));
+    FS4_TRY(launch_colred((const uint16_t *)dY, T, M, N, r, beta, dU, false, w.partials, w.bt, s));
   }
   if (r > 0 && dV) {
     // dV[j][k] = beta sum_m P[m][j] X[m][k]
-    FS4_TRY(launch_small_gemm(w.P, true, 1, r, X, false, 1, K, r, K, M, beta, dV, false,
-                              w.partials, s));
+    FS4_TRY(launch_colred((const uint16_t *)X, w.P, M, K, r, beta, dV, true, w.partials, w.bt, s));
   }
   return FS4_OK;
 }

@@ -97,6 +97,11 @@ size_t quantize_ws_bytes();
 fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                            const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                            void *ws, hipStream_t s);
+// The encode pass alone, for a caller whose earlier kernel already wrote npart
+// (1..kAmaxPartials) partial maxima of |x| (fp32 bits) that cover all of x.
+fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
+                                  const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
+                                  const uint32_t *partials, int npart, hipStream_t s);
 
 struct LowRankEpilogue {
   const float *L = nullptr;     // fp32 [M][r], scaled by l_scale before use
@@ -112,11 +117,31 @@ fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, c
 // Q(b, k) = Q[b*q_sb + k*q_sk]; each operand bf16 or fp32 (p_f32 / q_f32);
 // Kc a multiple of 16.  Written row-major [Na][Nb], or [Nb][Na] when
 // transpose_out.  `partials` needs small_gemm_partials_bytes(Na, Nb, Kc).
+// With amax_parts, the kernel also writes one partial maximum of |P| per
+// workgroup (small_gemm_workgroups of them, which together cover all of P).
 size_t small_gemm_partials_bytes(int64_t Na, int64_t Nb, int64_t Kc);
+int64_t small_gemm_workgroups(int64_t Na, int64_t Nb, int64_t Kc);
 fs4_status launch_small_gemm(const void *P, bool p_f32, int64_t p_sa, int64_t p_sk, const void *Q,
                              bool q_f32, int64_t q_sb, int64_t q_sk, int64_t Na, int64_t Nb,
                              int64_t Kc, float scale, float *out, bool transpose_out,
-                             float *partials, hipStream_t s);
+                             float *partials, hipStream_t s, uint32_t *amax_parts = nullptr);
+// Skinny rank-r products (r <= 64), bandwidth-shaped:
+//   rowred: out[a][j] = scale * sum_k A[a][k] B[j][k], A bf16 [Na][K], B bf16
+//           [r][K] (K % 16 == 0, 16-byte aligned rows); optional amax
+//           partials of A (rowred_workgroups of them).
+//   colred: out[c][j] = scale * sum_m A[m][c] Bm[m][j], A bf16 [M][C] (C % 8
+//           == 0, M % 8 == 0), Bm fp32 [M][r]; written [C][r] or, with
+//           transpose_out, [r][C].  `bt` is scratch for 2 * M * r BF16.
+size_t rowred_partials_bytes(int64_t Na, int r, int64_t K);
+int64_t rowred_workgroups(int64_t Na, int64_t K);
+fs4_status launch_rowred(const uint16_t *A, const uint16_t *B, int64_t Na, int r, int64_t K,
+                         float scale, float *out, float *partials, uint32_t *amax_parts,
+                         hipStream_t s);
+size_t colred_partials_bytes(int64_t M, int64_t C, int r);
+fs4_status launch_colred(const uint16_t *A, const float *Bm, int64_t M, int64_t C, int r,
+                         float scale, float *out, bool transpose_out, float *partials,
+                         uint16_t *bt, hipStream_t s);
+fs4_status launch_transpose_rank(const uint16_t *U, int64_t N, int r, uint16_t *Ut, hipStream_t s);
 // Frobenius normalisation X = G / (||G||_F + eps), fp64 accumulation
 size_t normalize_ws_bytes();
 fs4_status launch_normalize(const void *G, fs4_dtype dt, int64_t n, float eps, float *X,

@@ -56,6 +56,7 @@ constexpr int kBK = 128;          // k-tile in elements
 constexpr int kRowBytes = 64;     // code bytes per row per k-tile
 constexpr int kLdsStride = 80;    // padded LDS row stride (conflict-free 16-byte reads)
 constexpr int kXcds = 8;
+constexpr int kLrStrideMax = 72;  // epilogue LDS row stride (BF16 elements) for rank <= 64
 constexpr int kGroupM = 8;
 
 struct GemmArgs {
@@ -142,7 +143,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int A_BYTES = BM * kLdsStride, B_BYTES = BN * kLdsStride;
   constexpr int STAGE = A_BYTES + B_BYTES + BM * 8 + BN * 8;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  constexpr int LR_BYTES = (2 * BM + BN) * kLrStrideMax * 2;   // rank-r staging in the epilogue
+  constexpr int LDS_BYTES = 2 * STAGE > LR_BYTES ? 2 * STAGE : LR_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ uint2 scale_lut[256];
 
   const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
@@ -314,35 +317,31 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   }
 
   // ---- epilogue ---------------------------------------------------------------
-  // C = alpha s_tA s_tB acc + (rank-r term) + beta_e E.  The rank-r term runs
-  // as BF16 MFMA k-steps on the hi/lo split of l_scale * L against R: per
-  // chunk of 32 rank columns the workgroup stages its L rows (as hi and lo
-  // BF16) and R rows in the LDS the main loop no longer needs, with every
-  // load in flight at once, then each wave adds its tiles from LDS.
+  // C = alpha s_tA s_tB acc + (rank-r term) + beta_e E, one 32x32 tile at a
+  // time.  The rank-r term runs as BF16 MFMA k-steps on the hi/lo split of
+  // l_scale * L against R.  The workgroup first stages its L rows (as hi and
+  // lo BF16) and R rows, all r <= 64 rank columns, in the LDS the main loop no
+  // longer needs, with the loads in flight together; each tile then reads its
+  // operands from LDS.
   // 32x32 accumulator layout: register e of lane l holds row
   // 8*(e/4) + 4*(l/32) + e%4, column l%32.
   const float scale = g.alpha * (*g.a_ts) * (*g.b_ts);
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] *= scale;
+  const int nchunks = (g.r + 15) / 16;                    // <= 4 (r <= 64)
+  const int lrs = (g.r <= 32 ? 32 : 64) + 8;              // 80 or 144 bytes: conflict-free 16-byte reads
+  uint16_t *lhi = (uint16_t *)lds, *llo = lhi + BM * lrs, *rt = llo + BM * lrs;
   if (g.r > 0) {
-    constexpr int LRS = 40;    // LDS row stride in BF16 elements (80 bytes: conflict-free 16-byte reads)
-    static_assert((2 * BM + BN) * LRS * 2 <= 2 * STAGE, "rank-r staging exceeds the main-loop LDS");
-    uint16_t *lhi = (uint16_t *)lds, *llo = lhi + BM * LRS, *rt = llo + BM * LRS;
     // 16-byte staging when rows are aligned (the usual case), element-wise otherwise
     const bool vec_l = g.r % 4 == 0 && ((uintptr_t)g.L & 15u) == 0;
     const bool vec_r_rows = g.r_sj == 1 && g.r_sn % 8 == 0 && ((uintptr_t)g.R & 15u) == 0;
     const bool vec_r_cols = g.r_sn == 1 && g.r_sj % 8 == 0 && g.N % 8 == 0 && ((uintptr_t)g.R & 15u) == 0;
+    auto put_l = [&](int row, int jj, float x) {
+      const uint32_t hb = float_to_bf16_rne_bits(x);
+      lhi[row * lrs + jj] = (uint16_t)hb;
+      llo[row * lrs + jj] = (uint16_t)float_to_bf16_rne_bits(x - bf16_bits_to_float(hb));
+    };
     for (int c0 = 0; c0 < g.r; c0 += 32) {
-      auto put_l = [&](int row, int jj, float x) {
-        const uint32_t hb = float_to_bf16_rne_bits(x);
-        lhi[row * LRS + jj] = (uint16_t)hb;
-        llo[row * LRS + jj] = (uint16_t)float_to_bf16_rne_bits(x - bf16_bits_to_float(hb));
-      };
       if (vec_l) {
         // BM rows x 8 four-column groups, in batches of 4 loads per thread
-        // (the accumulators stay live, so the batch is kept small)
         constexpr int NL = BM * 8 / NT, NB = NL < 4 ? NL : 4;
         static_assert(NL % NB == 0, "uneven rank-r staging");
 #pragma unroll
@@ -356,7 +355,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
           }
 #pragma unroll
           for (int q = 0; q < NB; ++q) {
-            const int e = tid + (q0 + q) * NT, row = e >> 3, jj = (e & 7) * 4;
+            const int e = tid + (q0 + q) * NT, row = e >> 3, jj = c0 + (e & 7) * 4;
             put_l(row, jj + 0, v[q].x * g.l_scale);
             put_l(row, jj + 1, v[q].y * g.l_scale);
             put_l(row, jj + 2, v[q].z * g.l_scale);
@@ -365,80 +364,69 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
         }
       } else {
         for (int e = tid; e < BM * 32; e += NT) {
-          const int row = e >> 5, jj = e & 31, j = c0 + jj;
+          const int row = e >> 5, jj = c0 + (e & 31);
           const int64_t m = m0 + row;
-          put_l(row, jj, (m < g.M && j < g.r) ? g.L[m * g.r + j] * g.l_scale : 0.0f);
+          put_l(row, jj, (m < g.M && jj < g.r) ? g.L[m * g.r + jj] * g.l_scale : 0.0f);
         }
       }
-      // R(n, j) = R[n r_sn + j r_sj], staged as rt[n][j]
-      constexpr int NR = BN * 4 / NT;          // 16-byte chunks per thread
+      // R(n, j) = R[n r_sn + j r_sj], staged as rt[n][j], one 16-byte chunk at a time
+      constexpr int NR = BN * 4 / NT;
       static_assert(BN * 4 % NT == 0, "uneven rank-r staging");
-      // (one 16-byte chunk at a time: a wider batch spills the accumulators)
       if (vec_r_rows) {
 #pragma unroll 1
         for (int q = 0; q < NR; ++q) {
-          const int e = tid + q * NT, row = e >> 2, jj = (e & 3) * 8, j = c0 + jj;
+          const int e = tid + q * NT, row = e >> 2, jj = c0 + (e & 3) * 8;
           const int64_t n = n0 + row;
-          *(uint4 *)(rt + row * LRS + jj) =
-              (n < g.N && j < g.r) ? *(const uint4 *)(g.R + n * g.r_sn + j) : make_uint4(0, 0, 0, 0);
+          *(uint4 *)(rt + row * lrs + jj) =
+              (n < g.N && jj < g.r) ? *(const uint4 *)(g.R + n * g.r_sn + jj) : make_uint4(0, 0, 0, 0);
         }
       } else if (vec_r_cols) {
         // eight consecutive n for one rank column j, written transposed
 #pragma unroll 1
         for (int q = 0; q < NR; ++q) {
-          const int e = tid + q * NT, jj = e / (BN / 8), n8 = (e % (BN / 8)) * 8, j = c0 + jj;
+          const int e = tid + q * NT, jj = c0 + e / (BN / 8), n8 = (e % (BN / 8)) * 8;
           const int64_t n = n0 + n8;
-          const uint4 v = (n < g.N && j < g.r) ? *(const uint4 *)(g.R + (int64_t)j * g.r_sj + n) : make_uint4(0, 0, 0, 0);
+          const uint4 v = (n < g.N && jj < g.r) ? *(const uint4 *)(g.R + (int64_t)jj * g.r_sj + n) : make_uint4(0, 0, 0, 0);
           const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            rt[(n8 + 2 * t) * LRS + jj] = (uint16_t)(w[t] & 0xFFFFu);
-            rt[(n8 + 2 * t + 1) * LRS + jj] = (uint16_t)(w[t] >> 16);
+            rt[(n8 + 2 * t) * lrs + jj] = (uint16_t)(w[t] & 0xFFFFu);
+            rt[(n8 + 2 * t + 1) * lrs + jj] = (uint16_t)(w[t] >> 16);
           }
         }
       } else {
         for (int e = tid; e < BN * 32; e += NT) {
-          const int row = e >> 5, jj = e & 31, j = c0 + jj;
+          const int row = e >> 5, jj = c0 + (e & 31);
           const int64_t n = n0 + row;
-          rt[row * LRS + jj] = (n < g.N && j < g.r) ? g.R[n * g.r_sn + (int64_t)j * g.r_sj] : (uint16_t)0;
+          rt[row * lrs + jj] = (n < g.N && jj < g.r) ? g.R[n * g.r_sn + (int64_t)jj * g.r_sj] : (uint16_t)0;
         }
       }
-      __syncthreads();
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        if (c0 + c * 16 < g.r) {
-          bf16x8_t ah[TM], al[TM];
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            const int row = wm * TM * 32 + i * 32 + l32;
-            ah[i] = *(const bf16x8_t *)(lhi + row * LRS + c * 16 + 8 * h);
-            al[i] = *(const bf16x8_t *)(llo + row * LRS + c * 16 + 8 * h);
-          }
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const int row = wn * TN * 32 + j * 32 + l32;
-            const bf16x8_t rv = *(const bf16x8_t *)(rt + row * LRS + c * 16 + 8 * h);
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], rv, acc[i][j], 0, 0, 0);
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], rv, acc[i][j], 0, 0, 0);
-            }
-          }
-        }
-      }
-      __syncthreads();
     }
+    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int arow = wm * TM * 32 + i * 32 + l32;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int64_t n = n0 + wn * TN * 32 + j * 32 + l32;
+      const int brow = wn * TN * 32 + j * 32 + l32;
+      floatx16_t t = acc[i][j] * scale;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c < nchunks) {
+          const bf16x8_t ah = *(const bf16x8_t *)(lhi + arow * lrs + c * 16 + 8 * h);
+          const bf16x8_t al = *(const bf16x8_t *)(llo + arow * lrs + c * 16 + 8 * h);
+          const bf16x8_t rv = *(const bf16x8_t *)(rt + brow * lrs + c * 16 + 8 * h);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, rv, t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, rv, t, 0, 0, 0);
+        }
+      }
+      const int64_t n = n0 + brow;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
         if (m < g.M && n < g.N) {
-          float v = acc[i][j][e];
+          float v = t[e];
           if (g.E) v += g.beta_e * g.E[m * g.N + n];
           g.C[m * g.N + n] = v;
         }

@@ -75,9 +75,18 @@ __device__ inline void load8(const void *base, int64_t row_off, int64_t sk, int6
   }
 }
 
-template <bool P_F32, bool P_CONTIG, bool Q_F32, bool Q_CONTIG>
-__global__ __launch_bounds__(256) void small_gemm_kernel(SmallGemm g) {
+// One workgroup: a 32 x 32 tile of `out` over one k chunk, split over its 4
+// waves.  Each wave issues the loads of kUnroll 16-k steps before converting
+// and multiplying them, so several loads per lane are in flight.  With
+// AMAX, the workgroup also writes the largest |P| it loaded (as fp32 bits) to
+// amax_parts[its linear id]: when the grid covers P exactly once (one tile
+// column), these are the tensor-amax partials of P.
+constexpr int kUnroll = 4;
+
+template <bool P_F32, bool P_CONTIG, bool Q_F32, bool Q_CONTIG, bool AMAX>
+__global__ __launch_bounds__(256) void small_gemm_kernel(SmallGemm g, uint32_t *amax_parts) {
   __shared__ float red[3][64][17];
+  __shared__ uint32_t mred[4];
   const int64_t tiles_b = (g.Nb + 31) / 32;
   const int64_t ta = blockIdx.x / tiles_b, tb = blockIdx.x % tiles_b;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -91,26 +100,47 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallGemm g) {
   floatx16_t acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  float pmax = 0.0f;
 
-  for (int64_t k0 = kbeg; k0 < kend; k0 += 16) {
-    const int64_t k = k0 + 8 * h;
-    float pv[8], qv[8];
-    load8<P_F32, P_CONTIG>(g.P, a * g.p_sa, g.p_sk, k, a < g.Na, pv);
-    load8<Q_F32, Q_CONTIG>(g.Q, b * g.q_sb, g.q_sk, k, b < g.Nb, qv);
-    uint32_t ph[8], pl[8], qh[8], ql[8];
+  for (int64_t k0 = kbeg; k0 < kend; k0 += 16 * kUnroll) {
+    float pv[kUnroll][8], qv[kUnroll][8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      ph[q] = float_to_bf16_rne_bits(pv[q]);
-      qh[q] = float_to_bf16_rne_bits(qv[q]);
-      if constexpr (P_F32) pl[q] = float_to_bf16_rne_bits(pv[q] - bf16_bits_to_float(ph[q]));
-      if constexpr (Q_F32) ql[q] = float_to_bf16_rne_bits(qv[q] - bf16_bits_to_float(qh[q]));
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t k = k0 + 16 * u + 8 * h;
+      const bool in = k0 + 16 * u < kend;       // kend - kbeg is a multiple of 16
+      load8<P_F32, P_CONTIG>(g.P, a * g.p_sa, g.p_sk, k, in && a < g.Na, pv[u]);
+      load8<Q_F32, Q_CONTIG>(g.Q, b * g.q_sb, g.q_sk, k, in && b < g.Nb, qv[u]);
     }
-    const bf16x8_t fph = make_frag(ph), fqh = make_frag(qh);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fph, fqh, acc, 0, 0, 0);
-    if constexpr (P_F32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(make_frag(pl), fqh, acc, 0, 0, 0);
-    if constexpr (Q_F32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fph, make_frag(ql), acc, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (k0 + 16 * u < kend) {
+        uint32_t ph[8], pl[8], qh[8], ql[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if constexpr (AMAX) pmax = fmaxf(pmax, fabsf(pv[u][q]));
+          ph[q] = float_to_bf16_rne_bits(pv[u][q]);
+          qh[q] = float_to_bf16_rne_bits(qv[u][q]);
+          if constexpr (P_F32) pl[q] = float_to_bf16_rne_bits(pv[u][q] - bf16_bits_to_float(ph[q]));
+          if constexpr (Q_F32) ql[q] = float_to_bf16_rne_bits(qv[u][q] - bf16_bits_to_float(qh[q]));
+        }
+        const bf16x8_t fph = make_frag(ph), fqh = make_frag(qh);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fph, fqh, acc, 0, 0, 0);
+        if constexpr (P_F32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(make_frag(pl), fqh, acc, 0, 0, 0);
+        if constexpr (Q_F32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fph, make_frag(ql), acc, 0, 0, 0);
+      }
+    }
   }
 
+  if constexpr (AMAX) {
+    // |x| as fp32 bits is monotone; lanes holding no rows contribute 0
+    uint32_t mv = __builtin_bit_cast(uint32_t, pmax);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t o = __shfl_xor(mv, off, 64);
+      mv = mv > o ? mv : o;
+    }
+    if (lane == 0) mred[wave] = mv;
+  }
   if (wave > 0) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) red[wave - 1][lane][e] = acc[e];
@@ -126,6 +156,14 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallGemm g) {
     for (int e = 0; e < 16; ++e) {
       const int64_t ra = ta * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
       if (ra < g.Na && b < g.Nb) out[ra * g.Nb + b] = acc[e];
+    }
+    if constexpr (AMAX) {
+      if (lane == 0) {
+        uint32_t m = mred[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) m = m > mred[w] ? m : mred[w];
+        amax_parts[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m;
+      }
     }
   }
 }
@@ -157,10 +195,13 @@ int64_t pick_splits(int64_t tiles, int64_t Kc, int64_t *kchunk) {
 
 template <bool PF, bool PC, bool QF, bool QC>
 fs4_status run_small(const SmallGemm &g0, int64_t S, float scale, float *out, bool transpose_out,
-                     hipStream_t s) {
+                     uint32_t *amax_parts, hipStream_t s) {
   const int64_t tiles = ((g0.Na + 31) / 32) * ((g0.Nb + 31) / 32);
   dim3 grid((unsigned)tiles, (unsigned)S);
-  small_gemm_kernel<PF, PC, QF, QC><<<grid, 256, 0, s>>>(g0);
+  if (amax_parts)
+    small_gemm_kernel<PF, PC, QF, QC, true><<<grid, 256, 0, s>>>(g0, amax_parts);
+  else
+    small_gemm_kernel<PF, PC, QF, QC, false><<<grid, 256, 0, s>>>(g0, nullptr);
   const int64_t n = g0.Na * g0.Nb;
   reduce_partials_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(g0.partials, (int)S, g0.Na,
                                                                       g0.Nb, scale, out,
@@ -170,22 +211,284 @@ fs4_status run_small(const SmallGemm &g0, int64_t S, float scale, float *out, bo
 
 template <bool PF, bool PC, bool QF>
 fs4_status dispatch_q(bool qc, const SmallGemm &g, int64_t S, float scale, float *out, bool t,
-                      hipStream_t s) {
-  return qc ? run_small<PF, PC, QF, true>(g, S, scale, out, t, s)
-            : run_small<PF, PC, QF, false>(g, S, scale, out, t, s);
+                      uint32_t *am, hipStream_t s) {
+  return qc ? run_small<PF, PC, QF, true>(g, S, scale, out, t, am, s)
+            : run_small<PF, PC, QF, false>(g, S, scale, out, t, am, s);
 }
 template <bool PF, bool PC>
 fs4_status dispatch_qf(bool qf, bool qc, const SmallGemm &g, int64_t S, float scale, float *out,
-                       bool t, hipStream_t s) {
-  return qf ? dispatch_q<PF, PC, true>(qc, g, S, scale, out, t, s)
-            : dispatch_q<PF, PC, false>(qc, g, S, scale, out, t, s);
+                       bool t, uint32_t *am, hipStream_t s) {
+  return qf ? dispatch_q<PF, PC, true>(qc, g, S, scale, out, t, am, s)
+            : dispatch_q<PF, PC, false>(qc, g, S, scale, out, t, am, s);
 }
 fs4_status dispatch_small(bool pf, bool pc, bool qf, bool qc, const SmallGemm &g, int64_t S,
-                          float scale, float *out, bool t, hipStream_t s) {
-  if (pf) return pc ? dispatch_qf<true, true>(qf, qc, g, S, scale, out, t, s)
-                    : dispatch_qf<true, false>(qf, qc, g, S, scale, out, t, s);
-  return pc ? dispatch_qf<false, true>(qf, qc, g, S, scale, out, t, s)
-            : dispatch_qf<false, false>(qf, qc, g, S, scale, out, t, s);
+                          float scale, float *out, bool t, uint32_t *am, hipStream_t s) {
+  if (pf) return pc ? dispatch_qf<true, true>(qf, qc, g, S, scale, out, t, am, s)
+                    : dispatch_qf<true, false>(qf, qc, g, S, scale, out, t, am, s);
+  return pc ? dispatch_qf<false, true>(qf, qc, g, S, scale, out, t, am, s)
+            : dispatch_qf<false, false>(qf, qc, g, S, scale, out, t, am, s);
+}
+
+// ---------------------------------------------------------------------------
+// Skinny products for the rank-r (r <= 64) side of the LoRA-SVD projection,
+// shaped for HBM bandwidth: every global load is a 16-byte word of a row
+// segment (whole cache lines per wave), operands are staged row-major in LDS
+// and the MFMA fragments are read from there.
+//
+// rowred: part[s][a][j] = sum_{k in chunk s} A[a][k] B[j][k]
+//   A bf16 [Na][K], B bf16 [r][K], both contiguous along k.  A workgroup owns
+//   64 rows of A and one k chunk, walked in 128-k slabs (the next slab's loads
+//   in flight); its 4 waves take 2 row tiles x 2 k halves.  With AMAX it also
+//   writes the largest |A| it read (fp32 bits) to amax_parts[its linear id].
+// colred: part[s][c][j] = sum_{m in chunk s} A[m][c] Bm[m][j]
+//   A bf16 [M][C] row-major; Bm given as its transposed BF16 hi/lo split
+//   (bt_hi, bt_lo [r][M]).  A workgroup owns 128 columns and one m chunk,
+//   walked in 64-row slabs; wave w takes columns 32w..32w+31 and reads its
+//   A fragments down the LDS columns (2-byte reads, conflict-free).
+constexpr int kRrRows = 64, kRrK = 128, kRrStride = kRrK + 8;   // 272-byte LDS rows
+
+template <bool AMAX, int NJ>
+__global__ __launch_bounds__(256) void rowred_kernel(const uint16_t *__restrict__ A,
+                                                     const uint16_t *__restrict__ B, int64_t Na,
+                                                     int r, int64_t K, int64_t kchunk,
+                                                     float *__restrict__ part,
+                                                     uint32_t *__restrict__ amax_parts) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kRrRows][kRrStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[NJ * 32][kRrStride];
+  __shared__ float red[2][NJ][64][17];
+  __shared__ uint32_t mred[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int rt = wave & 1, kh = wave >> 1;
+  const int64_t a0 = (int64_t)blockIdx.x * kRrRows;
+  const int64_t kbeg = (int64_t)blockIdx.y * kchunk;
+  const int64_t kend = kbeg + kchunk < K ? kbeg + kchunk : K;
+  // slab loads: A 64 x 128 (4 words per thread), B NJ*32 x 128 (2*NJ per thread);
+  // 16 threads per 256-byte row segment
+  uint4 ga[4], gb[2 * NJ];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int idx = tid + p * 256, row = idx >> 4, seg = idx & 15;
+      const int64_t k = k0 + seg * 8;
+      ga[p] = (a0 + row < Na && k < kend) ? *(const uint4 *)(A + (a0 + row) * K + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < 2 * NJ; ++p) {
+      const int idx = tid + p * 256, j = idx >> 4, seg = idx & 15;
+      const int64_t k = k0 + seg * 8;
+      gb[p] = (j < r && k < kend) ? *(const uint4 *)(B + (int64_t)j * K + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  floatx16_t acc[NJ];
+#pragma unroll
+  for (int t = 0; t < NJ; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+  uint32_t amax = 0;    // bf16 magnitude bits
+  if (kbeg < kend) gload(kbeg);
+  for (int64_t k0 = kbeg; k0 < kend; k0 += kRrK) {
+    __syncthreads();          // the previous slab is fully read
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int idx = tid + p * 256, row = idx >> 4, seg = idx & 15;
+      *(uint4 *)&sa[row][seg * 8] = ga[p];
+      if constexpr (AMAX) {
+        const uint32_t w[4] = {ga[p].x, ga[p].y, ga[p].z, ga[p].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = w[q] & 0x7FFFu, hi = (w[q] >> 16) & 0x7FFFu;
+          const uint32_t m2 = lo > hi ? lo : hi;
+          amax = amax > m2 ? amax : m2;
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 2 * NJ; ++p) {
+      const int idx = tid + p * 256, j = idx >> 4, seg = idx & 15;
+      *(uint4 *)&sb[j][seg * 8] = gb[p];
+    }
+    __syncthreads();
+    if (k0 + kRrK < kend) gload(k0 + kRrK);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kk = kh * 64 + st * 16 + 8 * h;
+      const bf16x8_t fa = *(const bf16x8_t *)&sa[rt * 32 + l32][kk];
+#pragma unroll
+      for (int t = 0; t < NJ; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, *(const bf16x8_t *)&sb[t * 32 + l32][kk], acc[t], 0, 0, 0);
+    }
+  }
+  if constexpr (AMAX) {
+    uint32_t mv = amax << 16;   // bf16 magnitude bits -> fp32 bits
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t o = __shfl_xor(mv, off, 64);
+      mv = mv > o ? mv : o;
+    }
+    if (lane == 0) mred[wave] = mv;
+  }
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < NJ; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[rt][t][lane][e] = acc[t][e];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    float *out = part + (int64_t)blockIdx.y * Na * r;
+#pragma unroll
+    for (int t = 0; t < NJ; ++t) {
+      const int j = t * 32 + l32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t ra = a0 + rt * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (ra < Na && j < r) out[ra * r + j] = acc[t][e] + red[rt][t][lane][e];
+      }
+    }
+  }
+  if constexpr (AMAX) {
+    if (tid == 0) {
+      uint32_t m = mred[0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) m = m > mred[w] ? m : mred[w];
+      amax_parts[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m;
+    }
+  }
+}
+
+constexpr int kColBlock = 128;   // columns of A per workgroup (4 waves x 32)
+constexpr int kColSlab = 64;     // rows of A per LDS slab
+constexpr int kColAStride = kColBlock + 8;   // 272-byte LDS rows
+constexpr int kColBStride = kColSlab + 8;    // 144-byte LDS rows
+
+template <int NJ>
+__global__ __launch_bounds__(256) void colred_kernel(const uint16_t *__restrict__ A,
+                                                     const uint16_t *__restrict__ bt_hi,
+                                                     const uint16_t *__restrict__ bt_lo,
+                                                     int64_t M, int64_t C, int r, int64_t mchunk,
+                                                     float *__restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kColSlab][kColAStride];   // A slab [m][c]
+  __shared__ __attribute__((aligned(16))) uint16_t sh[NJ * 32][kColBStride];    // Bm^T hi [j][m]
+  __shared__ __attribute__((aligned(16))) uint16_t sl[NJ * 32][kColBStride];    // Bm^T lo [j][m]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t c0 = (int64_t)blockIdx.x * kColBlock;
+  const int64_t mbeg = (int64_t)blockIdx.y * mchunk;
+  const int64_t mend = mbeg + mchunk < M ? mbeg + mchunk : M;
+  // slab loads: A 64 x 128 (4 words per thread, 16 threads per row segment);
+  // Bm^T hi and lo NJ*32 x 64 (NJ words each per thread, 8 threads per row)
+  uint4 ga[4], gh[NJ], gl[NJ];
+  auto gload = [&](int64_t m0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int idx = tid + p * 256, row = idx >> 4, seg = idx & 15;
+      const int64_t m = m0 + row, c = c0 + seg * 8;
+      ga[p] = (m < mend && c < C) ? *(const uint4 *)(A + m * C + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < NJ; ++p) {
+      const int idx = tid + p * 256, j = idx >> 3, seg = idx & 7;
+      const int64_t m = m0 + seg * 8;
+      const bool in = j < r && m < mend;
+      gh[p] = in ? *(const uint4 *)(bt_hi + (int64_t)j * M + m) : make_uint4(0, 0, 0, 0);
+      gl[p] = in ? *(const uint4 *)(bt_lo + (int64_t)j * M + m) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  floatx16_t acc[NJ];
+#pragma unroll
+  for (int t = 0; t < NJ; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+  if (mbeg < mend) gload(mbeg);
+  const int col = wave * 32 + l32;
+  for (int64_t m0 = mbeg; m0 < mend; m0 += kColSlab) {
+    __syncthreads();            // the previous slab is fully read
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int idx = tid + p * 256, row = idx >> 4, seg = idx & 15;
+      *(uint4 *)&sa[row][seg * 8] = ga[p];
+    }
+#pragma unroll
+    for (int p = 0; p < NJ; ++p) {
+      const int idx = tid + p * 256, j = idx >> 3, seg = idx & 7;
+      *(uint4 *)&sh[j][seg * 8] = gh[p];
+      *(uint4 *)&sl[j][seg * 8] = gl[p];
+    }
+    __syncthreads();
+    if (m0 + kColSlab < mend) gload(m0 + kColSlab);   // next slab in flight during the MFMAs
+#pragma unroll
+    for (int st = 0; st < kColSlab / 16; ++st) {
+      const int mm = st * 16 + 8 * h;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = (uint32_t)sa[mm + 2 * q][col] | ((uint32_t)sa[mm + 2 * q + 1][col] << 16);
+      const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+      for (int t = 0; t < NJ; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, *(const bf16x8_t *)&sh[t * 32 + l32][mm], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, *(const bf16x8_t *)&sl[t * 32 + l32][mm], acc[t], 0, 0, 0);
+      }
+    }
+  }
+  float *out = part + (int64_t)blockIdx.y * C * r;
+#pragma unroll
+  for (int t = 0; t < NJ; ++t) {
+    const int j = t * 32 + l32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t c = c0 + wave * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (c < C && j < r) out[c * r + j] = acc[t][e];
+    }
+  }
+}
+
+// Bm fp32 [M][r] -> transposed BF16 hi and lo parts [r][M] (Bm = hi + lo +
+// O(2^-17 |Bm|))
+__global__ void split_transpose_kernel(const float *__restrict__ Bm, int64_t M, int r,
+                                       uint16_t *__restrict__ hi, uint16_t *__restrict__ lo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * r) return;
+  const int64_t j = i / M, m = i % M;
+  const float x = Bm[m * r + j];
+  const uint32_t hb = float_to_bf16_rne_bits(x);
+  hi[i] = (uint16_t)hb;
+  lo[i] = (uint16_t)float_to_bf16_rne_bits(x - bf16_bits_to_float(hb));
+}
+
+// U [N][r] -> U^T [r][N] (bf16)
+__global__ void transpose_rank_kernel(const uint16_t *__restrict__ U, int64_t N, int r,
+                                      uint16_t *__restrict__ Ut) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N * r) return;
+  const int64_t j = i / N, n = i % N;
+  Ut[i] = U[n * r + j];
+}
+
+int64_t rowred_splits(int64_t Na, int64_t K, int64_t *kchunk) {
+  const int64_t blocks = (Na + kRrRows - 1) / kRrRows;
+  // >= 1024 workgroups when K allows, chunks of whole 128-k slabs
+  int64_t S = (1024 + blocks - 1) / blocks;
+  const int64_t maxS = (K + kRrK - 1) / kRrK;
+  if (S > maxS) S = maxS;
+  if (S < 1) S = 1;
+  int64_t kc = (K + S - 1) / S;
+  kc = (kc + kRrK - 1) / kRrK * kRrK;
+  *kchunk = kc;
+  return (K + kc - 1) / kc;
+}
+
+int64_t colred_splits(int64_t M, int64_t C, int64_t *mchunk) {
+  const int64_t blocks = (C + kColBlock - 1) / kColBlock;
+  int64_t S = (1024 + blocks - 1) / blocks;
+  const int64_t maxS = (M + kColSlab - 1) / kColSlab;
+  if (S > maxS) S = maxS;
+  if (S < 1) S = 1;
+  int64_t mc = (M + S - 1) / S;
+  mc = (mc + kColSlab - 1) / kColSlab * kColSlab;
+  *mchunk = mc;
+  return (M + mc - 1) / mc;
 }
 
 }  // namespace
@@ -193,7 +496,7 @@ fs4_status dispatch_small(bool pf, bool pc, bool qf, bool qc, const SmallGemm &g
 fs4_status launch_small_gemm(const void *P, bool p_f32, int64_t p_sa, int64_t p_sk, const void *Q,
                              bool q_f32, int64_t q_sb, int64_t q_sk, int64_t Na, int64_t Nb,
                              int64_t Kc, float scale, float *out, bool transpose_out,
-                             float *partials, hipStream_t s) {
+                             float *partials, hipStream_t s, uint32_t *amax_parts) {
   if (Na == 0 || Nb == 0) return FS4_OK;
   SmallGemm g;
   g.P = P; g.p_sa = p_sa; g.p_sk = p_sk;
@@ -204,7 +507,68 @@ fs4_status launch_small_gemm(const void *P, bool p_f32, int64_t p_sa, int64_t p_
   // vector loads along k need unit k-stride and 8-element aligned rows
   const bool pc = p_sk == 1 && (p_sa % 8 == 0 || Na == 1);
   const bool qc = q_sk == 1 && (q_sb % 8 == 0 || Nb == 1);
-  return dispatch_small(p_f32, pc, q_f32, qc, g, S, scale, out, transpose_out, s);
+  return dispatch_small(p_f32, pc, q_f32, qc, g, S, scale, out, transpose_out, amax_parts, s);
+}
+
+int64_t small_gemm_workgroups(int64_t Na, int64_t Nb, int64_t Kc) {
+  const int64_t tiles = ((Na + 31) / 32) * ((Nb + 31) / 32);
+  int64_t kc;
+  return tiles * pick_splits(tiles, Kc, &kc);
+}
+
+size_t rowred_partials_bytes(int64_t Na, int r, int64_t K) {
+  int64_t kc;
+  return (size_t)(rowred_splits(Na, K, &kc) * Na * r) * sizeof(float);
+}
+int64_t rowred_workgroups(int64_t Na, int64_t K) {
+  int64_t kc;
+  return ((Na + kRrRows - 1) / kRrRows) * rowred_splits(Na, K, &kc);
+}
+fs4_status launch_rowred(const uint16_t *A, const uint16_t *B, int64_t Na, int r, int64_t K,
+                         float scale, float *out, float *partials, uint32_t *amax_parts,
+                         hipStream_t s) {
+  if (Na == 0 || r == 0) return FS4_OK;
+  int64_t kc;
+  const int64_t S = rowred_splits(Na, K, &kc);
+  dim3 grid((unsigned)((Na + kRrRows - 1) / kRrRows), (unsigned)S);
+  if (r <= 32) {
+    if (amax_parts) rowred_kernel<true, 1><<<grid, 256, 0, s>>>(A, B, Na, r, K, kc, partials, amax_parts);
+    else rowred_kernel<false, 1><<<grid, 256, 0, s>>>(A, B, Na, r, K, kc, partials, nullptr);
+  } else {
+    if (amax_parts) rowred_kernel<true, 2><<<grid, 256, 0, s>>>(A, B, Na, r, K, kc, partials, amax_parts);
+    else rowred_kernel<false, 2><<<grid, 256, 0, s>>>(A, B, Na, r, K, kc, partials, nullptr);
+  }
+  const int64_t n = Na * r;
+  reduce_partials_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(partials, (int)S, Na, r, scale,
+                                                                      out, false);
+  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+}
+size_t colred_partials_bytes(int64_t M, int64_t C, int r) {
+  int64_t mc;
+  return (size_t)(colred_splits(M, C, &mc) * C * r) * sizeof(float);
+}
+fs4_status launch_colred(const uint16_t *A, const float *Bm, int64_t M, int64_t C, int r,
+                         float scale, float *out, bool transpose_out, float *partials,
+                         uint16_t *bt, hipStream_t s) {
+  if (C == 0 || r == 0) return FS4_OK;
+  uint16_t *bt_hi = bt, *bt_lo = bt + M * r;
+  const int64_t nb = M * r;
+  split_transpose_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, s>>>(Bm, M, r, bt_hi, bt_lo);
+  int64_t mc;
+  const int64_t S = colred_splits(M, C, &mc);
+  dim3 grid((unsigned)((C + kColBlock - 1) / kColBlock), (unsigned)S);
+  if (r <= 32) colred_kernel<1><<<grid, 256, 0, s>>>(A, bt_hi, bt_lo, M, C, r, mc, partials);
+  else colred_kernel<2><<<grid, 256, 0, s>>>(A, bt_hi, bt_lo, M, C, r, mc, partials);
+  const int64_t n = C * r;
+  reduce_partials_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(partials, (int)S, C, r, scale,
+                                                                      out, transpose_out);
+  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+}
+fs4_status launch_transpose_rank(const uint16_t *U, int64_t N, int r, uint16_t *Ut, hipStream_t s) {
+  const int64_t n = N * r;
+  if (n == 0) return FS4_OK;
+  transpose_rank_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(U, N, r, Ut);
+  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 
 size_t small_gemm_partials_bytes(int64_t Na, int64_t Nb, int64_t Kc) {

@@ -466,29 +466,18 @@ __global__ void write_zero_scale_kernel(float *a, float *b) {
 
 size_t quantize_ws_bytes() { return kAmaxPartials * sizeof(uint32_t); }
 
-fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
-                           const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise, void *ws,
-                           hipStream_t s) {
+fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
+                                  const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
+                                  const uint32_t *partials, int npart, hipStream_t s) {
   const fs4_nvfp4 none = {nullptr, nullptr, nullptr, 0, 0};
   const fs4_nvfp4 rv = rowwise ? *rowwise : none;
   const fs4_nvfp4 cv = colwise ? *colwise : none;
-  if (rows == 0 || cols == 0) {
-    write_zero_scale_kernel<<<1, 1, 0, s>>>(rv.tscale, cv.tscale);
-    return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
-  }
   const bool bf16 = dt == FS4_BF16;
-  const int64_t n = rows * cols;
-  const int64_t nvec = n / (bf16 ? 8 : 4);
-  const int64_t g = (nvec + kThreads * kAmaxUnroll * 2 - 1) / (kThreads * kAmaxUnroll * 2);
-  const int npart = (int)(g < 1 ? 1 : (g > kAmaxPartials ? kAmaxPartials : g));
-  uint32_t *partials = (uint32_t *)ws;
   // one workgroup per tile slot (4 x 4 tiles per super-tile), at most kEncodeGrid
   const int64_t slots = ((rows + 4 * kTile - 1) / (4 * kTile)) * ((cols + 4 * kTile - 1) / (4 * kTile)) * 16;
   const unsigned grid = (unsigned)(slots < kEncodeGrid ? slots : kEncodeGrid);   // multiple of 16
   static_assert(kEncodeGrid % 16 == 0, "the tile walk needs a grid that is a multiple of 16");
   const bool row = rv.codes != nullptr, col = cv.codes != nullptr;
-  if (bf16) amax_partial_kernel<true><<<npart, kThreads, 0, s>>>((const uint4 *)x, nvec, partials);
-  else amax_partial_kernel<false><<<npart, kThreads, 0, s>>>((const uint4 *)x, nvec, partials);
 #define FS4_QK(B, R, C) quantize_kernel<B, R, C><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv)
   if (bf16) {
     if (row && col) FS4_QK(true, true, true);
@@ -501,6 +490,26 @@ fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t co
   }
 #undef FS4_QK
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+}
+
+fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
+                           const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise, void *ws,
+                           hipStream_t s) {
+  if (rows == 0 || cols == 0) {
+    write_zero_scale_kernel<<<1, 1, 0, s>>>(rowwise ? rowwise->tscale : nullptr,
+                                             colwise ? colwise->tscale : nullptr);
+    return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+  }
+  const bool bf16 = dt == FS4_BF16;
+  const int64_t n = rows * cols;
+  const int64_t nvec = n / (bf16 ? 8 : 4);
+  const int64_t g = (nvec + kThreads * kAmaxUnroll * 2 - 1) / (kThreads * kAmaxUnroll * 2);
+  const int npart = (int)(g < 1 ? 1 : (g > kAmaxPartials ? kAmaxPartials : g));
+  uint32_t *partials = (uint32_t *)ws;
+  if (bf16) amax_partial_kernel<true><<<npart, kThreads, 0, s>>>((const uint4 *)x, nvec, partials);
+  else amax_partial_kernel<false><<<npart, kThreads, 0, s>>>((const uint4 *)x, nvec, partials);
+  if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
+  return launch_quantize_encode(x, dt, rows, cols, rowwise, colwise, partials, npart, s);
 }
 
 }  // namespace fs4
