@@ -1,6 +1,7 @@
 """Benchmark of the NVFP4 linear-projection hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+    python bench.py --only {gemm,quantizer,copy}     (one leg alone, for profilers)
 
 One step is one pass of the whole hot path over one batch of synthetic input
 at the 3B-shape projection (X 8192 x 3072 bf16, W 8192 x 3072 with a rank-32
@@ -21,12 +22,20 @@ with HIP events around its own launches at the three step shapes), the
 quantizer's HBM GB/s on the 4096 x 4096 workload (both layouts, inputs rotated
 through 12 copies so every call reads from HBM), the 5-step NVFP4
 Newton-Schulz on 3072 x 8192, and the CPU oracle timed on a bounded sample.
+
+The GEMM's HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
+counter runs of ``--only gemm``, scaled by what the same counters read for a
+plain device copy of known size (``--only copy``); the summary under
+profiles/ records the SHA-256 of the GEMM source it was taken on, and the
+figure is reported only while the source is unchanged (null otherwise).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -65,7 +74,29 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the quantizer/NS/roofline legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["gemm", "quantizer", "copy"],
+                    help="run one leg alone (for counter runs under a profiler) and exit")
     return ap.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nt_traffic_3b.md")
+GEMM_SOURCE = os.path.join(ROOT, "precision_pretraining_amd", "csrc", "gemm.hip")
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch (average over the three step shapes) from the
+    committed counter summary, or None when it is missing or was taken on
+    another version of the GEMM source."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        digest = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"source sha256: ([0-9a-f]{64})", text)
+    t = re.search(r"bytes per launch \(scaled\): ([0-9.]+)", text)
+    if not m or not t or m.group(1) != digest:
+        return None
+    return float(t.group(1))
 
 
 def cpu_baseline():
@@ -108,9 +139,20 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
 
     def to_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if a.only == "copy":
+        # plain device copy of known size, the scale for the traffic counters
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4}))
+        return
 
     d = synth.linear3b()
     X, U, V = to_bf16(d["X"]), to_bf16(d["U"]), to_bf16(d["V"])
@@ -122,6 +164,64 @@ def main():
     R_row = fs4.NVFP4.empty(N, K, dev)
     R_col = fs4.NVFP4.empty(K, N, dev, R_row.tscale)
 
+    def gemm_leg(reps):
+        # the dominant kernel alone at the three step shapes, HIP events
+        # around each launch on the stream it runs on
+        fs4.quantize(Rw, out_row=R_row, out_col=R_col)
+        X_row, X_col = fs4.quantize(X)
+        dY_row, dY_col = fs4.quantize(dY)
+        shapes = [(X_row, R_row), (dY_row, R_col), (dY_col, X_col)]
+        Cs = [torch.empty((A.rows, B.rows), dtype=torch.float32, device=dev) for A, B in shapes]
+        for (A, B), C in zip(shapes, Cs):
+            fs4.gemm_nt(A, B, out=C)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * 3)]
+        i = 0
+        for _ in range(reps):
+            for (A, B), C in zip(shapes, Cs):
+                ev[i][0].record(stream)
+                fs4.gemm_nt(A, B, out=C)
+                ev[i][1].record(stream)
+                i += 1
+        torch.cuda.synchronize()
+        gemm_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+        gemm_flop = 2.0 * M * N * K
+        ach = gemm_flop / (gemm_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": "gemm_nt_kernel (block-scaled NVFP4 NT GEMM)",
+                "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": gemm_traffic(),
+                "per_launch": "8192x8192x3072 = %.1f GFLOP" % (gemm_flop / 1e9),
+                "avg_launch_ms": round(gemm_ms, 4)}
+
+    def quantizer_leg(qreps=48):
+        qb = synth.quantizer_input()
+        copies = [to_bf16(qb) for _ in range(12)]
+        rows_q, cols_q = qb.shape
+        qrow = fs4.NVFP4.empty(rows_q, cols_q, dev)
+        qcol = fs4.NVFP4.empty(cols_q, rows_q, dev, qrow.tscale)
+        for c in copies[:3]:
+            fs4.quantize(c, out_row=qrow, out_col=qcol)
+        torch.cuda.synchronize()
+        qe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(qreps)]
+        for j in range(qreps):
+            qe[j][0].record(stream)
+            fs4.quantize(copies[j % len(copies)], out_row=qrow, out_col=qcol)
+            qe[j][1].record(stream)
+        torch.cuda.synchronize()
+        q_ms = float(np.mean([s.elapsed_time(e) for s, e in qe]))
+        q_gbs = quantizer_bytes(rows_q, cols_q) / (q_ms * 1e-3) / 1e9
+        return {"workload": "4096x4096 bf16 ~N(0,1), 0.1% x50; row+col layouts",
+                "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(q_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(q_ms * 1e3, 2),
+                "bytes_per_call": quantizer_bytes(rows_q, cols_q)}
+
+    if a.only == "gemm":
+        print(json.dumps({"only": "gemm", "roofline": gemm_leg(max(3, a.steps))}), flush=True)
+        return
+    if a.only == "quantizer":
+        print(json.dumps({"only": "quantizer", "quantizer": quantizer_leg()}), flush=True)
+        return
+
     def step():
         fs4.quantize(Rw, out_row=R_row, out_col=R_col)
         f = fs4.linear_fwd(X, R_row, U, V)
@@ -131,7 +231,6 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
@@ -152,57 +251,8 @@ def main():
            "step_frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)}
 
     if not a.no_extra:
-        # ---- dominant kernel: block-scaled GEMM at the three step shapes ----
-        X_row, X_col = fs4.quantize(X)
-        dY_row, dY_col = fs4.quantize(dY)
-        shapes = [(X_row, R_row), (dY_row, R_col), (dY_col, X_col)]
-        Cs = [torch.empty((A.rows, B.rows), dtype=torch.float32, device=dev) for A, B in shapes]
-        for (A, B), C in zip(shapes, Cs):
-            fs4.gemm_nt(A, B, out=C)
-        torch.cuda.synchronize()
-        reps = max(3, a.steps)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * 3)]
-        i = 0
-        for _ in range(reps):
-            for (A, B), C in zip(shapes, Cs):
-                ev[i][0].record(stream)
-                fs4.gemm_nt(A, B, out=C)
-                ev[i][1].record(stream)
-                i += 1
-        torch.cuda.synchronize()
-        durs = [s.elapsed_time(e) for s, e in ev]
-        gemm_ms = float(np.mean(durs))
-        gemm_flop = 2.0 * M * N * K
-        ach = gemm_flop / (gemm_ms * 1e-3) / 1e12
-        out["roofline"] = {"bound": "mfma", "kernel": "gemm_nt_kernel (block-scaled NVFP4 NT GEMM)",
-                           "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                           "per_launch": "8192x8192x3072 = %.1f GFLOP" % (gemm_flop / 1e9),
-                           "avg_launch_ms": round(gemm_ms, 4)}
-
-        # ---- quantizer on the 4096 x 4096 workload ---------------------------
-        qb = synth.quantizer_input()
-        copies = [to_bf16(qb) for _ in range(12)]
-        rows_q, cols_q = qb.shape
-        qrow = fs4.NVFP4.empty(rows_q, cols_q, dev)
-        qcol = fs4.NVFP4.empty(cols_q, rows_q, dev, qrow.tscale)
-        for c in copies[:3]:
-            fs4.quantize(c, out_row=qrow, out_col=qcol)
-        torch.cuda.synchronize()
-        qreps = 48
-        qe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(qreps)]
-        for j in range(qreps):
-            qe[j][0].record(stream)
-            fs4.quantize(copies[j % len(copies)], out_row=qrow, out_col=qcol)
-            qe[j][1].record(stream)
-        torch.cuda.synchronize()
-        q_ms = float(np.mean([s.elapsed_time(e) for s, e in qe]))
-        q_gbs = quantizer_bytes(rows_q, cols_q) / (q_ms * 1e-3) / 1e9
-        out["quantizer"] = {"workload": "4096x4096 bf16 ~N(0,1), 0.1% x50; row+col layouts",
-                            "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(q_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(q_ms * 1e3, 2),
-                            "bytes_per_call": quantizer_bytes(rows_q, cols_q)}
-        del copies
+        out["roofline"] = gemm_leg(max(3, a.steps))
+        out["quantizer"] = quantizer_leg()
 
         # ---- NVFP4 Newton-Schulz, 3072 x 8192, 5 steps ------------------------
         G = to_bf16(synth.ns_input())
