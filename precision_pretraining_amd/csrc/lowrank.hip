@@ -584,20 +584,35 @@ namespace {
 
 constexpr int kNormParts = 1024;
 
+// Eight consecutive elements (one 16-byte word of bf16, two of fp32) as double.
 template <bool BF16>
-__device__ inline double load_elem(const void *x, int64_t i) {
-  if constexpr (BF16) return (double)bf16_bits_to_float(((const uint16_t *)x)[i]);
-  else return (double)((const float *)x)[i];
+__device__ inline void load8d(const void *x, int64_t v, double *o) {
+  if constexpr (BF16) {
+    const uint4 w = ((const uint4 *)x)[v];
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = (double)bf16_bits_to_float(u[q] & 0xFFFFu);
+      o[2 * q + 1] = (double)bf16_bits_to_float(u[q] >> 16);
+    }
+  } else {
+    const float4 a = ((const float4 *)x)[2 * v], b = ((const float4 *)x)[2 * v + 1];
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
 }
 
+// Partial sums of squares in fp64 over 8-element words (n % 8 == 0).
 template <bool BF16>
-__global__ __launch_bounds__(256) void sumsq_kernel(const void *__restrict__ x, int64_t n,
+__global__ __launch_bounds__(256) void sumsq_kernel(const void *__restrict__ x, int64_t nv,
                                                     double *__restrict__ parts) {
   __shared__ double red[256];
   double s = 0.0;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const double v = load_elem<BF16>(x, i);
-    s += v * v;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += (int64_t)gridDim.x * 256) {
+    double o[8];
+    load8d<BF16>(x, v, o);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += o[q] * o[q];
   }
   red[threadIdx.x] = s;
   __syncthreads();
@@ -608,8 +623,10 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const void *__restrict__ x, 
   if (threadIdx.x == 0) parts[blockIdx.x] = red[0];
 }
 
+// out = x / (||x||_F + eps) as fp32: the fp64 reciprocal of the fp64 norm
+// times each element in fp64, rounded once to fp32.
 template <bool BF16>
-__global__ __launch_bounds__(256) void scale_kernel(const void *__restrict__ x, int64_t n,
+__global__ __launch_bounds__(256) void scale_kernel(const void *__restrict__ x, int64_t nv,
                                                     const double *__restrict__ parts, int nparts,
                                                     double eps, float *__restrict__ out) {
   __shared__ double inv_s;
@@ -620,15 +637,25 @@ __global__ __launch_bounds__(256) void scale_kernel(const void *__restrict__ x, 
   }
   __syncthreads();
   const double inv = inv_s;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    out[i] = (float)(load_elem<BF16>(x, i) * inv);
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += (int64_t)gridDim.x * 256) {
+    double o[8];
+    load8d<BF16>(x, v, o);
+    float4 *d = (float4 *)out + 2 * v;
+    d[0] = make_float4((float)(o[0] * inv), (float)(o[1] * inv), (float)(o[2] * inv), (float)(o[3] * inv));
+    d[1] = make_float4((float)(o[4] * inv), (float)(o[5] * inv), (float)(o[6] * inv), (float)(o[7] * inv));
+  }
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void copy_kernel(const void *__restrict__ x, int64_t n,
+__global__ __launch_bounds__(256) void copy_kernel(const void *__restrict__ x, int64_t nv,
                                                    float *__restrict__ out) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    out[i] = (float)load_elem<BF16>(x, i);
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += (int64_t)gridDim.x * 256) {
+    double o[8];
+    load8d<BF16>(x, v, o);
+    float4 *d = (float4 *)out + 2 * v;
+    d[0] = make_float4((float)o[0], (float)o[1], (float)o[2], (float)o[3]);
+    d[1] = make_float4((float)o[4], (float)o[5], (float)o[6], (float)o[7]);
+  }
 }
 
 }  // namespace
@@ -637,25 +664,28 @@ size_t normalize_ws_bytes() { return kNormParts * sizeof(double); }
 
 fs4_status launch_normalize(const void *G, fs4_dtype dt, int64_t n, float eps, float *X, void *ws,
                             hipStream_t s) {
+  // n is a multiple of 16 (both dimensions are); 8-element words
   double *parts = (double *)ws;
-  int64_t g = (n + 256 * 16 - 1) / (256 * 16);
+  const int64_t nv = n / 8;
+  int64_t g = (nv + 256 * 4 - 1) / (256 * 4);
   const int np = (int)(g < 1 ? 1 : (g > kNormParts ? kNormParts : g));
-  const unsigned gs = (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+  const unsigned gs = (unsigned)((nv + 255) / 256 < 4096 ? (nv + 255) / 256 : 4096);
   if (dt == FS4_BF16) {
-    sumsq_kernel<true><<<np, 256, 0, s>>>(G, n, parts);
-    scale_kernel<true><<<gs, 256, 0, s>>>(G, n, parts, np, (double)eps, X);
+    sumsq_kernel<true><<<np, 256, 0, s>>>(G, nv, parts);
+    scale_kernel<true><<<gs, 256, 0, s>>>(G, nv, parts, np, (double)eps, X);
   } else {
-    sumsq_kernel<false><<<np, 256, 0, s>>>(G, n, parts);
-    scale_kernel<false><<<gs, 256, 0, s>>>(G, n, parts, np, (double)eps, X);
+    sumsq_kernel<false><<<np, 256, 0, s>>>(G, nv, parts);
+    scale_kernel<false><<<gs, 256, 0, s>>>(G, nv, parts, np, (double)eps, X);
   }
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 
 fs4_status launch_copy_f32(const void *src, fs4_dtype dt, int64_t n, float *dst, hipStream_t s) {
-  const unsigned gs = (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+  const int64_t nv = n / 8;
+  const unsigned gs = (unsigned)((nv + 255) / 256 < 4096 ? (nv + 255) / 256 : 4096);
   if (n == 0) return FS4_OK;
-  if (dt == FS4_BF16) copy_kernel<true><<<gs, 256, 0, s>>>(src, n, dst);
-  else copy_kernel<false><<<gs, 256, 0, s>>>(src, n, dst);
+  if (dt == FS4_BF16) copy_kernel<true><<<gs, 256, 0, s>>>(src, nv, dst);
+  else copy_kernel<false><<<gs, 256, 0, s>>>(src, nv, dst);
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 

@@ -38,7 +38,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
-constexpr int kEncodeGrid = 1024;     // persistent workgroups of the encode pass
+// persistent workgroups of the encode pass: as many as fit on the 256 CUs at
+// once (bf16 tiles: 6 per CU; fp32: 4 per CU by registers)
+constexpr int kEncodeGridBf16 = 1536, kEncodeGridF32 = 1024;
 constexpr int kAmaxUnroll = 4;
 
 __device__ inline uint32_t wave_max_u32(uint32_t v) {
@@ -109,15 +111,16 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint4 *__r
 }
 
 // ---- lookup tables (per workgroup, from s_t) ---------------------------------
-// e4t[c], c = 0..125: amax_b >= e4t[c] exactly when the E4M3 scale code is at
-//   least c + 1.
-// rlo[c], rhi[c], c = 0..126: the bracket of 1/(e4m3(c) s_t); rlo < 0 marks a
-//   code whose blocks take the exact path; code 0 (step 0) has rlo = rhi = 0.
+// e4p[c] = (e4t[c-1], e4t[c]), c = 0..126, where amax_b >= e4t[c] exactly when
+//   the E4M3 scale code is at least c + 1 (e4t[-1] = -inf, e4t[126] = +inf):
+//   one 8-byte read checks an estimate against both of its boundaries.
+// rr[c] = (rlo, rhi), c = 0..126: the bracket of 1/(e4m3(c) s_t); rlo < 0 marks
+//   a code whose blocks take the exact path; code 0 (step 0) has rlo = rhi = 0.
 // eth[c][i], i = 0..6: |x| >= eth[c][i] exactly when the E2M1 index exceeds i
 //   for scale code c.
 struct Tables {
-  float e4t[128];
-  float rlo[128], rhi[128];
+  float2 e4p[128];
+  float2 rr[128];
   float eth[128][8];
 };
 
@@ -133,27 +136,22 @@ __device__ inline double e4m3_value(int c) { return (double)e4m3_to_float((uint3
 
 __device__ void build_tables(Tables &t, float s_t) {
   const double st = (double)s_t;
+  // threshold between codes c and c+1 (ties to the even code), c = -1..126
+  auto e4t = [&](int c) -> float {
+    if (c < 0) return -__builtin_huge_valf();
+    if (c >= 126 || !(st > 0.0)) return __builtin_huge_valf();
+    const double mid = 0.5 * (e4m3_value(c) + e4m3_value(c + 1));
+    return ge_threshold(mid * 6.0 * st, (c + 1) % 2 == 0);
+  };
   for (int c = threadIdx.x; c < 128; c += kThreads) {
-    if (c < 126) {
-      // boundary between codes c and c+1: ties go to the even code
-      const double mid = 0.5 * (e4m3_value(c) + e4m3_value(c + 1));
-      t.e4t[c] = st > 0.0 ? ge_threshold(mid * 6.0 * st, (c + 1) % 2 == 0) : __builtin_huge_valf();
-    } else {
-      t.e4t[c] = __builtin_huge_valf();
-    }
+    t.e4p[c] = make_float2(e4t(c - 1), e4t(c));
     const double step = c < 127 ? e4m3_value(c) * st : 0.0;
     if (step > 0.0) {
       const double r = 1.0 / step;
-      if (r < 0x1p120) {
-        t.rlo[c] = (float)(r * (1.0 - 0x1p-20));
-        t.rhi[c] = (float)(r * (1.0 + 0x1p-20));
-      } else {
-        t.rlo[c] = -1.0f;
-        t.rhi[c] = -1.0f;
-      }
+      if (r < 0x1p120) t.rr[c] = make_float2((float)(r * (1.0 - 0x1p-20)), (float)(r * (1.0 + 0x1p-20)));
+      else t.rr[c] = make_float2(-1.0f, -1.0f);
     } else {
-      t.rlo[c] = 0.0f;
-      t.rhi[c] = 0.0f;
+      t.rr[c] = make_float2(0.0f, 0.0f);
     }
     // E2M1 midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5; ties go to the even index,
     // i.e. up at 0.75, 1.75 and 3.5
@@ -167,52 +165,50 @@ __device__ void build_tables(Tables &t, float s_t) {
 }
 
 // E4M3 scale code of a block.  The estimate rounds q = amax_b / (6 s_t),
-// taken in fp32, to 3 mantissa bits (nearest, from the bit pattern; the
-// subnormal range on the 2^-9 grid); fp32 rounding of q moves it by at most one
-// code from the exact round-to-nearest-even code, which the two table compares
-// then give exactly.
-__device__ inline uint32_t scale_code(float amax, float inv6st, const Tables &t) {
+// taken in fp32 (two roundings), to 3 mantissa bits (nearest, from the bit
+// pattern; the subnormal range on the 2^-9 grid): it is within one code of the
+// exact round-to-nearest-even code, so one compare against each of its two
+// boundaries makes it exact.  When 1/(6 s_t) overflows fp32 (a subnormal s_t)
+// the estimate means nothing and a binary search over the boundaries decides.
+__device__ inline uint32_t scale_code(float amax, float inv6st, bool inv_finite, const Tables &t) {
   if (!(amax > 0.0f) || !(inv6st > 0.0f)) return 0u;
-  float q = amax * inv6st;
-  q = q < 448.0f ? q : 448.0f;
-  int c;
-  if (q >= 0.015625f) {
-    const uint32_t b = __builtin_bit_cast(uint32_t, q);
-    c = (int)((b + (1u << 19)) >> 20) - (120 << 3);   // biased exponent and 3 mantissa bits
-  } else {
-    c = (int)(q * 512.0f + 0.5f);
-  }
-  c = c > 126 ? 126 : (c < 0 ? 0 : c);
-  if (c < 126 && amax >= t.e4t[c]) ++c;
-  else if (c > 0 && amax < t.e4t[c - 1]) --c;
-  // exact code c satisfies e4t[c-1] <= amax < e4t[c]; an estimate that was
-  // off by more than one (e.g. 1/(6 s_t) overflowed for a subnormal s_t) is
-  // redone by binary search over the thresholds
-  const bool ok = (c == 0 || amax >= t.e4t[c - 1]) && (c == 126 || amax < t.e4t[c]);
-  if (!ok) {
-    int lo = 0, hi = 126;                 // number of thresholds <= amax lies in [lo, hi]
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (amax >= t.e4t[mid]) lo = mid + 1;
-      else hi = mid;
+  if (inv_finite) {
+    float q = amax * inv6st;
+    q = q < 448.0f ? q : 448.0f;
+    int c;
+    if (q >= 0.015625f) {
+      const uint32_t b = __builtin_bit_cast(uint32_t, q);
+      c = (int)((b + (1u << 19)) >> 20) - (120 << 3);   // biased exponent and 3 mantissa bits
+    } else {
+      c = (int)(q * 512.0f + 0.5f);
     }
-    c = lo;
+    c = c > 126 ? 126 : (c < 0 ? 0 : c);
+    const float2 th = t.e4p[c];
+    c += (amax >= th.y) ? 1 : (amax < th.x ? -1 : 0);
+    return (uint32_t)c;
   }
-  return (uint32_t)c;
+  int lo = 0, hi = 126;                 // number of boundaries <= amax lies in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (amax >= t.e4p[mid].y) lo = mid + 1;
+    else hi = mid;
+  }
+  return (uint32_t)lo;
 }
 
 // Encodes 16 values v[i] = src[i * estride] (LDS); returns the scale code and
 // packs the codes (element 2j in the low nibble of byte j).
-__device__ inline uint32_t encode16(const float *src, int estride, float inv6st, const Tables &t,
-                                    uint2 &packed) {
+__device__ inline uint32_t encode16(const float *src, int estride, float inv6st, bool inv_finite,
+                                    const Tables &t, uint2 &packed) {
   float v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = src[i * estride];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const uint32_t sb = scale_code(amax, inv6st, t);
-  const float rl = t.rlo[sb], rh = t.rhi[sb];
+  const uint32_t sb = scale_code(amax, inv6st, inv_finite, t);
+  const float2 rlh = t.rr[sb];
+  const float rl = rlh.x, rh = rlh.y;
   const float *th = t.eth[sb];
   uint32_t lo0 = 0, lo1 = 0;
   if (rl >= 0.0f) {
@@ -409,6 +405,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
   build_tables(tab, s_t);
   // 1/(6 s_t) only seeds the scale-code estimate; the tables make it exact
   const float inv6st = s_t > 0.0f ? (float)(1.0 / (6.0 * (double)s_t)) : 0.0f;   // may be inf
+  const bool inv_finite = inv6st < __builtin_huge_valf();
   tile_store<BF16>(g0, rows, cols, order.r0(sr), order.c0(sc), tile);
   __syncthreads();
 
@@ -428,8 +425,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
     // zero padding outside the tensor encodes harmlessly; only stores are masked
     uint2 pr = make_uint2(0, 0), pc = make_uint2(0, 0);
     uint32_t sbr = 0, sbc = 0;
-    if (ROW) sbr = encode16(&tile[line][blk * kBlock], 1, inv6st, tab, pr);
-    if (COL) sbc = encode16(&tile[blk * kBlock][line], kTile + 1, inv6st, tab, pc);
+    if (ROW) sbr = encode16(&tile[line][blk * kBlock], 1, inv6st, inv_finite, tab, pr);
+    if (COL) sbc = encode16(&tile[blk * kBlock][line], kTile + 1, inv6st, inv_finite, tab, pc);
     __syncthreads();
     tile_store<BF16>(nxt, rows, cols, order.r0(sr1), order.c0(sc1), tile);   // unread past the last tile
     if (ROW) {
@@ -473,10 +470,12 @@ fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int
   const fs4_nvfp4 rv = rowwise ? *rowwise : none;
   const fs4_nvfp4 cv = colwise ? *colwise : none;
   const bool bf16 = dt == FS4_BF16;
-  // one workgroup per tile slot (4 x 4 tiles per super-tile), at most kEncodeGrid
+  // one workgroup per tile slot (4 x 4 tiles per super-tile), at most the cap
   const int64_t slots = ((rows + 4 * kTile - 1) / (4 * kTile)) * ((cols + 4 * kTile - 1) / (4 * kTile)) * 16;
-  const unsigned grid = (unsigned)(slots < kEncodeGrid ? slots : kEncodeGrid);   // multiple of 16
-  static_assert(kEncodeGrid % 16 == 0, "the tile walk needs a grid that is a multiple of 16");
+  const int64_t cap = bf16 ? kEncodeGridBf16 : kEncodeGridF32;
+  const unsigned grid = (unsigned)(slots < cap ? slots : cap);   // multiple of 16
+  static_assert(kEncodeGridBf16 % 128 == 0 && kEncodeGridF32 % 128 == 0,
+                "the tile walk needs a multiple of 16, whole super-tiles per XCD a multiple of 128");
   const bool row = rv.codes != nullptr, col = cv.codes != nullptr;
 #define FS4_QK(B, R, C) quantize_kernel<B, R, C><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv)
   if (bf16) {
