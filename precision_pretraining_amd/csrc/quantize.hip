@@ -52,17 +52,19 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-__device__ inline uint32_t block_max_u32(uint32_t v, uint32_t *red) {
+template <int NT>
+__device__ inline uint32_t block_max_u32_n(uint32_t v, uint32_t *red) {
   v = wave_max_u32(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) red[wave] = v;
   __syncthreads();
   uint32_t r = red[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) r = r > red[i] ? r : red[i];
+  for (int i = 1; i < NT / 64; ++i) r = r > red[i] ? r : red[i];
   __syncthreads();
   return r;
 }
+__device__ inline uint32_t block_max_u32(uint32_t v, uint32_t *red) { return block_max_u32_n<kThreads>(v, red); }
 
 // largest magnitude bit pattern in a 16-byte word, as fp32 bits
 template <bool BF16>
@@ -134,7 +136,8 @@ __device__ inline float ge_threshold(double exact, bool tie_up) {
 
 __device__ inline double e4m3_value(int c) { return (double)e4m3_to_float((uint32_t)c); }
 
-__device__ void build_tables(Tables &t, float s_t) {
+template <int NT>
+__device__ void build_tables_n(Tables &t, float s_t) {
   const double st = (double)s_t;
   // threshold between codes c and c+1 (ties to the even code), c = -1..126
   auto e4t = [&](int c) -> float {
@@ -143,7 +146,7 @@ __device__ void build_tables(Tables &t, float s_t) {
     const double mid = 0.5 * (e4m3_value(c) + e4m3_value(c + 1));
     return ge_threshold(mid * 6.0 * st, (c + 1) % 2 == 0);
   };
-  for (int c = threadIdx.x; c < 128; c += kThreads) {
+  for (int c = threadIdx.x; c < 128; c += NT) {
     t.e4p[c] = make_float2(e4t(c - 1), e4t(c));
     const double step = c < 127 ? e4m3_value(c) * st : 0.0;
     if (step > 0.0) {
@@ -196,13 +199,15 @@ __device__ inline uint32_t scale_code(float amax, float inv6st, bool inv_finite,
   return (uint32_t)lo;
 }
 
-// Encodes 16 values v[i] = src[i * estride] (LDS); returns the scale code and
-// packs the codes (element 2j in the low nibble of byte j).
-__device__ inline uint32_t encode16(const float *src, int estride, float inv6st, bool inv_finite,
-                                    const Tables &t, uint2 &packed) {
+// Encodes the 16 values rd(0..15) (rd reads LDS, and is called again for the
+// rare element that needs an exact decision); returns the scale code and packs
+// the codes (element 2j in the low nibble of byte j).
+template <typename Reader>
+__device__ inline uint32_t encode16(const Reader &rd, float inv6st, bool inv_finite, const Tables &t,
+                                    uint2 &packed) {
   float v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = src[i * estride];
+  for (int i = 0; i < 16; ++i) v[i] = rd(i);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -235,7 +240,7 @@ __device__ inline uint32_t encode16(const float *src, int estride, float inv6st,
       const uint32_t sh = (uint32_t)__builtin_ctz(d) & ~3u;
       const uint32_t lo = w1 ? lo1 : lo0, hi = w1 ? hi1 : hi0;
       const int e = (int)(sh >> 2) + (w1 ? 8 : 0);
-      const float a = fabsf(src[e * estride]);
+      const float a = fabsf(rd(e));
       const uint32_t c = a >= th[(lo >> sh) & 7u] ? (hi >> sh) & 15u : (lo >> sh) & 15u;
       const uint32_t nl = (lo & ~(15u << sh)) | (c << sh);
       if (w1) {
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
   TileRegs<BF16> g0, g1;
   tile_gload<BF16>(x, rows, cols, order.r0(sr), order.c0(sc), have != 0, g0);
   tile_gload<BF16>(x, rows, cols, order.r0(sr1), order.c0(sc1), have1 != 0, g1);
-  build_tables(tab, s_t);
+  build_tables_n<kThreads>(tab, s_t);
   // 1/(6 s_t) only seeds the scale-code estimate; the tables make it exact
   const float inv6st = s_t > 0.0f ? (float)(1.0 / (6.0 * (double)s_t)) : 0.0f;   // may be inf
   const bool inv_finite = inv6st < __builtin_huge_valf();
@@ -425,8 +430,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
     // zero padding outside the tensor encodes harmlessly; only stores are masked
     uint2 pr = make_uint2(0, 0), pc = make_uint2(0, 0);
     uint32_t sbr = 0, sbc = 0;
-    if (ROW) sbr = encode16(&tile[line][blk * kBlock], 1, inv6st, inv_finite, tab, pr);
-    if (COL) sbc = encode16(&tile[blk * kBlock][line], kTile + 1, inv6st, inv_finite, tab, pc);
+    if (ROW) {
+      const float *src = &tile[line][blk * kBlock];
+      sbr = encode16([&](int i) { return src[i]; }, inv6st, inv_finite, tab, pr);
+    }
+    if (COL) {
+      const float *src = &tile[blk * kBlock][line];
+      sbc = encode16([&](int i) { return src[i * (kTile + 1)]; }, inv6st, inv_finite, tab, pc);
+    }
     __syncthreads();
     tile_store<BF16>(nxt, rows, cols, order.r0(sr1), order.c0(sc1), tile);   // unread past the last tile
     if (ROW) {
