@@ -135,6 +135,40 @@ __device__ inline void tile_coords(int64_t bid, int64_t tiles_m, int64_t tiles_n
   *tn = in_group / gsz;
 }
 
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 (a loop whose index
+// is a constant expression in the body).
+template <int B, int E, class F>
+__device__ inline void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Direct global->LDS loads (gfx950 global_load_lds): lane l's 16 (or 4)
+// bytes from `src` land at LDS byte address `lds_dst + 16 l` (or + 4 l);
+// lds_dst must be wave-uniform.  Issued as inline assembly so the compiler
+// does not guard every later LDS read with a wait for them; the kernel waits
+// explicitly (wait_vmcnt) before a barrier publishes a stage.
+// M0 (the LDS destination register) is set inside each statement and listed
+// as clobbered; the compiler warns that it is a reserved register, and nothing
+// else in these kernels uses it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void lds_dma16(uint32_t lds_dst, const void *src) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_dst), "v"(src)
+               : "memory", "m0");
+}
+__device__ inline void lds_dma4(uint32_t lds_dst, const void *src) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dword %1, off" ::"s"(lds_dst), "v"(src)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // KFAST: K % 128 == 0 (16-byte code chunks, 8-byte scale chunks, no k tail);
 // otherwise K % 16 == 0 with 8-byte code chunks and byte-wise scales.
 template <int WM, int WN, int TM, int TN, bool KFAST>
@@ -143,8 +177,13 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int A_BYTES = BM * kLdsStride, B_BYTES = BN * kLdsStride;
   constexpr int STAGE = A_BYTES + B_BYTES + BM * 8 + BN * 8;
+  // KFAST stages are filled by direct global->LDS loads: unpadded 64-byte code
+  // rows (16-byte slots XOR-swizzled by row), then 8 scale bytes per row; three
+  // stages, plus 1 KB that idle load instructions write to
+  constexpr int STAGE_D = (BM + BN) * (kRowBytes + 8);
+  constexpr int MAIN_BYTES = KFAST ? 3 * STAGE_D + 1024 : 2 * STAGE;
   constexpr int LR_BYTES = (2 * BM + BN) * kLrStrideMax * 2;   // rank-r staging in the epilogue
-  constexpr int LDS_BYTES = 2 * STAGE > LR_BYTES ? 2 * STAGE : LR_BYTES;
+  constexpr int LDS_BYTES = MAIN_BYTES > LR_BYTES ? MAIN_BYTES : LR_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ uint2 scale_lut[256];
 
@@ -240,17 +279,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   fill_scale_lut(scale_lut);
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
+  const int sw = ((l32 >> 1) ^ (l32 >> 3)) & 3;    // slot swizzle of this lane's rows (KFAST stages)
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_global(kt + 1);
-    const uint8_t *la = lds + cur * STAGE, *lb = la + A_BYTES, *lsa = lb + B_BYTES, *lsb = lsa + BM * 8;
-    // this lane's rows in the stage: codes at row*80 + h*32, scale bytes at row*8 + h*4
-    const uint8_t *pa = la + (wm * TM * 32 + l32) * kLdsStride + h * 32;
-    const uint8_t *pb = lb + (wn * TN * 32 + l32) * kLdsStride + h * 32;
+  // One k-tile from an LDS stage: 8 k-steps of TM x TN MFMAs.  Block b's codes
+  // and scale pairs are read one block ahead, and step s+1's operands are
+  // expanded while step s's MFMAs run.
+  auto compute_tile = [&](const uint8_t *la, const uint8_t *lb, const uint8_t *lsa, const uint8_t *lsb) {
     uint32_t sa4[TM], sb4[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -258,47 +292,48 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       sb4[j] = *(const uint32_t *)(lsb + (wn * TN * 32 + j * 32 + l32) * 8 + h * 4);
-
-    // Software pipeline over the 8 k-steps of the tile: block b's codes and
-    // scale pairs are read one block ahead, and step s+1's operands are
-    // expanded while step s's MFMAs run.
-    uint2 ca[TM], cb[TN];
-    ScalePair sa[TM], sb[TN];
-    auto read_block = [&](int blk) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        ca[i] = *(const uint2 *)(pa + i * 32 * kLdsStride + blk * 8);
-        sa[i] = lut_scale(scale_lut, (sa4[i] >> (8 * blk)) & 0xFFu);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        cb[j] = *(const uint2 *)(pb + j * 32 * kLdsStride + blk * 8);
-        sb[j] = lut_scale(scale_lut, (sb4[j] >> (8 * blk)) & 0xFFu);
-      }
+    // codes of blocks 2p and 2p+1 (16 bytes) of row r for this lane half
+    auto codes_at = [&](const uint8_t *base, int r, int p) -> uint4 {
+      if constexpr (KFAST) return *(const uint4 *)(base + r * kRowBytes + (((2 * h + p) ^ sw) << 4));
+      else return *(const uint4 *)(base + r * kLdsStride + h * 32 + p * 16);
     };
-    read_block(0);
+    uint4 ca[TM], cb[TN];
+    ScalePair sa[TM], sb[TN];
+    auto read_pair = [&](int p) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ca[i] = codes_at(la, wm * TM * 32 + i * 32 + l32, p);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) cb[j] = codes_at(lb, wn * TN * 32 + j * 32 + l32, p);
+    };
+    auto read_scales = [&](int blk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa[i] = lut_scale(scale_lut, (sa4[i] >> (8 * blk)) & 0xFFu);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb[j] = lut_scale(scale_lut, (sb4[j] >> (8 * blk)) & 0xFFu);
+    };
+    // the 32-bit code word of step s: block s/2, half s%2
+    auto word = [](const uint4 &c, int s) -> uint32_t {
+      const int q = s & 3;
+      return q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
+    };
+    read_pair(0);
+    read_scales(0);
     f16x8_t av[TM], bv[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) av[i] = expand8(ca[i].x, sa[i]);
 #pragma unroll
     for (int j = 0; j < TN; ++j) bv[j] = expand8(cb[j].x, sb[j]);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      // next step's operands: the other half of this block, or the next block
+    static_for<0, 8>([&](auto step) {
+      constexpr int s = decltype(step)::value;
       f16x8_t an[TM], bn[TN];
       if (s + 1 < 8) {
-        if ((s & 1) == 0) {
+        const int t = s + 1;          // next step: block t/2, half t%2
+        if (t == 4) read_pair(1);
+        if ((t & 1) == 0) read_scales(t >> 1);
 #pragma unroll
-          for (int i = 0; i < TM; ++i) an[i] = expand8(ca[i].y, sa[i]);
+        for (int i = 0; i < TM; ++i) an[i] = expand8(word(ca[i], t), sa[i]);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) bn[j] = expand8(cb[j].y, sb[j]);
-        } else {
-          read_block((s + 1) >> 1);
-#pragma unroll
-          for (int i = 0; i < TM; ++i) an[i] = expand8(ca[i].x, sa[i]);
-#pragma unroll
-          for (int j = 0; j < TN; ++j) bn[j] = expand8(cb[j].x, sb[j]);
-        }
+        for (int j = 0; j < TN; ++j) bn[j] = expand8(word(cb[j], t), sb[j]);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -306,14 +341,109 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
       if (s + 1 < 8) {
+        // Interleave: each MFMA (32 cycles in the matrix pipe) is followed by
+        // an even share of the next step's expansion, which the SIMD issues
+        // while the MFMA runs.  Left to itself the scheduler clusters the
+        // conversions into long VALU runs that stall the matrix pipe.
+        constexpr int VPM = (8 * (TM + TN) + TM * TN - 1) / (TM * TN);
+#pragma unroll
+        for (int i = 0; i < TM * TN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0); // VPM VALU
+        }
+      }
+      if (s + 1 < 8) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) av[i] = an[i];
 #pragma unroll
         for (int j = 0; j < TN; ++j) bv[j] = bn[j];
       }
+      __builtin_amdgcn_sched_barrier(0);   // one scheduling region per k-step
+    });
+  };
+
+  if constexpr (KFAST) {
+    // Three-stage pipeline of direct global->LDS loads (no staging registers):
+    // tile kt+2's loads are issued before tile kt is multiplied, into the
+    // stage tile kt-1 used (free since the barrier that ended tile kt-1).
+    // Every wave issues the same number of 64-lane load instructions per tile
+    // (idle ones write the spare 1 KB), so "tile kt+1 has landed" is exactly
+    // "at most DMA_PER_TILE loads outstanding".  Rows past M or N load a
+    // clamped row: they only feed outputs that are never stored.
+    constexpr int NW = NT / 64;
+    constexpr int CODE_Q = (BM + BN) * 4, SC_U = (BM + BN) * 2;
+    static_assert(CODE_Q % 64 == 0 && SC_U % 64 == 0, "load instructions must be all-real or all-idle");
+    constexpr int CODE_I = (CODE_Q + 64 * NW - 1) / (64 * NW), SC_I = (SC_U + 64 * NW - 1) / (64 * NW);
+    constexpr int DMA_PER_TILE = CODE_I + SC_I;
+    static_assert(DMA_PER_TILE < 64, "vmcnt range");
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;     // LDS byte address of the stages
+    auto issue_tile = [&](int kt, int st) {
+      const uint32_t sbase = lds0 + (uint32_t)(st * STAGE_D), spare = lds0 + 3u * STAGE_D;
+      const int64_t kbyte0 = (int64_t)kt * kRowBytes, ksc0 = (int64_t)kt * 8;
+#pragma unroll
+      for (int j = 0; j < CODE_I; ++j) {
+        const int q0 = (j * NW + wave) * 64, q = q0 + lane;
+        const uint8_t *src = g.a_codes;
+        uint32_t dst = spare;
+        if (q0 < CODE_Q) {
+          const bool isa = q < BM * 4;
+          const int qq = isa ? q : q - BM * 4, row = qq >> 2;
+          const int logical = (qq & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+          const int64_t lim = isa ? g.M : g.N;
+          int64_t gr = (isa ? m0 : n0) + row;
+          gr = gr < lim ? gr : lim - 1;
+          src = (isa ? g.a_codes : g.b_codes) + gr * kb + kbyte0 + logical * 16;
+          dst = sbase + (uint32_t)(q0 * 16);
+        }
+        lds_dma16(__builtin_amdgcn_readfirstlane(dst), src);
+      }
+#pragma unroll
+      for (int j = 0; j < SC_I; ++j) {
+        const int u0 = (j * NW + wave) * 64, u = u0 + lane;
+        const uint8_t *src = g.a_scales;
+        uint32_t dst = spare;
+        if (u0 < SC_U) {
+          const bool isa = u < BM * 2;
+          const int uu = isa ? u : u - BM * 2, row = uu >> 1;
+          const int64_t lim = isa ? g.M : g.N;
+          int64_t gr = (isa ? m0 : n0) + row;
+          gr = gr < lim ? gr : lim - 1;
+          src = (isa ? g.a_scales : g.b_scales) + gr * ks + ksc0 + (uu & 1) * 4;
+          dst = sbase + (uint32_t)((BM + BN) * kRowBytes + u0 * 4);
+        }
+        lds_dma4(__builtin_amdgcn_readfirstlane(dst), src);
+      }
+    };
+    issue_tile(0, 0);
+    if (nk > 1) {
+      issue_tile(1, 1);
+      wait_vmcnt<DMA_PER_TILE>();
+    } else {
+      wait_vmcnt<0>();
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt % 3;
+      if (kt + 2 < nk) issue_tile(kt + 2, (kt + 2) % 3);
+      const uint8_t *la = lds + cur * STAGE_D, *lb = la + BM * kRowBytes;
+      const uint8_t *lsa = la + (BM + BN) * kRowBytes, *lsb = lsa + BM * 8;
+      compute_tile(la, lb, lsa, lsb);
+      if (kt + 2 < nk) wait_vmcnt<DMA_PER_TILE>();   // tile kt+1 has landed
+      else wait_vmcnt<0>();
+      __syncthreads();
+    }
+  } else {
+    load_global(0);
+    store_lds(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) load_global(kt + 1);
+      const uint8_t *la = lds + cur * STAGE, *lb = la + A_BYTES, *lsa = lb + B_BYTES, *lsb = lsa + BM * 8;
+      compute_tile(la, lb, lsa, lsb);
+      if (kt + 1 < nk) store_lds(cur ^ 1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -439,7 +569,7 @@ template <int WM, int WN, int TM, int TN>
 fs4_status launch_cfg(const GemmArgs &g, hipStream_t s) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  if (g.K % kBK == 0)
+  if (g.K > 0 && g.K % kBK == 0)
     gemm_nt_kernel<WM, WN, TM, TN, true><<<(unsigned)tiles, WM * WN * 64, 0, s>>>(g);
   else
     gemm_nt_kernel<WM, WN, TM, TN, false><<<(unsigned)tiles, WM * WN * 64, 0, s>>>(g);
