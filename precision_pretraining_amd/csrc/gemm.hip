@@ -281,66 +281,77 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   fill_scale_lut(scale_lut);
   const int sw = ((l32 >> 1) ^ (l32 >> 3)) & 3;    // slot swizzle of this lane's rows (KFAST stages)
 
-  // One k-tile from an LDS stage: 8 k-steps of TM x TN MFMAs.  Block b's codes
-  // and scale pairs are read one block ahead, and step s+1's operands are
-  // expanded while step s's MFMAs run.
-  auto compute_tile = [&](const uint8_t *la, const uint8_t *lb, const uint8_t *lsa, const uint8_t *lsb) {
-    uint32_t sa4[TM], sb4[TN];
+  // One k-tile from an LDS stage is 8 k-steps of TM x TN MFMAs.  Block b's
+  // codes and scale pairs are read one block ahead, and step s+1's operands
+  // are expanded while step s's MFMAs run.
+  struct Stage { const uint8_t *a, *b, *sa, *sb; };
+  uint32_t sa4[TM], sb4[TN];      // the four scale bytes of each row's blocks in this lane half
+  uint4 ca[TM], cb[TN];           // codes of two blocks
+  ScalePair sa[TM], sb[TN];
+  f16x8_t av[TM], bv[TN];         // operands of the current k-step
+  // codes of blocks 2p and 2p+1 (16 bytes) of row r for this lane half
+  auto codes_at = [&](const uint8_t *base, int r, int p) -> uint4 {
+    if constexpr (KFAST) return *(const uint4 *)(base + r * kRowBytes + (((2 * h + p) ^ sw) << 4));
+    else return *(const uint4 *)(base + r * kLdsStride + h * 32 + p * 16);
+  };
+  auto read_pair = [&](const Stage &t, int p) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ca[i] = codes_at(t.a, wm * TM * 32 + i * 32 + l32, p);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) cb[j] = codes_at(t.b, wn * TN * 32 + j * 32 + l32, p);
+  };
+  auto read_scales = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = lut_scale(scale_lut, (sa4[i] >> (8 * blk)) & 0xFFu);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] = lut_scale(scale_lut, (sb4[j] >> (8 * blk)) & 0xFFu);
+  };
+  // the 32-bit code word of step s: block s/2, half s%2
+  auto word = [](const uint4 &c, int s) -> uint32_t {
+    const int q = s & 3;
+    return q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
+  };
+  auto expand_step = [&](int s, f16x8_t *ao, f16x8_t *bo) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ao[i] = expand8(word(ca[i], s), sa[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bo[j] = expand8(word(cb[j], s), sb[j]);
+  };
+  // reads a stage's scale bytes and first code pair, expands its step 0
+  auto begin_tile = [&](const Stage &t, f16x8_t *ao, f16x8_t *bo) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      sa4[i] = *(const uint32_t *)(lsa + (wm * TM * 32 + i * 32 + l32) * 8 + h * 4);
+      sa4[i] = *(const uint32_t *)(t.sa + (wm * TM * 32 + i * 32 + l32) * 8 + h * 4);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      sb4[j] = *(const uint32_t *)(lsb + (wn * TN * 32 + j * 32 + l32) * 8 + h * 4);
-    // codes of blocks 2p and 2p+1 (16 bytes) of row r for this lane half
-    auto codes_at = [&](const uint8_t *base, int r, int p) -> uint4 {
-      if constexpr (KFAST) return *(const uint4 *)(base + r * kRowBytes + (((2 * h + p) ^ sw) << 4));
-      else return *(const uint4 *)(base + r * kLdsStride + h * 32 + p * 16);
-    };
-    uint4 ca[TM], cb[TN];
-    ScalePair sa[TM], sb[TN];
-    auto read_pair = [&](int p) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) ca[i] = codes_at(la, wm * TM * 32 + i * 32 + l32, p);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) cb[j] = codes_at(lb, wn * TN * 32 + j * 32 + l32, p);
-    };
-    auto read_scales = [&](int blk) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) sa[i] = lut_scale(scale_lut, (sa4[i] >> (8 * blk)) & 0xFFu);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sb[j] = lut_scale(scale_lut, (sb4[j] >> (8 * blk)) & 0xFFu);
-    };
-    // the 32-bit code word of step s: block s/2, half s%2
-    auto word = [](const uint4 &c, int s) -> uint32_t {
-      const int q = s & 3;
-      return q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
-    };
-    read_pair(0);
+      sb4[j] = *(const uint32_t *)(t.sb + (wn * TN * 32 + j * 32 + l32) * 8 + h * 4);
+    read_pair(t, 0);
     read_scales(0);
-    f16x8_t av[TM], bv[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) av[i] = expand8(ca[i].x, sa[i]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bv[j] = expand8(cb[j].x, sb[j]);
+    expand_step(0, ao, bo);
+  };
+  // The 8 k-steps of stage t (whose step 0 is already in av/bv).  With CROSS,
+  // the last step's MFMAs overlap the reads and step-0 expansion of stage nt;
+  // mid() runs after step 3, when this wave's last LDS read of t is issued.
+  auto run_tile = [&](const Stage &t, const Stage &nt, auto cross, auto mid) {
+    constexpr bool CROSS = decltype(cross)::value;
     static_for<0, 8>([&](auto step) {
       constexpr int s = decltype(step)::value;
+      constexpr bool EXPAND = s + 1 < 8 || CROSS;
       f16x8_t an[TM], bn[TN];
-      if (s + 1 < 8) {
-        const int t = s + 1;          // next step: block t/2, half t%2
-        if (t == 4) read_pair(1);
-        if ((t & 1) == 0) read_scales(t >> 1);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) an[i] = expand8(word(ca[i], t), sa[i]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bn[j] = expand8(word(cb[j], t), sb[j]);
+      if constexpr (s + 1 < 8) {
+        constexpr int u = s + 1;      // next step: block u/2, half u%2
+        if constexpr (u == 4) read_pair(t, 1);
+        if constexpr ((u & 1) == 0) read_scales(u >> 1);
+        expand_step(u, an, bn);
+      } else if constexpr (CROSS) {
+        begin_tile(nt, an, bn);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-      if (s + 1 < 8) {
+      if constexpr (EXPAND) {
         // Interleave: each MFMA (32 cycles in the matrix pipe) is followed by
         // an even share of the next step's expansion, which the SIMD issues
         // while the MFMA runs.  Left to itself the scheduler clusters the
@@ -351,21 +362,27 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0); // VPM VALU
         }
-      }
-      if (s + 1 < 8) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) av[i] = an[i];
 #pragma unroll
         for (int j = 0; j < TN; ++j) bv[j] = bn[j];
       }
       __builtin_amdgcn_sched_barrier(0);   // one scheduling region per k-step
+      if constexpr (s == 3) {
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     });
   };
 
   if constexpr (KFAST) {
-    // Three-stage pipeline of direct global->LDS loads (no staging registers):
-    // tile kt+2's loads are issued before tile kt is multiplied, into the
-    // stage tile kt-1 used (free since the barrier that ended tile kt-1).
+    // Three-stage pipeline of direct global->LDS loads (no staging registers).
+    // Tile kt+2's loads are issued as tile kt starts, into the stage of tile
+    // kt-1.  One barrier per tile, in its middle: before it each wave has
+    // issued its last read of tile kt and waited for its own loads of tile
+    // kt+1; after it tile kt+1 is visible to all and tile kt's stage may be
+    // refilled (at the start of tile kt+1).  So the last k-step of tile kt
+    // can already read and expand tile kt+1.
     // Every wave issues the same number of 64-lane load instructions per tile
     // (idle ones write the spare 1 KB), so "tile kt+1 has landed" is exactly
     // "at most DMA_PER_TILE loads outstanding".  Rows past M or N load a
@@ -414,6 +431,10 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
         lds_dma4(__builtin_amdgcn_readfirstlane(dst), src);
       }
     };
+    auto stage = [&](int st) -> Stage {
+      const uint8_t *base = lds + st * STAGE_D;
+      return Stage{base, base + BM * kRowBytes, base + (BM + BN) * kRowBytes, base + (BM + BN) * kRowBytes + BM * 8};
+    };
     issue_tile(0, 0);
     if (nk > 1) {
       issue_tile(1, 1);
@@ -422,16 +443,19 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
       wait_vmcnt<0>();
     }
     __syncthreads();
+    begin_tile(stage(0), av, bv);
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt % 3;
       if (kt + 2 < nk) issue_tile(kt + 2, (kt + 2) % 3);
-      const uint8_t *la = lds + cur * STAGE_D, *lb = la + BM * kRowBytes;
-      const uint8_t *lsa = la + (BM + BN) * kRowBytes, *lsb = lsa + BM * 8;
-      compute_tile(la, lb, lsa, lsb);
-      if (kt + 2 < nk) wait_vmcnt<DMA_PER_TILE>();   // tile kt+1 has landed
-      else wait_vmcnt<0>();
-      __syncthreads();
+      const bool more = kt + 2 < nk;
+      // after the last tile the "next" stage is the current one again (a
+      // harmless re-read; nothing refills it any more)
+      run_tile(stage(kt % 3), stage(kt + 1 < nk ? (kt + 1) % 3 : kt % 3), std::true_type{}, [&] {
+        if (more) wait_vmcnt<DMA_PER_TILE>();     // tile kt+1 has landed
+        else wait_vmcnt<0>();
+        __syncthreads();
+      });
     }
+    __syncthreads();           // the epilogue reuses the stages
   } else {
     load_global(0);
     store_lds(0);
@@ -439,8 +463,10 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
       if (kt + 1 < nk) load_global(kt + 1);
-      const uint8_t *la = lds + cur * STAGE, *lb = la + A_BYTES, *lsa = lb + B_BYTES, *lsb = lsa + BM * 8;
-      compute_tile(la, lb, lsa, lsb);
+      const uint8_t *la = lds + cur * STAGE;
+      const Stage t{la, la + A_BYTES, la + A_BYTES + B_BYTES, la + A_BYTES + B_BYTES + BM * 8};
+      begin_tile(t, av, bv);
+      run_tile(t, t, std::false_type{}, [] {});
       if (kt + 1 < nk) store_lds(cur ^ 1);
       __syncthreads();
     }
