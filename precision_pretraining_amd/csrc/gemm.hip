@@ -145,6 +145,9 @@ __device__ inline void static_for(F &&f) {
   }
 }
 
+// Word 3 of a raw buffer resource: 32-bit data format (untyped dword access).
+constexpr int kBufferWord3 = 0x00020000;
+
 // Direct global->LDS loads (gfx950 global_load_lds): lane l's 16 (or 4)
 // bytes from `src` land at LDS byte address `lds_dst + 16 l` (or + 4 l);
 // lds_dst must be wave-uniform.  Issued as inline assembly so the compiler
@@ -155,12 +158,14 @@ __device__ inline void static_for(F &&f) {
 // else in these kernels uses it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void lds_dma16(uint32_t lds_dst, const void *src) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_dst), "v"(src)
+// The source is a wave-uniform base (scalar registers) plus a 32-bit per-lane
+// byte offset.
+__device__ inline void lds_dma16(uint32_t lds_dst, const void *base, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(off), "s"(base)
                : "memory", "m0");
 }
-__device__ inline void lds_dma4(uint32_t lds_dst, const void *src) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dword %1, off" ::"s"(lds_dst), "v"(src)
+__device__ inline void lds_dma4(uint32_t lds_dst, const void *base, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_dst), "v"(off), "s"(base)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -193,6 +198,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the same value, known uniform
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t K = g.K, kb = K / 2, ks = K / kBlock;
   const int nk = (int)((K + kBK - 1) / kBK);
@@ -281,24 +287,28 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   fill_scale_lut(scale_lut);
   const int sw = ((l32 >> 1) ^ (l32 >> 3)) & 3;    // slot swizzle of this lane's rows (KFAST stages)
 
-  // One k-tile from an LDS stage is 8 k-steps of TM x TN MFMAs.  Block b's
-  // codes and scale pairs are read one block ahead, and step s+1's operands
-  // are expanded while step s's MFMAs run.
+  // One k-tile from an LDS stage is 8 k-steps of TM x TN MFMAs.  Step s uses
+  // the 32-bit code word s%4 of code pair s/4 (a pair is two blocks, 16
+  // bytes of a row for this lane half) and the scales of block s/2.  Step
+  // s+1's operands are expanded while step s's MFMAs run.  Codes are read
+  // in 8-byte halves two steps ahead of their use, into the registers of the
+  // half they replace: lo = words 0-1, hi = words 2-3.
   struct Stage { const uint8_t *a, *b, *sa, *sb; };
   uint32_t sa4[TM], sb4[TN];      // the four scale bytes of each row's blocks in this lane half
-  uint4 ca[TM], cb[TN];           // codes of two blocks
+  uint2 clo_a[TM], clo_b[TN], chi_a[TM], chi_b[TN];
   ScalePair sa[TM], sb[TN];
   f16x8_t av[TM], bv[TN];         // operands of the current k-step
-  // codes of blocks 2p and 2p+1 (16 bytes) of row r for this lane half
-  auto codes_at = [&](const uint8_t *base, int r, int p) -> uint4 {
-    if constexpr (KFAST) return *(const uint4 *)(base + r * kRowBytes + (((2 * h + p) ^ sw) << 4));
-    else return *(const uint4 *)(base + r * kLdsStride + h * 32 + p * 16);
+  // half q (0: words 0-1, 1: words 2-3) of code pair p of row r
+  auto codes_at = [&](const uint8_t *base, int r, int p, int q) -> uint2 {
+    if constexpr (KFAST) return *(const uint2 *)(base + r * kRowBytes + (((2 * h + p) ^ sw) << 4) + q * 8);
+    else return *(const uint2 *)(base + r * kLdsStride + h * 32 + p * 16 + q * 8);
   };
-  auto read_pair = [&](const Stage &t, int p) {
+  auto read_codes = [&](const Stage &t, int p, int q) {
+    uint2 *da = q ? chi_a : clo_a, *db = q ? chi_b : clo_b;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ca[i] = codes_at(t.a, wm * TM * 32 + i * 32 + l32, p);
+    for (int i = 0; i < TM; ++i) da[i] = codes_at(t.a, wm * TM * 32 + i * 32 + l32, p, q);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) cb[j] = codes_at(t.b, wn * TN * 32 + j * 32 + l32, p);
+    for (int j = 0; j < TN; ++j) db[j] = codes_at(t.b, wn * TN * 32 + j * 32 + l32, p, q);
   };
   auto read_scales = [&](int blk) {
 #pragma unroll
@@ -306,45 +316,55 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) sb[j] = lut_scale(scale_lut, (sb4[j] >> (8 * blk)) & 0xFFu);
   };
-  // the 32-bit code word of step s: block s/2, half s%2
-  auto word = [](const uint4 &c, int s) -> uint32_t {
-    const int q = s & 3;
-    return q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
-  };
   auto expand_step = [&](int s, f16x8_t *ao, f16x8_t *bo) {
+    const int w = s & 3;
+    const uint2 *wa = w < 2 ? clo_a : chi_a, *wb = w < 2 ? clo_b : chi_b;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ao[i] = expand8(word(ca[i], s), sa[i]);
+    for (int i = 0; i < TM; ++i) ao[i] = expand8((w & 1) ? wa[i].y : wa[i].x, sa[i]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bo[j] = expand8(word(cb[j], s), sb[j]);
+    for (int j = 0; j < TN; ++j) bo[j] = expand8((w & 1) ? wb[j].y : wb[j].x, sb[j]);
   };
-  // reads a stage's scale bytes and first code pair, expands its step 0
-  auto begin_tile = [&](const Stage &t, f16x8_t *ao, f16x8_t *bo) {
+  auto read_scale_bytes = [&](const Stage &t) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       sa4[i] = *(const uint32_t *)(t.sa + (wm * TM * 32 + i * 32 + l32) * 8 + h * 4);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       sb4[j] = *(const uint32_t *)(t.sb + (wn * TN * 32 + j * 32 + l32) * 8 + h * 4);
-    read_pair(t, 0);
-    read_scales(0);
-    expand_step(0, ao, bo);
   };
-  // The 8 k-steps of stage t (whose step 0 is already in av/bv).  With CROSS,
-  // the last step's MFMAs overlap the reads and step-0 expansion of stage nt;
-  // mid() runs after step 3, when this wave's last LDS read of t is issued.
+  // a stage's scale bytes and first code pair, then its step 0
+  auto begin_tile = [&](const Stage &t) {
+    read_scale_bytes(t);
+    read_codes(t, 0, 0);
+    read_codes(t, 0, 1);
+    read_scales(0);
+    expand_step(0, av, bv);
+  };
+  // The 8 k-steps of stage t (whose step 0 is already in av/bv and whose
+  // pair-0 codes are in clo/chi).  Reads: pair 1 lo in step 1, pair 1 hi in
+  // step 3.  With CROSS, stage nt's scale bytes (step 6) and pair 0 (lo in
+  // step 5, hi in step 7) are read too, and the last step expands nt's
+  // step 0, so no k-step runs without expansion work beside its MFMAs.
+  // mid() runs after step 3, once this wave has issued its last read of t;
+  // the reads of nt come after it.
   auto run_tile = [&](const Stage &t, const Stage &nt, auto cross, auto mid) {
     constexpr bool CROSS = decltype(cross)::value;
     static_for<0, 8>([&](auto step) {
       constexpr int s = decltype(step)::value;
       constexpr bool EXPAND = s + 1 < 8 || CROSS;
       f16x8_t an[TM], bn[TN];
+      if constexpr (s == 1) read_codes(t, 1, 0);
+      if constexpr (s == 3) read_codes(t, 1, 1);
+      if constexpr (CROSS && s == 5) read_codes(nt, 0, 0);
+      if constexpr (CROSS && s == 6) read_scale_bytes(nt);   // this stage's were last decoded in step 5
+      if constexpr (CROSS && s == 7) read_codes(nt, 0, 1);
       if constexpr (s + 1 < 8) {
-        constexpr int u = s + 1;      // next step: block u/2, half u%2
-        if constexpr (u == 4) read_pair(t, 1);
+        constexpr int u = s + 1;
         if constexpr ((u & 1) == 0) read_scales(u >> 1);
         expand_step(u, an, bn);
       } else if constexpr (CROSS) {
-        begin_tile(nt, an, bn);
+        read_scales(0);
+        expand_step(0, an, bn);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -394,41 +414,54 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
     constexpr int DMA_PER_TILE = CODE_I + SC_I;
     static_assert(DMA_PER_TILE < 64, "vmcnt range");
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;     // LDS byte address of the stages
+    // Per load instruction: whether it fills A or B (uniform: the A part is a
+    // whole number of instructions) and this lane's byte offset from the
+    // start of the A or B codes (scales) at k = 0; 32 bits suffice (the
+    // launcher checks).  Idle instructions read offset 0.
+    uint32_t coff[CODE_I], soff[SC_I];
+#pragma unroll
+    for (int j = 0; j < CODE_I; ++j) {
+      const int q0 = (j * NW + wave_u) * 64, q = q0 + lane;
+      coff[j] = 0;
+      if (q0 < CODE_Q) {
+        const bool isa = q0 < BM * 4;
+        const int qq = isa ? q : q - BM * 4, row = qq >> 2;
+        const int logical = (qq & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+        const int64_t lim = isa ? g.M : g.N;
+        int64_t gr = (isa ? m0 : n0) + row;
+        gr = gr < lim ? gr : lim - 1;
+        coff[j] = (uint32_t)(gr * kb + logical * 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SC_I; ++j) {
+      const int u0 = (j * NW + wave_u) * 64, u = u0 + lane;
+      soff[j] = 0;
+      if (u0 < SC_U) {
+        const bool isa = u0 < BM * 2;
+        const int uu = isa ? u : u - BM * 2, row = uu >> 1;
+        const int64_t lim = isa ? g.M : g.N;
+        int64_t gr = (isa ? m0 : n0) + row;
+        gr = gr < lim ? gr : lim - 1;
+        soff[j] = (uint32_t)(gr * ks + (uu & 1) * 4);
+      }
+    }
     auto issue_tile = [&](int kt, int st) {
       const uint32_t sbase = lds0 + (uint32_t)(st * STAGE_D), spare = lds0 + 3u * STAGE_D;
       const int64_t kbyte0 = (int64_t)kt * kRowBytes, ksc0 = (int64_t)kt * 8;
 #pragma unroll
       for (int j = 0; j < CODE_I; ++j) {
-        const int q0 = (j * NW + wave) * 64, q = q0 + lane;
-        const uint8_t *src = g.a_codes;
-        uint32_t dst = spare;
-        if (q0 < CODE_Q) {
-          const bool isa = q < BM * 4;
-          const int qq = isa ? q : q - BM * 4, row = qq >> 2;
-          const int logical = (qq & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
-          const int64_t lim = isa ? g.M : g.N;
-          int64_t gr = (isa ? m0 : n0) + row;
-          gr = gr < lim ? gr : lim - 1;
-          src = (isa ? g.a_codes : g.b_codes) + gr * kb + kbyte0 + logical * 16;
-          dst = sbase + (uint32_t)(q0 * 16);
-        }
-        lds_dma16(__builtin_amdgcn_readfirstlane(dst), src);
+        const int q0 = (j * NW + wave_u) * 64;
+        const bool real = q0 < CODE_Q, isa = q0 < BM * 4;
+        const uint8_t *base = (isa || !real ? g.a_codes : g.b_codes) + kbyte0;
+        lds_dma16(real ? sbase + (uint32_t)(q0 * 16) : spare, base, coff[j]);
       }
 #pragma unroll
       for (int j = 0; j < SC_I; ++j) {
-        const int u0 = (j * NW + wave) * 64, u = u0 + lane;
-        const uint8_t *src = g.a_scales;
-        uint32_t dst = spare;
-        if (u0 < SC_U) {
-          const bool isa = u < BM * 2;
-          const int uu = isa ? u : u - BM * 2, row = uu >> 1;
-          const int64_t lim = isa ? g.M : g.N;
-          int64_t gr = (isa ? m0 : n0) + row;
-          gr = gr < lim ? gr : lim - 1;
-          src = (isa ? g.a_scales : g.b_scales) + gr * ks + ksc0 + (uu & 1) * 4;
-          dst = sbase + (uint32_t)((BM + BN) * kRowBytes + u0 * 4);
-        }
-        lds_dma4(__builtin_amdgcn_readfirstlane(dst), src);
+        const int u0 = (j * NW + wave_u) * 64;
+        const bool real = u0 < SC_U, isa = u0 < BM * 2;
+        const uint8_t *base = (isa || !real ? g.a_scales : g.b_scales) + ksc0;
+        lds_dma4(real ? sbase + (uint32_t)((BM + BN) * kRowBytes + u0 * 4) : spare, base, soff[j]);
       }
     };
     auto stage = [&](int st) -> Stage {
@@ -443,7 +476,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
       wait_vmcnt<0>();
     }
     __syncthreads();
-    begin_tile(stage(0), av, bv);
+    begin_tile(stage(0));
     for (int kt = 0; kt < nk; ++kt) {
       if (kt + 2 < nk) issue_tile(kt + 2, (kt + 2) % 3);
       const bool more = kt + 2 < nk;
@@ -465,7 +498,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
       if (kt + 1 < nk) load_global(kt + 1);
       const uint8_t *la = lds + cur * STAGE;
       const Stage t{la, la + A_BYTES, la + A_BYTES + B_BYTES, la + A_BYTES + B_BYTES + BM * 8};
-      begin_tile(t, av, bv);
+      begin_tile(t);
       run_tile(t, t, std::false_type{}, [] {});
       if (kt + 1 < nk) store_lds(cur ^ 1);
       __syncthreads();
@@ -482,6 +515,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   // 32x32 accumulator layout: register e of lane l holds row
   // 8*(e/4) + 4*(l/32) + e%4, column l%32.
   const float scale = g.alpha * (*g.a_ts) * (*g.b_ts);
+  // (buffer offsets are 32-bit: rows up to 32 apart within one base)
+  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N && 32 * g.N * 4 + BN * 4 < (int64_t(1) << 31);
+  const int wm_u = wave_u / WN;     // wm, known uniform
   const int nchunks = (g.r + 15) / 16;                    // <= 4 (r <= 64)
   const int lrs = (g.r <= 32 ? 32 : 64) + 8;              // 80 or 144 bytes: conflict-free 16-byte reads
   uint16_t *lhi = (uint16_t *)lds, *llo = lhi + BM * lrs, *rt = llo + BM * lrs;
@@ -577,14 +613,36 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
           t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, rv, t, 0, 0, 0);
         }
       }
-      const int64_t n = n0 + brow;
+      if (interior) {
+        // Whole tile in range: buffer stores (and loads of E) from a uniform
+        // base at row m0 + wm*TM*32 + i*32, column n0, with the row offset of
+        // register e in a scalar register and this lane's offset (rows 4h..,
+        // column l32) in a vector register: no per-element address work.
+        const int64_t base = (m0 + wm_u * TM * 32 + i * 32) * g.N + n0;
+        const int nrec = (int)((g.M * g.N - base) * 4 < 0x7FFFFFFF ? (g.M * g.N - base) * 4 : 0x7FFFFFFF);
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(g.C + base, 0, nrec, kBufferWord3);
+        const int loff = (4 * h * (int)g.N + wn * TN * 32 + j * 32 + l32) * 4;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m < g.M && n < g.N) {
+        for (int e = 0; e < 16; ++e) {
+          const int soff = (8 * (e >> 2) + (e & 3)) * (int)g.N * 4;
           float v = t[e];
-          if (g.E) v += g.beta_e * g.E[m * g.N + n];
-          g.C[m * g.N + n] = v;
+          if (g.E) {
+            const __amdgpu_buffer_rsrc_t re =
+                __builtin_amdgcn_make_buffer_rsrc((float *)g.E + base, 0, nrec, kBufferWord3);
+            v += g.beta_e * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, loff, soff, 0));
+          }
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, loff, soff, 0);
+        }
+      } else {
+        const int64_t n = n0 + brow;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (m < g.M && n < g.N) {
+            float v = t[e];
+            if (g.E) v += g.beta_e * g.E[m * g.N + n];
+            g.C[m * g.N + n] = v;
+          }
         }
       }
     }
@@ -595,7 +653,9 @@ template <int WM, int WN, int TM, int TN>
 fs4_status launch_cfg(const GemmArgs &g, hipStream_t s) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  if (g.K > 0 && g.K % kBK == 0)
+  // the direct-load path addresses operands with 32-bit per-lane offsets
+  const int64_t rows = g.M > g.N ? g.M : g.N;
+  if (g.K > 0 && g.K % kBK == 0 && rows * (g.K / 2) < (int64_t(1) << 32))
     gemm_nt_kernel<WM, WN, TM, TN, true><<<(unsigned)tiles, WM * WN * 64, 0, s>>>(g);
   else
     gemm_nt_kernel<WM, WN, TM, TN, false><<<(unsigned)tiles, WM * WN * 64, 0, s>>>(g);
