@@ -94,6 +94,7 @@ struct NsWs {
   fs4_nvfp4 x_row, x_col, a_row, a_col, b_row;
   uint32_t *qws;
   void *nws;
+  uint32_t *amax;   // per-workgroup max |.| of the tensor about to be quantized
 };
 NsWs carve_ns(void *ws, int64_t m, int64_t n, size_t *total) {
   Carver c(ws);
@@ -108,6 +109,10 @@ NsWs carve_ns(void *ws, int64_t m, int64_t n, size_t *total) {
   w.b_row = carve_view(c, m, m);
   w.qws = (uint32_t *)c.take(quantize_ws_bytes());
   w.nws = c.take(normalize_ws_bytes());
+  {
+    const int64_t np = std::max<int64_t>(gemm_max_workgroups(m, n), kNormMaxParts);
+    w.amax = (uint32_t *)c.take((size_t)np * sizeof(uint32_t));
+  }
   if (total) *total = c.off;
   return w;
 }
@@ -336,18 +341,28 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
     return ((steps - k) % 2 == 0) ? X_out : w.X;
   };
   float *cur = slot(0);
-  if (normalize) FS4_TRY(launch_normalize(G, dt, mn, eps, cur, w.nws, s));
+  // Each producer (normalisation, GEMM epilogue) leaves per-workgroup amax
+  // partials of its output in w.amax, so each quantization is one encode
+  // pass; np = 0 means no partials (a plain copy), and the quantizer takes
+  // its own amax pass.
+  int np = 0;
+  if (normalize) FS4_TRY(launch_normalize(G, dt, mn, eps, cur, w.nws, s, w.amax, &np));
   else FS4_TRY(launch_copy_f32(G, dt, mn, cur, s));
+  auto quantize = [&](const float *x, int64_t rows, int64_t cols, const fs4_nvfp4 *rv,
+                      const fs4_nvfp4 *cv) -> fs4_status {
+    if (np > 0) return launch_quantize_encode(x, FS4_FP32, rows, cols, rv, cv, w.amax, np, s);
+    return launch_quantize(x, FS4_FP32, rows, cols, rv, cv, w.qws, s);
+  };
   for (int k = 0; k < steps; ++k) {
     float *A = trace_A ? trace_A + (int64_t)k * mm : w.A;
     float *B = trace_B ? trace_B + (int64_t)k * mm : w.B;
     float *next = slot(k + 1);
-    FS4_TRY(launch_quantize(cur, FS4_FP32, m, n, &w.x_row, &w.x_col, w.qws, s));
-    FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s));
-    FS4_TRY(launch_quantize(A, FS4_FP32, m, m, &w.a_row, &w.a_col, w.qws, s));
-    FS4_TRY(launch_gemm_nt(w.a_row, w.a_col, c, A, b, B, LowRankEpilogue(), s));
-    FS4_TRY(launch_quantize(B, FS4_FP32, m, m, &w.b_row, nullptr, w.qws, s));
-    FS4_TRY(launch_gemm_nt(w.b_row, w.x_col, 1.0f, cur, a, next, LowRankEpilogue(), s));
+    FS4_TRY(quantize(cur, m, n, &w.x_row, &w.x_col));
+    FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s, w.amax, &np));
+    FS4_TRY(quantize(A, m, m, &w.a_row, &w.a_col));
+    FS4_TRY(launch_gemm_nt(w.a_row, w.a_col, c, A, b, B, LowRankEpilogue(), s, w.amax, &np));
+    FS4_TRY(quantize(B, m, m, &w.b_row, nullptr));
+    FS4_TRY(launch_gemm_nt(w.b_row, w.x_col, 1.0f, cur, a, next, LowRankEpilogue(), s, w.amax, &np));
     cur = next;
   }
   if (trace_X) FS4_TRY(launch_copy_f32(cur, FS4_FP32, mn, X_out, s));

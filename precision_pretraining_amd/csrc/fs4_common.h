@@ -110,8 +110,13 @@ struct LowRankEpilogue {
   int64_t r_sn = 0, r_sj = 1;
   float l_scale = 1.0f;
 };
+// amax_parts (nullable) receives one max |C| per workgroup (fp32 bits, the
+// form launch_quantize_encode reduces); *nwg (nullable) their count, which is
+// at most gemm_max_workgroups(M, N).
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
-                          float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s);
+                          float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
+                          uint32_t *amax_parts = nullptr, int *nwg = nullptr);
+inline int64_t gemm_max_workgroups(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
 // out[a][b] = scale * sum_k P(a, k) Q(b, k) with P(a, k) = P[a*p_sa + k*p_sk],
 // Q(b, k) = Q[b*q_sb + k*q_sk]; each operand bf16 or fp32 (p_f32 / q_f32);
@@ -144,8 +149,12 @@ fs4_status launch_colred(const uint16_t *A, const float *Bm, int64_t M, int64_t 
 fs4_status launch_transpose_rank(const uint16_t *U, int64_t N, int r, uint16_t *Ut, hipStream_t s);
 // Frobenius normalisation X = G / (||G||_F + eps), fp64 accumulation
 size_t normalize_ws_bytes();
+// X = G / (||G||_F + eps) in fp32; amax_parts (nullable) receives one max |X|
+// per workgroup, *nparts (nullable) their count (at most 2048).
 fs4_status launch_normalize(const void *G, fs4_dtype dt, int64_t n, float eps, float *X,
-                            void *ws, hipStream_t s);
+                            void *ws, hipStream_t s, uint32_t *amax_parts = nullptr,
+                            int *nparts = nullptr);
+constexpr int kNormMaxParts = 2048;
 fs4_status launch_copy_f32(const void *src, fs4_dtype dt, int64_t n, float *dst, hipStream_t s);
 
 }  // namespace fs4

@@ -70,6 +70,7 @@ struct GemmArgs {
   const uint16_t *R;
   int64_t r_sn, r_sj;
   int r;
+  uint32_t *amax_parts;   // nullable: per-workgroup max |C| (fp32 bits)
 };
 
 // E4M3 block scale -> (2^E as fp32, F as a pair of FP16) with s_b = 2^E F.
@@ -518,6 +519,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   // (buffer offsets are 32-bit: rows up to 32 apart within one base)
   const bool interior = m0 + BM <= g.M && n0 + BN <= g.N && 32 * g.N * 4 + BN * 4 < (int64_t(1) << 31);
   const int wm_u = wave_u / WN;     // wm, known uniform
+  float amax = 0.0f;                // max |C| over this thread's stored elements
   const int nchunks = (g.r + 15) / 16;                    // <= 4 (r <= 64)
   const int lrs = (g.r <= 32 ? 32 : 64) + 8;              // 80 or 144 bytes: conflict-free 16-byte reads
   uint16_t *lhi = (uint16_t *)lds, *llo = lhi + BM * lrs, *rt = llo + BM * lrs;
@@ -631,6 +633,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
                 __builtin_amdgcn_make_buffer_rsrc((float *)g.E + base, 0, nrec, kBufferWord3);
             v += g.beta_e * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, loff, soff, 0));
           }
+          if (g.amax_parts) amax = fmaxf(amax, fabsf(v));
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, loff, soff, 0);
         }
       } else {
@@ -642,17 +645,37 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
             float v = t[e];
             if (g.E) v += g.beta_e * g.E[m * g.N + n];
             g.C[m * g.N + n] = v;
+            if (g.amax_parts) amax = fmaxf(amax, fabsf(v));
           }
         }
       }
     }
   }
+  if (g.amax_parts) {
+    // workgroup max (non-negative floats order as their bit patterns)
+    __shared__ uint32_t wmax[NT / 64];
+    uint32_t u = __builtin_bit_cast(uint32_t, amax);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint32_t v = (uint32_t)__shfl_xor((int)u, o);
+      u = u > v ? u : v;
+    }
+    if (lane == 0) wmax[wave] = u;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = wmax[0];
+#pragma unroll
+      for (int w = 1; w < NT / 64; ++w) m = m > wmax[w] ? m : wmax[w];
+      g.amax_parts[blockIdx.x] = m;
+    }
+  }
 }
 
 template <int WM, int WN, int TM, int TN>
-fs4_status launch_cfg(const GemmArgs &g, hipStream_t s) {
+fs4_status launch_cfg(const GemmArgs &g, hipStream_t s, int *nwg) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  if (nwg) *nwg = (int)tiles;
   // the direct-load path addresses operands with 32-bit per-lane offsets
   const int64_t rows = g.M > g.N ? g.M : g.N;
   if (g.K > 0 && g.K % kBK == 0 && rows * (g.K / 2) < (int64_t(1) << 32))
@@ -665,8 +688,11 @@ fs4_status launch_cfg(const GemmArgs &g, hipStream_t s) {
 }  // namespace
 
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
-                          float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s) {
+                          float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
+                          uint32_t *amax_parts, int *nwg) {
   GemmArgs g;
+  g.amax_parts = amax_parts;
+  if (nwg) *nwg = 0;
   g.a_codes = A.codes; g.a_scales = A.scales; g.a_ts = A.tscale;
   g.b_codes = B.codes; g.b_scales = B.scales; g.b_ts = B.tscale;
   g.M = A.rows; g.N = B.rows; g.K = A.cols;
@@ -687,9 +713,9 @@ fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, c
     return (double)((tiles + 255) / 256) * (double)(bm * bn) / rate;
   };
   const double c256 = cost(256, 256, 1.0), c192 = cost(256, 192, 0.83), c128 = cost(128, 128, 0.70);
-  if (c256 <= c192 && c256 <= c128) return launch_cfg<2, 4, 4, 2>(g, s);
-  if (c192 <= c128) return launch_cfg<2, 2, 4, 3>(g, s);
-  return launch_cfg<2, 2, 2, 2>(g, s);
+  if (c256 <= c192 && c256 <= c128) return launch_cfg<2, 4, 4, 2>(g, s, nwg);
+  if (c192 <= c128) return launch_cfg<2, 2, 4, 3>(g, s, nwg);
+  return launch_cfg<2, 2, 2, 2>(g, s, nwg);
 }
 
 }  // namespace fs4

@@ -583,6 +583,7 @@ size_t small_gemm_partials_bytes(int64_t Na, int64_t Nb, int64_t Kc) {
 namespace {
 
 constexpr int kNormParts = 1024;
+constexpr int kNormBlocks = 2048;   // scale_kernel workgroups (and amax partials)
 
 // Eight consecutive elements (one 16-byte word of bf16, two of fp32) as double.
 template <bool BF16>
@@ -628,21 +629,45 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const void *__restrict__ x, 
 template <bool BF16>
 __global__ __launch_bounds__(256) void scale_kernel(const void *__restrict__ x, int64_t nv,
                                                     const double *__restrict__ parts, int nparts,
-                                                    double eps, float *__restrict__ out) {
-  __shared__ double inv_s;
-  if (threadIdx.x == 0) {
-    double s = 0.0;
-    for (int p = 0; p < nparts; ++p) s += parts[p];
-    inv_s = 1.0 / (__builtin_sqrt(s) + eps);
-  }
+                                                    double eps, float *__restrict__ out,
+                                                    uint32_t *__restrict__ amax_parts) {
+  // every block reduces the partial sums the same way (fixed order): a
+  // strided sum per thread, then a tree over the block
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int p = threadIdx.x; p < nparts; p += 256) s += parts[p];
+  red[threadIdx.x] = s;
   __syncthreads();
-  const double inv = inv_s;
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const double inv = 1.0 / (__builtin_sqrt(red[0]) + eps);
+  float am = 0.0f;
   for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += (int64_t)gridDim.x * 256) {
     double o[8];
     load8d<BF16>(x, v, o);
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      f[q] = (float)(o[q] * inv);
+      am = fmaxf(am, fabsf(f[q]));
+    }
     float4 *d = (float4 *)out + 2 * v;
-    d[0] = make_float4((float)(o[0] * inv), (float)(o[1] * inv), (float)(o[2] * inv), (float)(o[3] * inv));
-    d[1] = make_float4((float)(o[4] * inv), (float)(o[5] * inv), (float)(o[6] * inv), (float)(o[7] * inv));
+    d[0] = make_float4(f[0], f[1], f[2], f[3]);
+    d[1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  if (amax_parts) {
+    // block max of the written values, for the quantizer that follows
+    // (non-negative floats order as their bit patterns)
+    __shared__ uint32_t bm[256];
+    bm[threadIdx.x] = __builtin_bit_cast(uint32_t, am);
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) bm[threadIdx.x] = bm[threadIdx.x] > bm[threadIdx.x + w] ? bm[threadIdx.x] : bm[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) amax_parts[blockIdx.x] = bm[0];
   }
 }
 
@@ -663,19 +688,20 @@ __global__ __launch_bounds__(256) void copy_kernel(const void *__restrict__ x, i
 size_t normalize_ws_bytes() { return kNormParts * sizeof(double); }
 
 fs4_status launch_normalize(const void *G, fs4_dtype dt, int64_t n, float eps, float *X, void *ws,
-                            hipStream_t s) {
+                            hipStream_t s, uint32_t *amax_parts, int *nparts) {
   // n is a multiple of 16 (both dimensions are); 8-element words
   double *parts = (double *)ws;
   const int64_t nv = n / 8;
   int64_t g = (nv + 256 * 4 - 1) / (256 * 4);
   const int np = (int)(g < 1 ? 1 : (g > kNormParts ? kNormParts : g));
-  const unsigned gs = (unsigned)((nv + 255) / 256 < 4096 ? (nv + 255) / 256 : 4096);
+  const unsigned gs = (unsigned)((nv + 255) / 256 < kNormBlocks ? (nv + 255) / 256 : kNormBlocks);
+  if (nparts) *nparts = (int)gs;
   if (dt == FS4_BF16) {
     sumsq_kernel<true><<<np, 256, 0, s>>>(G, nv, parts);
-    scale_kernel<true><<<gs, 256, 0, s>>>(G, nv, parts, np, (double)eps, X);
+    scale_kernel<true><<<gs, 256, 0, s>>>(G, nv, parts, np, (double)eps, X, amax_parts);
   } else {
     sumsq_kernel<false><<<np, 256, 0, s>>>(G, nv, parts);
-    scale_kernel<false><<<gs, 256, 0, s>>>(G, nv, parts, np, (double)eps, X);
+    scale_kernel<false><<<gs, 256, 0, s>>>(G, nv, parts, np, (double)eps, X, amax_parts);
   }
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
