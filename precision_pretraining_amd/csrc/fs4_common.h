@@ -98,7 +98,7 @@ fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t co
                            const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                            void *ws, hipStream_t s);
 // The encode pass alone, for a caller whose earlier kernel already wrote npart
-// (1..kAmaxPartials) partial maxima of |x| (fp32 bits) that cover all of x.
+// (npart >= 1) partial maxima of |x| (fp32 bits) that cover all of x.
 fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                                   const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                                   const uint32_t *partials, int npart, hipStream_t s);
