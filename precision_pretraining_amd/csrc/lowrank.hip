@@ -173,8 +173,18 @@ __global__ void reduce_partials_kernel(const float *__restrict__ partials, int S
                                        bool transpose_out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= Na * Nb) return;
+  // (unrolled so that eight loads are in flight; the sum order stays p = 0, 1, ..)
+  const int64_t stride = Na * Nb;
   float s = 0.0f;
-  for (int p = 0; p < S; ++p) s += partials[(int64_t)p * Na * Nb + i];
+  int p = 0;
+  for (; p + 8 <= S; p += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = partials[(int64_t)(p + q) * stride + i];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += v[q];
+  }
+  for (; p < S; ++p) s += partials[(int64_t)p * stride + i];
   const int64_t ra = i / Nb, cb = i % Nb;
   out[transpose_out ? cb * Na + ra : i] = scale * s;
 }
