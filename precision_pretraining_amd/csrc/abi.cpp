@@ -91,7 +91,7 @@ BwdWs carve_bwd(void *ws, int64_t M, int64_t N, int64_t K, int r, size_t *total)
 
 struct NsWs {
   float *X, *A, *B;
-  fs4_nvfp4 x_row, x_col, a_row, a_col, b_row;
+  fs4_nvfp4 x_row, x_col, a_row, b_row;
   uint32_t *qws;
   void *nws;
   uint32_t *amax;   // per-workgroup max |.| of the tensor about to be quantized
@@ -105,7 +105,6 @@ NsWs carve_ns(void *ws, int64_t m, int64_t n, size_t *total) {
   w.x_row = carve_view(c, m, n);
   w.x_col = carve_view(c, n, m);
   w.a_row = carve_view(c, m, m);
-  w.a_col = carve_view(c, m, m);
   w.b_row = carve_view(c, m, m);
   w.qws = (uint32_t *)c.take(quantize_ws_bytes());
   w.nws = c.take(normalize_ws_bytes());
@@ -357,10 +356,13 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
     float *A = trace_A ? trace_A + (int64_t)k * mm : w.A;
     float *B = trace_B ? trace_B + (int64_t)k * mm : w.B;
     float *next = slot(k + 1);
+    // A = Q(X) Q(X)^T is computed (and stored) exactly symmetric, so its
+    // column-wise quantization is its row-wise one bit for bit, and
+    // A^2 = Q_row(A) Q_col(A)^T = Q(A) Q(A)^T is symmetric as well.
     FS4_TRY(quantize(cur, m, n, &w.x_row, &w.x_col));
-    FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s, w.amax, &np));
-    FS4_TRY(quantize(A, m, m, &w.a_row, &w.a_col));
-    FS4_TRY(launch_gemm_nt(w.a_row, w.a_col, c, A, b, B, LowRankEpilogue(), s, w.amax, &np));
+    FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s, w.amax, &np, true));
+    FS4_TRY(quantize(A, m, m, &w.a_row, nullptr));
+    FS4_TRY(launch_gemm_nt(w.a_row, w.a_row, c, A, b, B, LowRankEpilogue(), s, w.amax, &np, true));
     FS4_TRY(quantize(B, m, m, &w.b_row, nullptr));
     FS4_TRY(launch_gemm_nt(w.b_row, w.x_col, 1.0f, cur, a, next, LowRankEpilogue(), s, w.amax, &np));
     cur = next;

@@ -110,12 +110,15 @@ struct LowRankEpilogue {
   int64_t r_sn = 0, r_sj = 1;
   float l_scale = 1.0f;
 };
-// amax_parts (nullable) receives one max |C| per workgroup (fp32 bits, the
+// amax_parts (nullable) receives one max |C| per output tile (fp32 bits, the
 // form launch_quantize_encode reduces); *nwg (nullable) their count, which is
-// at most gemm_max_workgroups(M, N).
+// at most gemm_max_workgroups(M, N).  sym: B is the same view as A, there is
+// no rank-r term and E, if any, is symmetric, so C is symmetric: only the
+// upper triangle's tiles are computed, each stored at both positions (the
+// flag is ignored when A and B differ).
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
                           float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
-                          uint32_t *amax_parts = nullptr, int *nwg = nullptr);
+                          uint32_t *amax_parts = nullptr, int *nwg = nullptr, bool sym = false);
 inline int64_t gemm_max_workgroups(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
 // out[a][b] = scale * sum_k P(a, k) Q(b, k) with P(a, k) = P[a*p_sa + k*p_sk],

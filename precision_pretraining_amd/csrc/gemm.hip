@@ -70,7 +70,10 @@ struct GemmArgs {
   const uint16_t *R;
   int64_t r_sn, r_sj;
   int r;
-  uint32_t *amax_parts;   // nullable: per-workgroup max |C| (fp32 bits)
+  uint32_t *amax_parts;   // nullable: per-tile max |C| (fp32 bits)
+  // sym: C is symmetric (A and B the same view): only tiles with
+  // tile_m <= tile_n are computed, each stored at both positions.
+  int sym;
 };
 
 // E4M3 block scale -> (2^E as fp32, F as a pair of FP16) with s_b = 2^E F.
@@ -194,8 +197,17 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   __shared__ uint2 scale_lut[256];
 
   const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int64_t tile = blockIdx.x;
   int64_t tile_m, tile_n;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, &tile_m, &tile_n);
+  if (g.sym) {
+    // tile -> (tile_m <= tile_n), row by row of the upper triangle
+    int64_t t = tile, tm = 0;
+    while (t >= tiles_n - tm) { t -= tiles_n - tm; ++tm; }
+    tile_m = tm;
+    tile_n = tm + t;
+  } else {
+    tile_coords(tile, tiles_m, tiles_n, &tile_m, &tile_n);
+  }
   const int64_t m0 = tile_m * BM, n0 = tile_n * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -615,6 +627,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
           t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, rv, t, 0, 0, 0);
         }
       }
+      float vv[16];   // the stored values (for the mirrored store of a symmetric C)
       if (interior) {
         // Whole tile in range: buffer stores (and loads of E) from a uniform
         // base at row m0 + wm*TM*32 + i*32, column n0, with the row offset of
@@ -635,18 +648,32 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
           }
           if (g.amax_parts) amax = fmaxf(amax, fabsf(v));
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, loff, soff, 0);
+          vv[e] = v;
         }
       } else {
         const int64_t n = n0 + brow;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          vv[e] = 0.0f;
           if (m < g.M && n < g.N) {
             float v = t[e];
             if (g.E) v += g.beta_e * g.E[m * g.N + n];
             g.C[m * g.N + n] = v;
             if (g.amax_parts) amax = fmaxf(amax, fabsf(v));
+            vv[e] = v;
           }
+        }
+      }
+      if (g.sym && tile_m != tile_n) {
+        // C[n][m] = C[m][n]: this lane's column n becomes a row, its rows m
+        // (four runs of four) become 16-byte pieces of that row
+        const int64_t n = n0 + brow;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * q + 4 * h;
+          if (n < g.M && m < g.N)
+            *(float4 *)(g.C + n * g.N + m) = make_float4(vv[4 * q], vv[4 * q + 1], vv[4 * q + 2], vv[4 * q + 3]);
         }
       }
     }
@@ -666,15 +693,13 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
       uint32_t m = wmax[0];
 #pragma unroll
       for (int w = 1; w < NT / 64; ++w) m = m > wmax[w] ? m : wmax[w];
-      g.amax_parts[blockIdx.x] = m;
+      g.amax_parts[tile] = m;
     }
   }
 }
 
 template <int WM, int WN, int TM, int TN>
-fs4_status launch_cfg(const GemmArgs &g, hipStream_t s, int *nwg) {
-  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+fs4_status launch_cfg(const GemmArgs &g, int64_t tiles, hipStream_t s, int *nwg) {
   if (nwg) *nwg = (int)tiles;
   // the direct-load path addresses operands with 32-bit per-lane offsets
   const int64_t rows = g.M > g.N ? g.M : g.N;
@@ -689,7 +714,7 @@ fs4_status launch_cfg(const GemmArgs &g, hipStream_t s, int *nwg) {
 
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
                           float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
-                          uint32_t *amax_parts, int *nwg) {
+                          uint32_t *amax_parts, int *nwg, bool sym) {
   GemmArgs g;
   g.amax_parts = amax_parts;
   if (nwg) *nwg = 0;
@@ -699,6 +724,9 @@ fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, c
   g.alpha = alpha; g.beta_e = beta_e; g.E = E; g.C = C;
   g.L = lr.L; g.R = lr.R; g.r = lr.L ? lr.r : 0; g.l_scale = lr.l_scale;
   g.r_sn = lr.r_sn; g.r_sj = lr.r_sj;
+  // a symmetric product (B the same view as A) stores only the upper
+  // triangle's tiles, each at both positions; not with a rank-r term
+  g.sym = sym && A.codes == B.codes && A.scales == B.scales && g.M == g.N && g.r == 0 ? 1 : 0;
   if (g.M == 0 || g.N == 0) return FS4_OK;
   // Tile shape: the one with the least estimated time, counted as rounds of
   // workgroups over the 256 CUs times tile area over the configuration's
@@ -708,14 +736,19 @@ fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, c
   //   128 x 128, 4 waves of 64 x 64                   0.70
   // Whole rounds matter: 384 tiles of 256 x 256 (an 8192 x 3072 output) leave
   // half the chip idle in the second round, 512 tiles of 256 x 192 do not.
-  auto cost = [&](int64_t bm, int64_t bn, double rate) {
-    const int64_t tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
-    return (double)((tiles + 255) / 256) * (double)(bm * bn) / rate;
+  // A symmetric product counts the upper triangle's tiles (square tiles only).
+  auto tiles_of = [&](int64_t bm, int64_t bn) {
+    const int64_t tm = (g.M + bm - 1) / bm, tn = (g.N + bn - 1) / bn;
+    return g.sym ? tm * (tm + 1) / 2 : tm * tn;
   };
-  const double c256 = cost(256, 256, 1.0), c192 = cost(256, 192, 0.83), c128 = cost(128, 128, 0.70);
-  if (c256 <= c192 && c256 <= c128) return launch_cfg<2, 4, 4, 2>(g, s, nwg);
-  if (c192 <= c128) return launch_cfg<2, 2, 4, 3>(g, s, nwg);
-  return launch_cfg<2, 2, 2, 2>(g, s, nwg);
+  auto cost = [&](int64_t bm, int64_t bn, double rate) {
+    return (double)((tiles_of(bm, bn) + 255) / 256) * (double)(bm * bn) / rate;
+  };
+  const double c0 = cost(256, 256, 1.0), c2 = cost(128, 128, 0.70);
+  const double c1 = g.sym ? 1e300 : cost(256, 192, 0.83);
+  if (c0 <= c1 && c0 <= c2) return launch_cfg<2, 4, 4, 2>(g, tiles_of(256, 256), s, nwg);
+  if (c1 <= c2) return launch_cfg<2, 2, 4, 3>(g, tiles_of(256, 192), s, nwg);
+  return launch_cfg<2, 2, 2, 2>(g, tiles_of(128, 128), s, nwg);
 }
 
 }  // namespace fs4
