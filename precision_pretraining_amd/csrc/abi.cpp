@@ -95,6 +95,8 @@ struct NsWs {
   uint32_t *qws;
   void *nws;
   uint32_t *amax;   // per-workgroup max |.| of the tensor about to be quantized
+  float *split;     // split-k partials of the GEMMs
+  int64_t split_floats;
 };
 NsWs carve_ns(void *ws, int64_t m, int64_t n, size_t *total) {
   Carver c(ws);
@@ -111,6 +113,13 @@ NsWs carve_ns(void *ws, int64_t m, int64_t n, size_t *total) {
   {
     const int64_t np = std::max<int64_t>(gemm_max_workgroups(m, n), kNormMaxParts);
     w.amax = (uint32_t *)c.take((size_t)np * sizeof(uint32_t));
+  }
+  {
+    // partials of at most 8 splits of tiles no larger than 256 x 256 that
+    // cover the output at most once
+    const int64_t r256 = (m + 255) / 256 * 256, c256 = (std::max(m, n) + 255) / 256 * 256;
+    w.split_floats = std::min<int64_t>(kGemmSplitFloats, 8 * r256 * c256);
+    w.split = (float *)c.take((size_t)w.split_floats * sizeof(float));
   }
   if (total) *total = c.off;
   return w;
@@ -360,11 +369,14 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
     // column-wise quantization is its row-wise one bit for bit, and
     // A^2 = Q_row(A) Q_col(A)^T = Q(A) Q(A)^T is symmetric as well.
     FS4_TRY(quantize(cur, m, n, &w.x_row, &w.x_col));
-    FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s, w.amax, &np, true));
+    FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s, w.amax, &np, true,
+                           w.split, w.split_floats));
     FS4_TRY(quantize(A, m, m, &w.a_row, nullptr));
-    FS4_TRY(launch_gemm_nt(w.a_row, w.a_row, c, A, b, B, LowRankEpilogue(), s, w.amax, &np, true));
+    FS4_TRY(launch_gemm_nt(w.a_row, w.a_row, c, A, b, B, LowRankEpilogue(), s, w.amax, &np, true, w.split,
+                           w.split_floats));
     FS4_TRY(quantize(B, m, m, &w.b_row, nullptr));
-    FS4_TRY(launch_gemm_nt(w.b_row, w.x_col, 1.0f, cur, a, next, LowRankEpilogue(), s, w.amax, &np));
+    FS4_TRY(launch_gemm_nt(w.b_row, w.x_col, 1.0f, cur, a, next, LowRankEpilogue(), s, w.amax, &np, false,
+                           w.split, w.split_floats));
     cur = next;
   }
   if (trace_X) FS4_TRY(launch_copy_f32(cur, FS4_FP32, mn, X_out, s));

@@ -115,10 +115,16 @@ struct LowRankEpilogue {
 // at most gemm_max_workgroups(M, N).  sym: B is the same view as A, there is
 // no rank-r term and E, if any, is symmetric, so C is symmetric: only the
 // upper triangle's tiles are computed, each stored at both positions (the
-// flag is ignored when A and B differ).
+// flag is ignored when A and B differ).  split_ws (nullable, split_floats
+// floats, at least kGemmSplitFloats to allow every split) lets the tiles of a
+// part-filled last round run split along k (fp32 partials, then a reduce
+// launch); without it, or with a rank-r term, tiles run whole.
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
                           float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
-                          uint32_t *amax_parts = nullptr, int *nwg = nullptr, bool sym = false);
+                          uint32_t *amax_parts = nullptr, int *nwg = nullptr, bool sym = false,
+                          float *split_ws = nullptr, int64_t split_floats = 0);
+// one round of 256 workgroups of split partials, 256 x 256 floats each
+constexpr int64_t kGemmSplitFloats = int64_t(256) * 256 * 256;
 inline int64_t gemm_max_workgroups(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
 // out[a][b] = scale * sum_k P(a, k) Q(b, k) with P(a, k) = P[a*p_sa + k*p_sk],

@@ -74,6 +74,14 @@ struct GemmArgs {
   // sym: C is symmetric (A and B the same view): only tiles with
   // tile_m <= tile_n are computed, each stored at both positions.
   int sym;
+  // Split-k: tiles [0, t_full) run whole, one workgroup each; every later
+  // tile runs as s_tail workgroups over consecutive ranges of whole k-tiles,
+  // which store their raw fp32 accumulators to `part` (slot (tile - t_full)
+  // * s_tail + split, in accumulator order) and end; split_reduce_kernel
+  // then adds them in split order and runs the epilogue.
+  int64_t t_full;
+  int s_tail;
+  float *part;
 };
 
 // E4M3 block scale -> (2^E as fp32, F as a pair of FP16) with s_b = 2^E F.
@@ -197,7 +205,15 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   __shared__ uint2 scale_lut[256];
 
   const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  const int64_t tile = blockIdx.x;
+  // workgroup -> (tile, split)
+  const int64_t wu = blockIdx.x;
+  int64_t tile = wu;
+  int S = 1, sp = 0;
+  if (wu >= g.t_full) {
+    tile = g.t_full + (wu - g.t_full) / g.s_tail;
+    sp = (int)((wu - g.t_full) % g.s_tail);
+    S = g.s_tail;
+  }
   int64_t tile_m, tile_n;
   if (g.sym) {
     // tile -> (tile_m <= tile_n), row by row of the upper triangle
@@ -214,7 +230,11 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the same value, known uniform
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t K = g.K, kb = K / 2, ks = K / kBlock;
-  const int nk = (int)((K + kBK - 1) / kBK);
+  const int nk_all = (int)((K + kBK - 1) / kBK);
+  const int kt_per = (nk_all + S - 1) / S;
+  // (uniform values, kept in scalar registers: they form load addresses)
+  const int kt0 = __builtin_amdgcn_readfirstlane(sp * kt_per);   // this split's first k-tile
+  const int nk = __builtin_amdgcn_readfirstlane((kt0 + kt_per < nk_all ? kt0 + kt_per : nk_all) - kt0);
 
   // ---- global -> register staging ----------------------------------------
   constexpr int CH = KFAST ? 16 : 8;
@@ -231,7 +251,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   schunk_t rsa[SA_CH], rsb[SB_CH];
 
   auto load_global = [&](int kt) {
-    const int64_t kbyte0 = (int64_t)kt * kRowBytes, ksc0 = (int64_t)kt * 8;
+    const int64_t kbyte0 = (int64_t)(kt0 + kt) * kRowBytes, ksc0 = (int64_t)(kt0 + kt) * 8;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT;
@@ -461,7 +481,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
     }
     auto issue_tile = [&](int kt, int st) {
       const uint32_t sbase = lds0 + (uint32_t)(st * STAGE_D), spare = lds0 + 3u * STAGE_D;
-      const int64_t kbyte0 = (int64_t)kt * kRowBytes, ksc0 = (int64_t)kt * 8;
+      const int64_t kbyte0 = (int64_t)(kt0 + kt) * kRowBytes, ksc0 = (int64_t)(kt0 + kt) * 8;
 #pragma unroll
       for (int j = 0; j < CODE_I; ++j) {
         const int q0 = (j * NW + wave_u) * 64;
@@ -516,6 +536,20 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
       if (kt + 1 < nk) store_lds(cur ^ 1);
       __syncthreads();
     }
+  }
+
+  if (S > 1) {
+    // a split's raw accumulators, coalesced: element e of MFMA tile (i, j) of
+    // thread tid at [((i * TN + j) * 16 + e) * NT + tid]
+    float *my = g.part + ((tile - g.t_full) * S + sp) * (int64_t)(BM * BN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) my[((i * TN + j) * 16 + e) * NT + tid] = acc[i][j][e];
+    if (g.amax_parts && sp == 0 && tid == 0) g.amax_parts[tile] = 0u;   // the reduce folds into it
+    return;
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -698,24 +732,124 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   }
 }
 
+// Adds the split partials of tiles t_full.. in split order and runs the
+// epilogue: C = alpha s_tA s_tB sum + beta_e E (no rank-r term), mirrored
+// for a symmetric C, and folds each tile's max |C| into amax_parts (which the
+// tile's first split set to 0).  One thread per four consecutive partials:
+// in accumulator order those are four adjacent lanes of one GEMM thread
+// register, i.e. C[m][n .. n+3]; kSplitReduceWg of them per tile.
+constexpr int kSplitReduceThreads = 256;
 template <int WM, int WN, int TM, int TN>
-fs4_status launch_cfg(const GemmArgs &g, int64_t tiles, hipStream_t s, int *nwg) {
+__global__ __launch_bounds__(kSplitReduceThreads) void split_reduce_kernel(GemmArgs g) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int WG_PER_TILE = BM * BN / 4 / kSplitReduceThreads;
+  static_assert(BM * BN % (4 * kSplitReduceThreads) == 0 && NT % 64 == 0, "reduce mapping");
+  const int64_t slot = blockIdx.x / WG_PER_TILE, tile = g.t_full + slot, S = g.s_tail;
+  const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  int64_t tile_m, tile_n;
+  if (g.sym) {
+    int64_t t = tile, tm = 0;
+    while (t >= tiles_n - tm) { t -= tiles_n - tm; ++tm; }
+    tile_m = tm;
+    tile_n = tm + t;
+  } else {
+    tile_coords(tile, tiles_m, tiles_n, &tile_m, &tile_n);
+  }
+  // flat partial index f = ((i * TN + j) * 16 + e) * NT + t  (t: GEMM thread)
+  const int f = ((int)(blockIdx.x % WG_PER_TILE) * kSplitReduceThreads + (int)threadIdx.x) * 4;
+  const int t = f % NT, ije = f / NT, e = ije % 16, i = ije / 16 / TN, j = ije / 16 % TN;
+  const int wave = t >> 6, lane = t & 63;
+  const int wm = wave / WN, wn = wave % WN, h = lane >> 5, l32 = lane & 31;
+  const int64_t m = tile_m * BM + wm * TM * 32 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+  const int64_t n = tile_n * BN + wn * TN * 32 + j * 32 + l32;     // .. n + 3
+  const float *base = g.part + slot * S * (int64_t)(BM * BN) + f;
+  float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int64_t q = 0; q < S; ++q) {          // in split order
+    const float4 p = *(const float4 *)(base + q * (BM * BN));
+    sum.x += p.x; sum.y += p.y; sum.z += p.z; sum.w += p.w;
+  }
+  const float scale = g.alpha * (*g.a_ts) * (*g.b_ts);
+  float v[4] = {scale * sum.x, scale * sum.y, scale * sum.z, scale * sum.w};
+  float amax = 0.0f;
+  if (m < g.M) {
+    const int64_t o = m * g.N + n;
+    const bool vec = n + 3 < g.N && (((uintptr_t)(g.C + o) | (g.E ? (uintptr_t)(g.E + o) : 0)) & 15u) == 0;
+    if (vec) {
+      if (g.E) {
+        const float4 ev = *(const float4 *)(g.E + o);
+        v[0] += g.beta_e * ev.x; v[1] += g.beta_e * ev.y; v[2] += g.beta_e * ev.z; v[3] += g.beta_e * ev.w;
+      }
+      *(float4 *)(g.C + o) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) amax = fmaxf(amax, fabsf(v[c]));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (n + c < g.N) {
+          if (g.E) v[c] += g.beta_e * g.E[o + c];
+          g.C[o + c] = v[c];
+          amax = fmaxf(amax, fabsf(v[c]));
+        }
+    }
+    if (g.sym && tile_m != tile_n) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (n + c < g.M && m < g.N) g.C[(n + c) * g.N + m] = v[c];
+    }
+  }
+  if (g.amax_parts) {
+    __shared__ uint32_t wmax[kSplitReduceThreads / 64];
+    uint32_t u = __builtin_bit_cast(uint32_t, amax);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint32_t w = (uint32_t)__shfl_xor((int)u, o);
+      u = u > w ? u : w;
+    }
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = u;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t mx = wmax[0];
+#pragma unroll
+      for (int w = 1; w < kSplitReduceThreads / 64; ++w) mx = mx > wmax[w] ? mx : wmax[w];
+      // non-negative floats order as their bit patterns
+      atomicMax(g.amax_parts + tile, mx);
+    }
+  }
+}
+
+template <int WM, int WN, int TM, int TN>
+fs4_status launch_cfg(GemmArgs g, int64_t tiles, int64_t t_full, int s_tail, hipStream_t s, int *nwg) {
   if (nwg) *nwg = (int)tiles;
+  g.t_full = t_full;
+  g.s_tail = s_tail;
+  const int64_t wgs = t_full + (tiles - t_full) * s_tail;
   // the direct-load path addresses operands with 32-bit per-lane offsets
   const int64_t rows = g.M > g.N ? g.M : g.N;
   if (g.K > 0 && g.K % kBK == 0 && rows * (g.K / 2) < (int64_t(1) << 32))
-    gemm_nt_kernel<WM, WN, TM, TN, true><<<(unsigned)tiles, WM * WN * 64, 0, s>>>(g);
+    gemm_nt_kernel<WM, WN, TM, TN, true><<<(unsigned)wgs, WM * WN * 64, 0, s>>>(g);
   else
-    gemm_nt_kernel<WM, WN, TM, TN, false><<<(unsigned)tiles, WM * WN * 64, 0, s>>>(g);
-  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+    gemm_nt_kernel<WM, WN, TM, TN, false><<<(unsigned)wgs, WM * WN * 64, 0, s>>>(g);
+  if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
+  if (s_tail > 1) {
+    constexpr int WG_PER_TILE = WM * TM * 32 * WN * TN * 32 / 4 / kSplitReduceThreads;
+    split_reduce_kernel<WM, WN, TM, TN>
+        <<<(unsigned)((tiles - t_full) * WG_PER_TILE), kSplitReduceThreads, 0, s>>>(g);
+    if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
+  }
+  return FS4_OK;
 }
 
 }  // namespace
 
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
                           float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
-                          uint32_t *amax_parts, int *nwg, bool sym) {
+                          uint32_t *amax_parts, int *nwg, bool sym, float *split_ws,
+                          int64_t split_floats) {
   GemmArgs g;
+  g.t_full = 0;
+  g.s_tail = 1;
+  g.part = split_ws;
   g.amax_parts = amax_parts;
   if (nwg) *nwg = 0;
   g.a_codes = A.codes; g.a_scales = A.scales; g.a_ts = A.tscale;
@@ -728,27 +862,64 @@ fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, c
   // triangle's tiles, each at both positions; not with a rank-r term
   g.sym = sym && A.codes == B.codes && A.scales == B.scales && g.M == g.N && g.r == 0 ? 1 : 0;
   if (g.M == 0 || g.N == 0) return FS4_OK;
-  // Tile shape: the one with the least estimated time, counted as rounds of
-  // workgroups over the 256 CUs times tile area over the configuration's
-  // relative MFMA throughput (measured on MI355X at the 3B shapes):
+  // Plan: the tile shape and work split with the least estimated time.  One
+  // k-tile (128 deep) of a 256 x 256 tile takes ~3.9 us on a CU (measured on
+  // MI355X at the 3B shapes); the configurations' relative MFMA throughput:
   //   256 x 256, 8 waves of 128 x 64 (two per SIMD)   1.00
   //   256 x 192, 4 waves of 128 x 96 (one per SIMD)   0.83
   //   128 x 128, 4 waves of 64 x 64                   0.70
-  // Whole rounds matter: 384 tiles of 256 x 256 (an 8192 x 3072 output) leave
-  // half the chip idle in the second round, 512 tiles of 256 x 192 do not.
-  // A symmetric product counts the upper triangle's tiles (square tiles only).
-  auto tiles_of = [&](int64_t bm, int64_t bn) {
+  // Tiles run in rounds of 256 workgroups (one per CU), and whole rounds
+  // matter: 384 tiles of 256 x 256 (an 8192 x 3072 output) leave half the
+  // chip idle in the second round, 512 tiles of 256 x 192 do not.  A
+  // symmetric product counts the upper triangle's tiles (square tiles only).
+  // With a split workspace (and no rank-r term) the tiles of a last round
+  // that fills at most half the chip are split along k so that it fills the
+  // chip, for the price of writing and re-reading fp32 partials (counted at
+  // 4 TB/s) and a reduce launch (~4 us).
+  const int64_t nk_all = (g.K + kBK - 1) / kBK;
+  const bool can_split = split_ws && g.r == 0 && g.K > 0 && g.K % kBK == 0;
+  struct Plan {
+    int cfg;
+    int64_t tiles, t_full;
+    int s_tail;
+    double cost;
+  };
+  auto plan = [&](int cfg, int64_t bm, int64_t bn, double rate) {
+    Plan p{cfg, 0, 0, 1, 0.0};
     const int64_t tm = (g.M + bm - 1) / bm, tn = (g.N + bn - 1) / bn;
-    return g.sym ? tm * (tm + 1) / 2 : tm * tn;
+    p.tiles = g.sym ? tm * (tm + 1) / 2 : tm * tn;
+    p.t_full = p.tiles;
+    const double tk = 3.9e-6 * (double)(bm * bn) / 65536.0 / rate;
+    p.cost = (double)((p.tiles + 255) / 256) * (double)nk_all * tk;
+    const int64_t tail = p.tiles % 256;
+    if (can_split && tail > 0 && tail <= 128) {
+      int st = (int)(256 / tail);
+      if (st > 8) st = 8;
+      // every split at least two k-tiles, and none empty
+      while (st > 1 && ((nk_all + st - 1) / st < 2 || (nk_all + st - 1) / st * (st - 1) >= nk_all)) --st;
+      if (st > 1 && (double)tail * st * bm * bn <= (double)split_floats) {
+        const double bytes = 2.0 * (double)tail * st * (double)(bm * bn) * 4.0;
+        const double c = (double)(p.tiles / 256) * (double)nk_all * tk +
+                         (double)((nk_all + st - 1) / st) * tk + bytes / 4e12 + 4e-6;
+        if (c < p.cost) {
+          p.cost = c;
+          p.t_full = p.tiles - tail;
+          p.s_tail = st;
+        }
+      }
+    }
+    return p;
   };
-  auto cost = [&](int64_t bm, int64_t bn, double rate) {
-    return (double)((tiles_of(bm, bn) + 255) / 256) * (double)(bm * bn) / rate;
-  };
-  const double c0 = cost(256, 256, 1.0), c2 = cost(128, 128, 0.70);
-  const double c1 = g.sym ? 1e300 : cost(256, 192, 0.83);
-  if (c0 <= c1 && c0 <= c2) return launch_cfg<2, 4, 4, 2>(g, tiles_of(256, 256), s, nwg);
-  if (c1 <= c2) return launch_cfg<2, 2, 4, 3>(g, tiles_of(256, 192), s, nwg);
-  return launch_cfg<2, 2, 2, 2>(g, tiles_of(128, 128), s, nwg);
+  Plan best = plan(0, 256, 256, 1.0);
+  if (!g.sym) {
+    const Plan p1 = plan(1, 256, 192, 0.83);
+    if (p1.cost < best.cost) best = p1;
+  }
+  const Plan p2 = plan(2, 128, 128, 0.70);
+  if (p2.cost < best.cost) best = p2;
+  if (best.cfg == 0) return launch_cfg<2, 4, 4, 2>(g, best.tiles, best.t_full, best.s_tail, s, nwg);
+  if (best.cfg == 1) return launch_cfg<2, 2, 4, 3>(g, best.tiles, best.t_full, best.s_tail, s, nwg);
+  return launch_cfg<2, 2, 2, 2>(g, best.tiles, best.t_full, best.s_tail, s, nwg);
 }
 
 }  // namespace fs4
