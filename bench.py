@@ -243,7 +243,7 @@ def main():
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
            "config": {"workload": "3B-shape NVFP4 LoRA-SVD linear fwd+bwd: X 8192x3072 bf16, "
                                   "W 8192x3072 (rank-32 bf16 factors + NVFP4 residual), dY 8192x8192 bf16",
                       "tokens": M, "in_features": K, "out_features": N, "rank": r,
