@@ -342,25 +342,30 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
   hipStream_t s = as_stream(stream);
   NsWs w = carve_ns(ws, m, n, nullptr);
   const int64_t mn = m * n, mm = m * m;
-  // iterate k lives in trace_X[k] when tracing, else alternates between X_out
-  // and the workspace so that the last one lands in X_out
-  auto slot = [&](int k) -> float * {
-    if (trace_X) return trace_X + (int64_t)k * mn;
-    return ((steps - k) % 2 == 0) ? X_out : w.X;
-  };
+  // The iterate is kept transposed, XT = X^T [n][m].  Quantizing XT gives
+  // Q_col(X) as its row-wise view and Q_row(X) as its column-wise view (the
+  // same blocks and tensor scale as quantizing X), and the update is computed
+  // as X'^T = a X^T + Q_col(X)^T Q_row(B)^T: an n x m output whose tiles fill
+  // the chip better than the m x n one.  Iterate k lives in w.X or X_out,
+  // alternating so that the last one is in w.X; X_out and each trace_X[k]
+  // get it transposed back.
+  auto slot = [&](int k) -> float * { return ((steps - k) % 2 == 0) ? w.X : X_out; };
   float *cur = slot(0);
   // Each producer (normalisation, GEMM epilogue) leaves per-workgroup amax
   // partials of its output in w.amax, so each quantization is one encode
-  // pass; np = 0 means no partials (a plain copy), and the quantizer takes
-  // its own amax pass.
+  // pass.
   int np = 0;
-  if (normalize) FS4_TRY(launch_normalize(G, dt, mn, eps, cur, w.nws, s, w.amax, &np));
-  else FS4_TRY(launch_copy_f32(G, dt, mn, cur, s));
+  if (normalize) FS4_TRY(launch_normalize_t(G, dt, m, n, eps, cur, w.nws, s, w.amax, &np));
+  else FS4_TRY(launch_transpose_f32(G, dt, m, n, cur, s, w.amax, &np));
   auto quantize = [&](const float *x, int64_t rows, int64_t cols, const fs4_nvfp4 *rv,
                       const fs4_nvfp4 *cv) -> fs4_status {
     if (np > 0) return launch_quantize_encode(x, FS4_FP32, rows, cols, rv, cv, w.amax, np, s);
     return launch_quantize(x, FS4_FP32, rows, cols, rv, cv, w.qws, s);
   };
+  auto trace = [&](int k) -> fs4_status {
+    return trace_X ? launch_transpose_f32(slot(k), FS4_FP32, n, m, trace_X + (int64_t)k * mn, s) : FS4_OK;
+  };
+  FS4_TRY(trace(0));
   for (int k = 0; k < steps; ++k) {
     float *A = trace_A ? trace_A + (int64_t)k * mm : w.A;
     float *B = trace_B ? trace_B + (int64_t)k * mm : w.B;
@@ -368,19 +373,19 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
     // A = Q(X) Q(X)^T is computed (and stored) exactly symmetric, so its
     // column-wise quantization is its row-wise one bit for bit, and
     // A^2 = Q_row(A) Q_col(A)^T = Q(A) Q(A)^T is symmetric as well.
-    FS4_TRY(quantize(cur, m, n, &w.x_row, &w.x_col));
+    FS4_TRY(quantize(cur, n, m, &w.x_col, &w.x_row));
     FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s, w.amax, &np, true,
                            w.split, w.split_floats));
     FS4_TRY(quantize(A, m, m, &w.a_row, nullptr));
     FS4_TRY(launch_gemm_nt(w.a_row, w.a_row, c, A, b, B, LowRankEpilogue(), s, w.amax, &np, true, w.split,
                            w.split_floats));
     FS4_TRY(quantize(B, m, m, &w.b_row, nullptr));
-    FS4_TRY(launch_gemm_nt(w.b_row, w.x_col, 1.0f, cur, a, next, LowRankEpilogue(), s, w.amax, &np, false,
+    FS4_TRY(launch_gemm_nt(w.x_col, w.b_row, 1.0f, cur, a, next, LowRankEpilogue(), s, w.amax, &np, false,
                            w.split, w.split_floats));
     cur = next;
+    FS4_TRY(trace(k + 1));
   }
-  if (trace_X) FS4_TRY(launch_copy_f32(cur, FS4_FP32, mn, X_out, s));
-  return FS4_OK;
+  return launch_transpose_f32(cur, FS4_FP32, n, m, X_out, s);
 }
 
 size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r) {

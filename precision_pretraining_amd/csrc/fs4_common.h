@@ -158,12 +158,17 @@ fs4_status launch_colred(const uint16_t *A, const float *Bm, int64_t M, int64_t 
 fs4_status launch_transpose_rank(const uint16_t *U, int64_t N, int r, uint16_t *Ut, hipStream_t s);
 // Frobenius normalisation X = G / (||G||_F + eps), fp64 accumulation
 size_t normalize_ws_bytes();
-// X = G / (||G||_F + eps) in fp32; amax_parts (nullable) receives one max |X|
-// per workgroup, *nparts (nullable) their count (at most 2048).
-fs4_status launch_normalize(const void *G, fs4_dtype dt, int64_t n, float eps, float *X,
-                            void *ws, hipStream_t s, uint32_t *amax_parts = nullptr,
-                            int *nparts = nullptr);
+// XT = (G / (||G||_F + eps))^T in fp32, G [rows][cols] bf16 or fp32 and XT
+// [cols][rows] (rows and cols multiples of 16); amax_parts (nullable)
+// receives one max |XT| per workgroup, *nparts (nullable) their count (at
+// most kNormMaxParts; 0 without amax_parts).
+fs4_status launch_normalize_t(const void *G, fs4_dtype dt, int64_t rows, int64_t cols, float eps,
+                              float *XT, void *ws, hipStream_t s, uint32_t *amax_parts = nullptr,
+                              int *nparts = nullptr);
 constexpr int kNormMaxParts = 2048;
-fs4_status launch_copy_f32(const void *src, fs4_dtype dt, int64_t n, float *dst, hipStream_t s);
+// dst [cols][rows] = src [rows][cols] as fp32, the same shape rules and
+// partials as launch_normalize_t.
+fs4_status launch_transpose_f32(const void *src, fs4_dtype dt, int64_t rows, int64_t cols, float *dst,
+                                hipStream_t s, uint32_t *amax_parts = nullptr, int *nparts = nullptr);
 
 }  // namespace fs4

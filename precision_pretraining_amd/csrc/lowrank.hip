@@ -593,7 +593,7 @@ size_t small_gemm_partials_bytes(int64_t Na, int64_t Nb, int64_t Kc) {
 namespace {
 
 constexpr int kNormParts = 1024;
-constexpr int kNormBlocks = 2048;   // scale_kernel workgroups (and amax partials)
+constexpr int kNormBlocks = 2048;   // transpose_scale_kernel workgroups (and amax partials)
 
 // Eight consecutive elements (one 16-byte word of bf16, two of fp32) as double.
 template <bool BF16>
@@ -634,62 +634,68 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const void *__restrict__ x, 
   if (threadIdx.x == 0) parts[blockIdx.x] = red[0];
 }
 
-// out = x / (||x||_F + eps) as fp32: the fp64 reciprocal of the fp64 norm
-// times each element in fp64, rounded once to fp32.
-template <bool BF16>
-__global__ __launch_bounds__(256) void scale_kernel(const void *__restrict__ x, int64_t nv,
-                                                    const double *__restrict__ parts, int nparts,
-                                                    double eps, float *__restrict__ out,
-                                                    uint32_t *__restrict__ amax_parts) {
-  // every block reduces the partial sums the same way (fixed order): a
-  // strided sum per thread, then a tree over the block
-  __shared__ double red[256];
-  double s = 0.0;
-  for (int p = threadIdx.x; p < nparts; p += 256) s += parts[p];
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  const double inv = 1.0 / (__builtin_sqrt(red[0]) + eps);
-  float am = 0.0f;
-  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += (int64_t)gridDim.x * 256) {
-    double o[8];
-    load8d<BF16>(x, v, o);
-    float f[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      f[q] = (float)(o[q] * inv);
-      am = fmaxf(am, fabsf(f[q]));
-    }
-    float4 *d = (float4 *)out + 2 * v;
-    d[0] = make_float4(f[0], f[1], f[2], f[3]);
-    d[1] = make_float4(f[4], f[5], f[6], f[7]);
-  }
-  if (amax_parts) {
-    // block max of the written values, for the quantizer that follows
-    // (non-negative floats order as their bit patterns)
-    __shared__ uint32_t bm[256];
-    bm[threadIdx.x] = __builtin_bit_cast(uint32_t, am);
+// out[c][r] = sc * x[r][c] as fp32 (x bf16 or fp32, rows and cols multiples
+// of 16), 64 x 64 tiles through LDS.  NORM: sc = 1 / (||x||_F + eps), every
+// workgroup reducing the fp64 partial sums in the same fixed order; each
+// element is x * sc in fp64, rounded once to fp32.  Otherwise sc = 1.  With
+// amax_parts, each workgroup writes the max |out| of what it wrote.
+template <bool BF16, bool NORM>
+__global__ __launch_bounds__(256) void transpose_scale_kernel(const void *__restrict__ x, int64_t rows,
+                                                              int64_t cols, const double *__restrict__ parts,
+                                                              int nparts, double eps, float *__restrict__ out,
+                                                              uint32_t *__restrict__ amax_parts) {
+  __shared__ float tile[64][65];
+  double inv = 1.0;
+  if constexpr (NORM) {
+    __shared__ double red[256];
+    double sum = 0.0;
+    for (int p = threadIdx.x; p < nparts; p += 256) sum += parts[p];
+    red[threadIdx.x] = sum;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
-      if (threadIdx.x < w) bm[threadIdx.x] = bm[threadIdx.x] > bm[threadIdx.x + w] ? bm[threadIdx.x] : bm[threadIdx.x + w];
+      if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
       __syncthreads();
     }
-    if (threadIdx.x == 0) amax_parts[blockIdx.x] = bm[0];
+    inv = 1.0 / (__builtin_sqrt(red[0]) + eps);
   }
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(256) void copy_kernel(const void *__restrict__ x, int64_t nv,
-                                                   float *__restrict__ out) {
-  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += (int64_t)gridDim.x * 256) {
-    double o[8];
-    load8d<BF16>(x, v, o);
-    float4 *d = (float4 *)out + 2 * v;
-    d[0] = make_float4((float)o[0], (float)o[1], (float)o[2], (float)o[3]);
-    d[1] = make_float4((float)o[4], (float)o[5], (float)o[6], (float)o[7]);
+  const int t = threadIdx.x;
+  const int64_t tcols = (cols + 63) / 64, ntiles = ((rows + 63) / 64) * tcols;
+  float am = 0.0f;
+  for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const int64_t r0 = tile_id / tcols * 64, c0 = tile_id % tcols * 64;
+    // 8-element words: row t/8 (+32), columns 8 (t%8) .. +7
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int rr = t / 8 + 32 * p, cc = 8 * (t % 8);
+      const int64_t r = r0 + rr, c = c0 + cc;
+      double o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (r < rows && c < cols) load8d<BF16>(x, (r * cols + c) / 8, o);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) tile[rr][cc + q] = NORM ? (float)(o[q] * inv) : (float)o[q];
+    }
+    __syncthreads();
+    // output row c0 + t/16 (+16, +32, +48), its columns r0 + 4 (t%16) .. +3
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int oc = t / 16 + 16 * p, q4 = 4 * (t % 16);
+      const int64_t c = c0 + oc, r = r0 + q4;
+      if (c < cols && r < rows) {
+        const float4 v = make_float4(tile[q4][oc], tile[q4 + 1][oc], tile[q4 + 2][oc], tile[q4 + 3][oc]);
+        *(float4 *)(out + c * rows + r) = v;
+        am = fmaxf(am, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      }
+    }
+    __syncthreads();          // the tile is rewritten by the next iteration
+  }
+  if (amax_parts) {
+    __shared__ uint32_t bm[256];
+    bm[t] = __builtin_bit_cast(uint32_t, am);
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (t < w) bm[t] = bm[t] > bm[t + w] ? bm[t] : bm[t + w];
+      __syncthreads();
+    }
+    if (t == 0) amax_parts[blockIdx.x] = bm[0];
   }
 }
 
@@ -697,32 +703,43 @@ __global__ __launch_bounds__(256) void copy_kernel(const void *__restrict__ x, i
 
 size_t normalize_ws_bytes() { return kNormParts * sizeof(double); }
 
-fs4_status launch_normalize(const void *G, fs4_dtype dt, int64_t n, float eps, float *X, void *ws,
-                            hipStream_t s, uint32_t *amax_parts, int *nparts) {
-  // n is a multiple of 16 (both dimensions are); 8-element words
+namespace {
+unsigned transpose_grid(int64_t rows, int64_t cols) {
+  const int64_t tiles = ((rows + 63) / 64) * ((cols + 63) / 64);
+  return (unsigned)(tiles < kNormBlocks ? tiles : kNormBlocks);
+}
+}  // namespace
+
+fs4_status launch_normalize_t(const void *G, fs4_dtype dt, int64_t rows, int64_t cols, float eps,
+                              float *XT, void *ws, hipStream_t s, uint32_t *amax_parts, int *nparts) {
   double *parts = (double *)ws;
-  const int64_t nv = n / 8;
+  const int64_t nv = rows * cols / 8;
   int64_t g = (nv + 256 * 4 - 1) / (256 * 4);
   const int np = (int)(g < 1 ? 1 : (g > kNormParts ? kNormParts : g));
-  const unsigned gs = (unsigned)((nv + 255) / 256 < kNormBlocks ? (nv + 255) / 256 : kNormBlocks);
-  if (nparts) *nparts = (int)gs;
+  const unsigned gs = transpose_grid(rows, cols);
+  if (nparts) *nparts = amax_parts ? (int)gs : 0;
+  if (rows == 0 || cols == 0) return FS4_OK;
   if (dt == FS4_BF16) {
     sumsq_kernel<true><<<np, 256, 0, s>>>(G, nv, parts);
-    scale_kernel<true><<<gs, 256, 0, s>>>(G, nv, parts, np, (double)eps, X, amax_parts);
+    transpose_scale_kernel<true, true><<<gs, 256, 0, s>>>(G, rows, cols, parts, np, (double)eps, XT, amax_parts);
   } else {
     sumsq_kernel<false><<<np, 256, 0, s>>>(G, nv, parts);
-    scale_kernel<false><<<gs, 256, 0, s>>>(G, nv, parts, np, (double)eps, X, amax_parts);
+    transpose_scale_kernel<false, true><<<gs, 256, 0, s>>>(G, rows, cols, parts, np, (double)eps, XT, amax_parts);
   }
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 
-fs4_status launch_copy_f32(const void *src, fs4_dtype dt, int64_t n, float *dst, hipStream_t s) {
-  const int64_t nv = n / 8;
-  const unsigned gs = (unsigned)((nv + 255) / 256 < 4096 ? (nv + 255) / 256 : 4096);
-  if (n == 0) return FS4_OK;
-  if (dt == FS4_BF16) copy_kernel<true><<<gs, 256, 0, s>>>(src, nv, dst);
-  else copy_kernel<false><<<gs, 256, 0, s>>>(src, nv, dst);
+fs4_status launch_transpose_f32(const void *src, fs4_dtype dt, int64_t rows, int64_t cols, float *dst,
+                                hipStream_t s, uint32_t *amax_parts, int *nparts) {
+  const unsigned gs = transpose_grid(rows, cols);
+  if (nparts) *nparts = amax_parts ? (int)gs : 0;
+  if (rows == 0 || cols == 0) return FS4_OK;
+  if (dt == FS4_BF16)
+    transpose_scale_kernel<true, false><<<gs, 256, 0, s>>>(src, rows, cols, nullptr, 0, 0.0, dst, amax_parts);
+  else
+    transpose_scale_kernel<false, false><<<gs, 256, 0, s>>>(src, rows, cols, nullptr, 0, 0.0, dst, amax_parts);
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
+
 
 }  // namespace fs4
