@@ -671,22 +671,21 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
         const int nrec = (int)((g.M * g.N - base) * 4 < 0x7FFFFFFF ? (g.M * g.N - base) * 4 : 0x7FFFFFFF);
         const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(g.C + base, 0, nrec, kBufferWord3);
         const int loff = (4 * h * (int)g.N + wn * TN * 32 + j * 32 + l32) * 4;
-        if (g.E) {
-          // all 16 loads of E before the first store of C (which the loads
-          // may not pass), so that they are in flight together
-          const __amdgpu_buffer_rsrc_t re =
-              __builtin_amdgcn_make_buffer_rsrc((float *)g.E + base, 0, nrec, kBufferWord3);
-          float ev[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            ev[e] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(re, loff, (8 * (e >> 2) + (e & 3)) * (int)g.N * 4, 0));
-#pragma unroll
-          for (int e = 0; e < 16; ++e) t[e] += g.beta_e * ev[e];
-        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int soff = (8 * (e >> 2) + (e & 3)) * (int)g.N * 4;
+          if (g.E && (e & 3) == 0) {
+            // E for four rows at once, before their stores of C (which the
+            // loads may not pass): four loads in flight, not one
+            const __amdgpu_buffer_rsrc_t re =
+                __builtin_amdgcn_make_buffer_rsrc((float *)g.E + base, 0, nrec, kBufferWord3);
+            float ev[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              ev[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, loff, soff + c * (int)g.N * 4, 0));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t[e + c] += g.beta_e * ev[c];
+          }
           const float v = t[e];
           if (g.amax_parts) amax = fmaxf(amax, fabsf(v));
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, loff, soff, 0);

@@ -21,14 +21,25 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-3
 
 
-def test_normalization():
+@pytest.mark.parametrize("m,n", [(192, 512), (80, 208)])
+def test_normalization(m, n):
     fs4 = need_gpu()
-    print_case(test="ns_normalize")
-    g = synth.ns_input(seed=5, m=192, n=512)
+    print_case(test="ns_normalize", m=m, n=n)
+    g = synth.ns_input(seed=5, m=m, n=n)
     X = fs4.newton_schulz(dev_bf16(g), steps=0).cpu().numpy()
     _, ref = oracle.ns_normalize(f32(g))
     # one fp32 rounding of an fp64 value on each side
     assert np.max(np.abs(X - ref) / np.maximum(np.abs(ref), 1e-30)) <= 2.0 ** -23
+
+
+def test_zero_steps_without_normalization_is_a_copy():
+    """steps=0, normalize=0 returns G as fp32 exactly (the iterate is held
+    transposed inside; 80 x 208 leaves partial 64 x 64 tiles)."""
+    fs4 = need_gpu()
+    print_case(test="ns_copy", m=80, n=208)
+    g = synth.ns_input(seed=6, m=80, n=208)
+    X = fs4.newton_schulz(dev_bf16(g), steps=0, normalize=False).cpu().numpy()
+    assert np.array_equal(X, f32(g))
 
 
 @pytest.mark.parametrize("m,n", [(192, 512), (768, 2048)])
