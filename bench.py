@@ -30,7 +30,9 @@ The GEMM's HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
 counter runs of ``--only gemm``, scaled by what the same counters read for a
 plain device copy of known size (``--only copy``); the summary under
 profiles/ records the SHA-256 of the GEMM source it was taken on, and the
-figure is reported only while the source is unchanged (null otherwise).
+figure is reported only while the source is unchanged (null otherwise).  The
+same holds for ``mfma_util_pct``: the percent of cycles the MFMA pipes are
+busy in the GEMM, from a rocprofv3 counter run of ``--only gemm``.
 """
 from __future__ import annotations
 
@@ -83,23 +85,35 @@ def parse():
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nt_traffic_3b.md")
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "gemm_nt_mfma_util_3b.md")
 GEMM_SOURCE = os.path.join(ROOT, "precision_pretraining_amd", "csrc", "gemm.hip")
 
 
-def gemm_traffic():
-    """HBM bytes per GEMM launch (average over the three step shapes) from the
-    committed counter summary, or None when it is missing or was taken on
-    another version of the GEMM source."""
+def _counter_figure(path, pattern):
+    """A figure from a committed counter summary, or None when the summary is
+    missing or was taken on another version of the GEMM source."""
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(path).read()
         digest = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
     m = re.search(r"source sha256: ([0-9a-f]{64})", text)
-    t = re.search(r"bytes per launch \(scaled\): ([0-9.]+)", text)
+    t = re.search(pattern, text)
     if not m or not t or m.group(1) != digest:
         return None
     return float(t.group(1))
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch (average over the three step shapes)."""
+    return _counter_figure(TRAFFIC_SUMMARY, r"bytes per launch \(scaled\): ([0-9.]+)")
+
+
+def gemm_mfma_util():
+    """Percent of cycles the MFMA pipes are busy in the GEMM (rocprofv3
+    SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per SIMD), at the clock the
+    part sustains."""
+    return _counter_figure(MFMA_SUMMARY, r"MFMA busy percent \(timed dispatches\): ([0-9.]+)")
 
 
 def cpu_baseline():
@@ -192,7 +206,7 @@ def main():
         ach = gemm_flop / (gemm_ms * 1e-3) / 1e12
         return {"bound": "mfma", "kernel": "gemm_nt_kernel (block-scaled NVFP4 NT GEMM)",
                 "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": gemm_traffic(),
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": gemm_traffic(), "mfma_util_pct": gemm_mfma_util(),
                 "per_launch": "8192x8192x3072 = %.1f GFLOP" % (gemm_flop / 1e9),
                 "avg_launch_ms": round(gemm_ms, 4)}
 
