@@ -156,7 +156,9 @@ fs4_status fs4_linear_bwd(const void *dY, int64_t M, int64_t N, int64_t K,
  *   X_out   fp32 [m][n]: X_steps
  *   trace_X fp32 [steps+1][m][n]: X_0..X_steps, nullable
  *   trace_A, trace_B fp32 [steps][m][m]: each step's A and B, nullable
- * The Frobenius norm is accumulated in fp64.  steps >= 0.
+ * The Frobenius norm is accumulated in fp64.  steps >= 0.  X_out holds
+ * intermediate iterates during the call, so it may not overlap G or a trace
+ * buffer (FS4_ERR_ARG).
  */
 size_t fs4_newton_schulz_workspace_bytes(int64_t m, int64_t n);
 fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, int steps,

@@ -338,6 +338,20 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
   size_t need = 0;
   carve_ns(nullptr, m, n, &need);
   FS4_TRY(check_ws(ws, ws_bytes, need));
+  // X_out holds iterates during the call: it may overlap neither G nor a
+  // trace buffer
+  {
+    const size_t xb = (size_t)(m * n) * sizeof(float), gb = (size_t)(m * n) * (dt == FS4_BF16 ? 2 : 4);
+    auto overlap = [](const void *p, size_t pb, const void *q, size_t qb) {
+      const uintptr_t a0 = (uintptr_t)p, b0 = (uintptr_t)q;
+      return p && q && a0 < b0 + qb && b0 < a0 + pb;
+    };
+    if (overlap(X_out, xb, G, gb) ||
+        overlap(X_out, xb, trace_X, (size_t)(steps + 1) * xb) ||
+        overlap(X_out, xb, trace_A, (size_t)steps * (size_t)(m * m) * sizeof(float)) ||
+        overlap(X_out, xb, trace_B, (size_t)steps * (size_t)(m * m) * sizeof(float)))
+      return FS4_ERR_ARG;
+  }
 
   hipStream_t s = as_stream(stream);
   NsWs w = carve_ns(ws, m, n, nullptr);

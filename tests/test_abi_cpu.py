@@ -125,8 +125,8 @@ def test_linear_bwd_validation():
     assert bwd(wsb=1) == WORKSPACE
 
 
-def ns(G=A16, dt=0, m=64, n=128, steps=5, X=A16, wsb=1 << 30):
-    return lib.fs4_newton_schulz(G, dt, m, n, steps, 3.4445, -4.775, 2.0315, 1, 1e-7, X, None, None, None,
+def ns(G=A16, dt=0, m=64, n=128, steps=5, X=A16 * 4, wsb=1 << 30, tX=None):
+    return lib.fs4_newton_schulz(G, dt, m, n, steps, 3.4445, -4.775, 2.0315, 1, 1e-7, X, tX, None, None,
                                  A16 * 16, wsb, None)
 
 
@@ -138,6 +138,9 @@ def test_newton_schulz_validation():
     assert ns(G=None) == NULL
     assert ns(X=A16 + 2) == ALIGN
     assert ns(wsb=1024) == WORKSPACE
+    assert ns(X=A16) == ARG                                # X_out overlapping G (bf16 64 x 128)
+    assert ns(X=A16 + 64 * 128 * 2 - 16) == ARG
+    assert ns(X=A16 * 4 + 64 * 128 * 4 * 3, tX=A16 * 4) == ARG   # X_out inside trace_X
 
 
 def test_workspace_sizes_grow_with_shape():
