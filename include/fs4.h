@@ -33,6 +33,9 @@
  *     matching fs4_*_workspace_bytes() call returns (256-byte aligned).
  *   - Calls are reentrant; calls that share a workspace or an output buffer
  *     must be ordered on one stream.
+ *   - Output buffers may overlap neither the inputs, nor each other, nor the
+ *     workspace (fs4_newton_schulz checks its iterate buffer; the other calls
+ *     do not check).
  */
 #ifndef FS4_H
 #define FS4_H
