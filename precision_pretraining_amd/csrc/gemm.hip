@@ -195,10 +195,10 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   constexpr int A_BYTES = BM * kLdsStride, B_BYTES = BN * kLdsStride;
   constexpr int STAGE = A_BYTES + B_BYTES + BM * 8 + BN * 8;
   // KFAST stages are filled by direct global->LDS loads: unpadded 64-byte code
-  // rows (16-byte slots XOR-swizzled by row), then 8 scale bytes per row; three
+  // rows (16-byte slots XOR-swizzled by row), then 8 scale bytes per row; four
   // stages, plus 1 KB that idle load instructions write to
   constexpr int STAGE_D = (BM + BN) * (kRowBytes + 8);
-  constexpr int MAIN_BYTES = KFAST ? 3 * STAGE_D + 1024 : 2 * STAGE;
+  constexpr int MAIN_BYTES = KFAST ? 4 * STAGE_D + 1024 : 2 * STAGE;
   constexpr int LR_BYTES = (2 * BM + BN) * kLrStrideMax * 2;   // rank-r staging in the epilogue
   constexpr int LDS_BYTES = MAIN_BYTES > LR_BYTES ? MAIN_BYTES : LR_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
@@ -429,8 +429,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   };
 
   if constexpr (KFAST) {
-    // Three-stage pipeline of direct global->LDS loads (no staging registers).
-    // Tile kt+2's loads are issued as tile kt starts, into the stage of tile
+    // Four-stage pipeline of direct global->LDS loads (no staging registers).
+    // Tile kt+3's loads are issued as tile kt starts, into the stage of tile
     // kt-1.  One barrier per tile, in its middle: before it each wave has
     // issued its last read of tile kt and waited for its own loads of tile
     // kt+1; after it tile kt+1 is visible to all and tile kt's stage may be
@@ -438,14 +438,15 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
     // can already read and expand tile kt+1.
     // Every wave issues the same number of 64-lane load instructions per tile
     // (idle ones write the spare 1 KB), so "tile kt+1 has landed" is exactly
-    // "at most DMA_PER_TILE loads outstanding".  Rows past M or N load a
-    // clamped row: they only feed outputs that are never stored.
+    // "at most DMA_PER_TILE loads outstanding per tile issued after it".  Rows
+    // past M or N load a clamped row: they only feed outputs that are never
+    // stored.
     constexpr int NW = NT / 64;
     constexpr int CODE_Q = (BM + BN) * 4, SC_U = (BM + BN) * 2;
     static_assert(CODE_Q % 64 == 0 && SC_U % 64 == 0, "load instructions must be all-real or all-idle");
     constexpr int CODE_I = (CODE_Q + 64 * NW - 1) / (64 * NW), SC_I = (SC_U + 64 * NW - 1) / (64 * NW);
     constexpr int DMA_PER_TILE = CODE_I + SC_I;
-    static_assert(DMA_PER_TILE < 64, "vmcnt range");
+    static_assert(2 * DMA_PER_TILE < 64, "vmcnt range");
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;     // LDS byte address of the stages
     // Per load instruction: whether it fills A or B (uniform: the A part is a
     // whole number of instructions) and this lane's byte offset from the
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
       }
     }
     auto issue_tile = [&](int kt, int st) {
-      const uint32_t sbase = lds0 + (uint32_t)(st * STAGE_D), spare = lds0 + 3u * STAGE_D;
+      const uint32_t sbase = lds0 + (uint32_t)(st * STAGE_D), spare = lds0 + 4u * STAGE_D;
       const int64_t kbyte0 = (int64_t)(kt0 + kt) * kRowBytes, ksc0 = (int64_t)(kt0 + kt) * 8;
 #pragma unroll
       for (int j = 0; j < CODE_I; ++j) {
@@ -502,21 +503,19 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
       return Stage{base, base + BM * kRowBytes, base + (BM + BN) * kRowBytes, base + (BM + BN) * kRowBytes + BM * 8};
     };
     issue_tile(0, 0);
-    if (nk > 1) {
-      issue_tile(1, 1);
-      wait_vmcnt<DMA_PER_TILE>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    if (nk > 1) issue_tile(1, 1);
+    if (nk > 2) issue_tile(2, 2);
+    if (nk > 2) wait_vmcnt<2 * DMA_PER_TILE>();
+    else if (nk > 1) wait_vmcnt<DMA_PER_TILE>();
+    else wait_vmcnt<0>();
     __syncthreads();
     begin_tile(stage(0));
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 2 < nk) issue_tile(kt + 2, (kt + 2) % 3);
-      const bool more = kt + 2 < nk;
-      // after the last tile the "next" stage is the current one again (a
-      // harmless re-read; nothing refills it any more)
-      run_tile(stage(kt % 3), stage(kt + 1 < nk ? (kt + 1) % 3 : kt % 3), std::true_type{}, [&] {
-        if (more) wait_vmcnt<DMA_PER_TILE>();     // tile kt+1 has landed
+      if (kt + 3 < nk) issue_tile(kt + 3, (kt + 3) % 4);
+      const int ahead = (kt + 2 < nk) + (kt + 3 < nk);   // tiles issued after kt+1
+      run_tile(stage(kt % 4), stage(kt + 1 < nk ? (kt + 1) % 4 : kt % 4), std::true_type{}, [&] {
+        if (ahead == 2) wait_vmcnt<2 * DMA_PER_TILE>();     // tile kt+1 has landed
+        else if (ahead == 1) wait_vmcnt<DMA_PER_TILE>();
         else wait_vmcnt<0>();
         __syncthreads();
       });
