@@ -147,7 +147,7 @@ def cpu_baseline():
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU; this build has no multi-GPU path (--gpus %d requested)" % a.gpus,
+        print("bench.py measures one GPU; the library has no multi-GPU path (--gpus %d requested)" % a.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch
