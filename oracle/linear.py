@@ -15,8 +15,8 @@ activations X [M, K]:
 Every quantized product is quantized along its own contraction dimension.
 Readings: beta = 1 unless given; the low-rank term uses the unquantized BF16
 X; dW is the gradient of the full weight, i.e. the update of the residual;
-the pages' Cholesky-QR constraint on the low-rank update is not applied (no
-formula is printed).
+dU and dV here are the plain chain-rule gradients (the pages' Cholesky-QR
+constraint on them is a separate step, oracle.lora.subspace_project).
 
 GEMMs are float64 BLAS over the exactly dequantized operands; the result is
 rounded to float32 only where the method stores float32.
