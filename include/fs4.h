@@ -169,15 +169,39 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
                              float *X_out, float *trace_X, float *trace_A, float *trace_B,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * fs4_lora_project — subspace-constrained gradients of the rank-r branch,
+ * [FS4 §2.1] (backward pass: a Cholesky-QR constraint keeps the update of the
+ * BF16 branch L2 L1 = U V inside its principal subspace).  With
+ * Q_U = CholQR(U) and Q_V = CholQR(V^T), where CholQR(A) = A L^-T for the
+ * Cholesky factor L L^T = A^T A:
+ *     dU <- Q_U Q_U^T dU          (columns projected onto span(U))
+ *     dV <- dV Q_V Q_V^T          (rows projected onto the row space of V)
+ * computed in fp64 as U (U^T U)^-1 (U^T dU) and (dV V^T)(V V^T)^-1 V, then
+ * rounded to fp32 once.
+ *   U  bf16 [N][r], V bf16 [r][K]      the branch's factors
+ *   dU fp32 [N][r], dV fp32 [r][K]     their gradients (fs4_linear_bwd's dU
+ *       and dV), overwritten in place; either may be NULL to skip that side
+ * 0 <= r <= 64 (FS4_ERR_RANK), N >= 0, K >= 0 (FS4_ERR_SHAPE); r = 0 does
+ * nothing.  U needs full column rank and V full row rank: where the fp64
+ * Cholesky of U^T U (or V V^T) breaks down (a pivot at or below 2^-46 of its
+ * diagonal entry), that side's output is all NaN.
+ * The residual's gradient (dW of fs4_linear_bwd) is left as it is.
+ */
+size_t fs4_lora_project_workspace_bytes(int64_t N, int64_t K, int r);
+fs4_status fs4_lora_project(const void *U, const void *V, int64_t N, int64_t K, int r,
+                            float *dU, float *dV, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace size for any of the calls above, dispatched on the operation:
  *   FS4_OP_QUANTIZE   d0 = rows, d1 = cols
  *   FS4_OP_GEMM       d0 = M, d1 = N, d2 = K
  *   FS4_OP_LINEAR_FWD d0 = M, d1 = K, d2 = N, r
  *   FS4_OP_LINEAR_BWD d0 = M, d1 = N, d2 = K, r
  *   FS4_OP_NS         d0 = m, d1 = n
+ *   FS4_OP_LORA_PROJECT d0 = N, d1 = K, r
  * Returns 0 for an unknown op. */
 typedef enum { FS4_OP_QUANTIZE = 0, FS4_OP_GEMM = 1, FS4_OP_LINEAR_FWD = 2,
-               FS4_OP_LINEAR_BWD = 3, FS4_OP_NS = 4 } fs4_op;
+               FS4_OP_LINEAR_BWD = 3, FS4_OP_NS = 4, FS4_OP_LORA_PROJECT = 5 } fs4_op;
 size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r);
 
 /* Human-readable name of a status code (static storage). */

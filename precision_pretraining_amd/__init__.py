@@ -3,7 +3,7 @@ library of Full-Stack FP4.
 
 Argument marshalling only: every step of the path runs in the HIP kernels of
 libfs4.so.  PyTorch provides device memory and the current stream.  The
-library must have been built (``python -m precision_pretraining_amd.build``);
+library must have been built (``python precision_pretraining_amd/build.py``);
 importing this package without it raises ImportError.
 
 Names follow the C ABI in include/fs4.h:
@@ -13,6 +13,7 @@ Names follow the C ABI in include/fs4.h:
     linear_fwd(X, R_row, U, V, beta)          -> LinearFwd(Y, T, X_col)
     linear_bwd(dY, X, X_col, R_col, U, V, T)  -> LinearBwd(dX, dW, dU, dV)
     newton_schulz(G, steps, abc, ...)         -> X (and traces)
+    lora_project(U, V, dU, dV)                -> (dU, dV) projected in place
 """
 from __future__ import annotations
 
@@ -27,19 +28,20 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfs4.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libfs4.so is not built; run `python -m precision_pretraining_amd.build` "
+    raise ImportError("libfs4.so is not built; run `python precision_pretraining_amd/build.py` "
                       "(expected at %s)" % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)
 
 FS4_BF16, FS4_FP32 = 0, 1
-FS4_OP_QUANTIZE, FS4_OP_GEMM, FS4_OP_LINEAR_FWD, FS4_OP_LINEAR_BWD, FS4_OP_NS = range(5)
+FS4_OP_QUANTIZE, FS4_OP_GEMM, FS4_OP_LINEAR_FWD, FS4_OP_LINEAR_BWD, FS4_OP_NS, FS4_OP_LORA_PROJECT = range(6)
 MUON_ABC = (3.4445, -4.7750, 2.0315)
 
 EXPORTS = [
     "fs4_quantize_workspace_bytes", "fs4_quantize", "fs4_gemm_workspace_bytes", "fs4_gemm_nt",
     "fs4_linear_fwd_workspace_bytes", "fs4_linear_fwd", "fs4_linear_bwd_workspace_bytes",
     "fs4_linear_bwd", "fs4_newton_schulz_workspace_bytes", "fs4_newton_schulz",
+    "fs4_lora_project_workspace_bytes", "fs4_lora_project",
     "fs4_workspace_bytes", "fs4_status_str", "fs4_version",
 ]
 
@@ -57,7 +59,11 @@ _VP = ctypes.POINTER(_View)
 
 
 def _sig(name, res, args):
-    f = getattr(_lib, name)
+    try:
+        f = getattr(_lib, name)
+    except AttributeError as e:
+        raise ImportError("%s does not export %s: the library is older than this binding; rebuild it "
+                          "with `python precision_pretraining_amd/build.py`" % (LIB_PATH, name)) from e
     f.restype = res
     f.argtypes = args
     return f
@@ -77,6 +83,8 @@ _sig("fs4_linear_bwd_workspace_bytes", _SZ, [_I64, _I64, _I64, ctypes.c_int])
 _sig("fs4_linear_bwd", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _VP, _VP, _P, _P, ctypes.c_int, _F,
                                       _P, _P, _P, _P, _P, _P, _SZ, _P])
 _sig("fs4_newton_schulz_workspace_bytes", _SZ, [_I64, _I64])
+_sig("fs4_lora_project_workspace_bytes", _SZ, [_I64, _I64, ctypes.c_int])
+_sig("fs4_lora_project", ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P, _SZ, _P])
 _sig("fs4_newton_schulz", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_int, _F, _F, _F,
                                          ctypes.c_int, _F, _P, _P, _P, _P, _P, _SZ, _P])
 
@@ -268,10 +276,26 @@ def newton_schulz(G: torch.Tensor, steps: int = 5, abc=MUON_ABC, normalize: bool
     return X
 
 
+def lora_project(U: torch.Tensor, V: torch.Tensor, dU: Optional[torch.Tensor] = None,
+                 dV: Optional[torch.Tensor] = None):
+    """Projects the rank-r gradients in place onto the branch's subspace:
+    dU <- Q_U Q_U^T dU, dV <- dV Q_V Q_V^T (Q_U = CholQR(U), Q_V = CholQR(V^T)).
+    U bf16 [N, r], V bf16 [r, K]; dU fp32 [N, r], dV fp32 [r, K] (either may
+    be None).  Returns (dU, dV)."""
+    N, r = U.shape
+    K = V.shape[1]
+    dev = U.device
+    nbytes = _lib.fs4_lora_project_workspace_bytes(N, K, r)
+    ws = _workspace(nbytes, dev)
+    _check(_lib.fs4_lora_project(U.data_ptr(), V.data_ptr(), N, K, r, _ptr(dU), _ptr(dV), ws.data_ptr(),
+                                 ws.numel(), _stream(dev)), "fs4_lora_project")
+    return dU, dV
+
+
 def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> int:
     return _lib.fs4_workspace_bytes(op, d0, d1, d2, r)
 
 
 __all__ = ["NVFP4", "quantize", "gemm_nt", "linear_fwd", "LinearFwd", "linear_bwd", "LinearBwd",
-           "newton_schulz", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
+           "newton_schulz", "lora_project", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
            "EXPORTS", "MUON_ABC"]

@@ -1,6 +1,9 @@
 """Builds libfs4.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m precision_pretraining_amd.build [--verbose] [--resource-usage]
+    python precision_pretraining_amd/build.py [--verbose] [--resource-usage]
+
+Run it as a script (not with -m): importing the package would first bind the
+library that is being rebuilt.
 
 Objects go to _build/ at the repository root; the shared library is written
 next to this file so that the Python binding finds it.
@@ -30,7 +33,7 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + I
                 "-Wall", "-Wno-unused-function"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-Wall"]
 
-SOURCES = ["quantize.hip", "gemm.hip", "lowrank.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "lowrank.hip", "subspace.hip", "abi.cpp"]
 
 
 def _run(cmd, verbose):

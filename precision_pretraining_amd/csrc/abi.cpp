@@ -402,6 +402,31 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
   return launch_transpose_f32(cur, FS4_FP32, n, m, X_out, s);
 }
 
+size_t fs4_lora_project_workspace_bytes(int64_t N, int64_t K, int r) {
+  if (N < 0 || K < 0 || r < 0 || r > kMaxRank) return 0;
+  return lora_project_ws_bytes(N, K, r);
+}
+
+fs4_status fs4_lora_project(const void *U, const void *V, int64_t N, int64_t K, int r, float *dU,
+                            float *dV, void *ws, size_t ws_bytes, void *stream) {
+  if (r < 0 || r > kMaxRank) return FS4_ERR_RANK;
+  if (N < 0 || K < 0) return FS4_ERR_SHAPE;
+  if (r == 0) return FS4_OK;
+  const bool do_u = dU && N > 0, do_v = dV && K > 0;
+  if (do_u) {
+    FS4_TRY(check_ptr(dU));
+    FS4_TRY(check_ptr(U));
+  }
+  if (do_v) {
+    FS4_TRY(check_ptr(dV));
+    FS4_TRY(check_ptr(V));
+  }
+  if (!do_u && !do_v) return FS4_OK;
+  FS4_TRY(check_ws(ws, ws_bytes, lora_project_ws_bytes(N, K, r)));
+  return launch_lora_project((const uint16_t *)U, (const uint16_t *)V, N, K, r, do_u ? dU : nullptr,
+                             do_v ? dV : nullptr, ws, as_stream(stream));
+}
+
 size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r) {
   switch (op) {
     case FS4_OP_QUANTIZE: return fs4_quantize_workspace_bytes(d0, d1);
@@ -409,6 +434,7 @@ size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r)
     case FS4_OP_LINEAR_FWD: return fs4_linear_fwd_workspace_bytes(d0, d1, d2, r);
     case FS4_OP_LINEAR_BWD: return fs4_linear_bwd_workspace_bytes(d0, d1, d2, r);
     case FS4_OP_NS: return fs4_newton_schulz_workspace_bytes(d0, d1);
+    case FS4_OP_LORA_PROJECT: return fs4_lora_project_workspace_bytes(d0, d1, r);
   }
   return 0;
 }

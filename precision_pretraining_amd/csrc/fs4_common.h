@@ -171,4 +171,11 @@ constexpr int kNormMaxParts = 2048;
 fs4_status launch_transpose_f32(const void *src, fs4_dtype dt, int64_t rows, int64_t cols, float *dst,
                                 hipStream_t s, uint32_t *amax_parts = nullptr, int *nparts = nullptr);
 
+// Subspace projection of the rank-r gradients (dU, dV in place; either
+// nullable), fp64 Gram matrices, Cholesky and solves; `ws` needs
+// lora_project_ws_bytes(N, K, r).
+size_t lora_project_ws_bytes(int64_t N, int64_t K, int r);
+fs4_status launch_lora_project(const uint16_t *U, const uint16_t *V, int64_t N, int64_t K, int r,
+                               float *dU, float *dV, void *ws, hipStream_t s);
+
 }  // namespace fs4

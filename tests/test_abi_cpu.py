@@ -149,3 +149,31 @@ def test_workspace_sizes_grow_with_shape():
     assert big > small > 0
     assert lib.fs4_newton_schulz_workspace_bytes(3072, 8192) > 3072 * 8192 * 4
     assert lib.fs4_workspace_bytes(99, 1, 1, 1, 0) == 0
+
+
+def lp(U=A16, V=A16 * 2, N=64, K=48, r=8, dU=A16 * 4, dV=A16 * 8, wsb=1 << 20):
+    return lib.fs4_lora_project(U, V, N, K, r, dU, dV, A16 * 16, wsb, None)
+
+
+def test_lora_project_validation():
+    assert lp(r=65) == RANK
+    assert lp(r=-1) == RANK
+    assert lp(N=-1) == SHAPE
+    assert lp(K=-16) == SHAPE
+    assert lp(U=None) == NULL                              # dU given needs U
+    assert lp(V=None) == NULL                              # dV given needs V
+    assert lp(dU=A16 + 4) == ALIGN
+    assert lp(V=A16 + 2) == ALIGN
+    assert lp(wsb=1) == WORKSPACE
+    # nothing to do: returns before any launch, whatever the pointers
+    assert lp(r=0, U=None, V=None) == OK
+    assert lp(dU=None, dV=None, U=None, V=None) == OK
+    assert lp(N=0, dV=None, U=None) == OK
+
+
+def test_lora_project_workspace():
+    n = lib.fs4_lora_project_workspace_bytes(8192, 3072, 32)
+    assert n > 0
+    assert lib.fs4_workspace_bytes(fs4.FS4_OP_LORA_PROJECT, 8192, 3072, 0, 32) == n
+    assert lib.fs4_lora_project_workspace_bytes(64, 64, 65) == 0
+    assert lib.fs4_lora_project_workspace_bytes(8192, 8192, 64) >= n
