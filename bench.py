@@ -286,6 +286,21 @@ def main():
                                 "achieved": round(ns_tf, 2), "unit": "TFLOP/s",
                                 "frac": round(ns_tf / PEAK_BF16_TFLOPS, 4), "ms_per_call": round(ns_ms, 4)}
 
+        # ---- subspace-constrained rank-r gradients at the 3B shapes ----------
+        # (the step's dU [N, r] and dV [r, K], projected in place; latency-
+        # bound: the r x r eliminations are sequential)
+        gu = torch.randn((N, r), device=dev, generator=torch.Generator(device=dev).manual_seed(7))
+        gv = torch.randn((r, K), device=dev, generator=torch.Generator(device=dev).manual_seed(8))
+        lp_call = lambda: fs4.lora_project(U, V, gu, gv)
+        for _ in range(5):
+            lp_call()
+        lp_ms = time_calls(lp_call, 50)
+        lp_bytes = N * r * 2 + r * K * 2 + 2 * (N * r * 4 + r * K * 4)
+        out["lora_project"] = {"workload": "U 8192x32, V 32x3072 bf16; dU, dV fp32, projected in place",
+                               "us_per_call": round(lp_ms * 1e3, 2), "bound": "latency",
+                               "algorithmic_bytes": lp_bytes,
+                               "achieved_GBps": round(lp_bytes / (lp_ms * 1e-3) / 1e9, 1)}
+
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
