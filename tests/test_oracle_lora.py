@@ -1,5 +1,5 @@
-"""Pins for the oracle's LoRA-SVD training-side steps (Cholesky-QR and the
-subspace-constrained low-rank gradients)."""
+"""Pins for the oracle's LoRA-SVD training-side steps (Cholesky-QR, the
+subspace-constrained low-rank gradients, the randomized-SVD realignment)."""
 import numpy as np
 import pytest
 
@@ -107,3 +107,77 @@ def test_projection_sides_are_independent():
     none_u, only_v = subspace_project(u, v, None, dv)
     assert none_u is None and none_v is None
     assert np.array_equal(both_u, only_u) and np.array_equal(both_v, only_v)
+
+
+# ---- realignment ------------------------------------------------------------
+from oracle.lora import bf16_rne, lora_realign
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(5000) * np.exp(rng.uniform(-20, 20, 5000)),
+                        [0.0, -0.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 65504.0, 1e-40]])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bf16_rne(x), want)
+
+
+def _split(w, r, rng, beta=1.0):
+    """An arbitrary (not principal) split of w: random BF16 factors, R the rest."""
+    n, k = w.shape
+    u = bf16_rne(rng.standard_normal((n, r)) * 0.1)
+    v = bf16_rne(rng.standard_normal((r, k)) * 0.1)
+    return u, v, (w - beta * (u @ v)).astype(np.float32)
+
+
+def test_realign_recovers_an_exactly_low_rank_weight():
+    rng = np.random.default_rng(1)
+    n, k, r, l = 120, 96, 6, 10
+    w = (rng.standard_normal((n, r)) * [8, 5, 3, 2, 1, 0.5]) @ rng.standard_normal((r, k))
+    w = w.astype(np.float32).astype(np.float64)
+    u, v, res = _split(w, r, rng)
+    w = u @ v + res.astype(np.float64)        # the weight the split holds (R is fp32)
+    s_true = np.linalg.svd(w, compute_uv=False)[:r]
+    for q in (0, 1, 2):
+        u2, v2, r2, s = lora_realign(u, v, res, 1.0, rng.standard_normal((l, k)), q)
+        assert np.allclose(s, s_true, rtol=1e-10, atol=0)
+        # W is rank r to within fp32: the residual holds the BF16 rounding of
+        # the factors
+        assert np.abs(r2).max() <= 2 ** -7 * np.abs(w).max()
+        assert np.abs(u2 @ v2 + r2 - w).max() <= 1e-6 * np.abs(w).max()
+
+
+def test_realign_matches_the_truncated_svd_with_a_gap():
+    rng = np.random.default_rng(2)
+    n, k, r, l = 200, 160, 8, 16
+    a, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    b, _ = np.linalg.qr(rng.standard_normal((k, k)))
+    sig = np.concatenate([np.linspace(10, 5, r), 0.05 * np.exp(-np.arange(k - r) / 20)])
+    w = (a[:, :k] * sig) @ b.T
+    u, v, res = _split(w, r, rng)
+    u2, v2, r2, s = lora_realign(u, v, res, 1.0, rng.standard_normal((l, k)), 2)
+    assert np.allclose(s, sig[:r], rtol=1e-8)
+    best = (a[:, :r] * sig[:r]) @ b[:, :r].T              # Eckart-Young
+    assert np.abs(u2 @ v2 - best).max() <= 2 ** -7 * np.abs(best).max()
+    # the residual's norm is the tail of the spectrum, up to the factors' rounding
+    assert abs(np.linalg.norm(r2) - np.linalg.norm(sig[r:])) <= 2 ** -7 * np.linalg.norm(best)
+
+
+def test_realign_depends_only_on_the_weight_and_splits_beta():
+    rng = np.random.default_rng(3)
+    n, k, r, l = 64, 80, 4, 8
+    w = rng.standard_normal((n, k)) + 6 * np.outer(rng.standard_normal(n), rng.standard_normal(k))
+    om = rng.standard_normal((l, k))
+    u, v, res = _split(w, r, rng)
+    u_b, v_b, res_b = _split(w, r, np.random.default_rng(33))
+    out1 = lora_realign(u, v, res, 1.0, om, 1)
+    out2 = lora_realign(u_b, v_b, res_b, 1.0, om, 1)
+    # the two splits hold W to within the fp32 rounding of their residuals
+    assert np.allclose(out1[3], out2[3], rtol=1e-6)
+    assert np.abs(out1[0] @ out1[1] - out2[0] @ out2[1]).max() <= 2 ** -7 * np.abs(w).max()
+    # beta: the same weight with beta = 4 gives factors half as large
+    u4, v4, res4 = _split(w, r, rng, beta=4.0)
+    o4 = lora_realign(u4, v4, res4, 4.0, om, 1)
+    assert np.allclose(o4[3], out1[3], rtol=1e-6)
+    assert np.abs(4.0 * o4[0] @ o4[1] - out1[0] @ out1[1]).max() <= 2 ** -7 * np.abs(w).max()
+    assert np.abs(4.0 * (o4[0] @ o4[1]) + o4[2] - w).max() <= 1e-6 * np.abs(w).max()
