@@ -192,6 +192,31 @@ size_t fs4_lora_project_workspace_bytes(int64_t N, int64_t K, int r);
 fs4_status fs4_lora_project(const void *U, const void *V, int64_t N, int64_t K, int r,
                             float *dU, float *dV, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * fs4_lora_realign — periodic realignment of the rank-r branch with a
+ * randomized SVD, [FS4 §2.1] (the subspace is reset every few thousand
+ * steps).  With W = beta U V + R:
+ *   Y = W Omega^T; q times: Y <- W orth(W^T orth(Y)); Q = orth(Y);
+ *   B = Q^T W = sum_i s_i (Q e_i) v_i^T  (the SVD of B, s descending);
+ *   U <- bf16(Q e_i sqrt(s_i / beta)), V <- bf16(sqrt(s_i / beta) v_i^T) for
+ *   i < r, and R <- fp32(W - beta U V) with those rounded factors,
+ * i.e. the randomized range finder of Halko, Martinsson and Tropp with q
+ * re-orthonormalised power iterations.
+ *   U     bf16 [N][r], in/out         V     bf16 [r][K], in/out
+ *   R     fp32 [N][K], in/out: the residual's master copy
+ *   Omega fp32 [l][K]: l Gaussian test vectors (drawn by the caller)
+ *   sigma fp32 [r], out, nullable: s_0 >= s_1 >= ...
+ * 1 <= r <= l <= 64 (FS4_ERR_RANK); N and K positive multiples of 16 with
+ * l <= min(N, K) (FS4_ERR_SHAPE); 0 <= power_iters <= 16 and beta > 0
+ * (FS4_ERR_ARG).  All sums run in fp64 except the products with W (fp32
+ * operands, ~16-bit products, fp32 accumulation), which only shape the basis
+ * Q: W = beta U V + R holds afterwards to fp32 rounding whatever Q is.
+ */
+size_t fs4_lora_realign_workspace_bytes(int64_t N, int64_t K, int l);
+fs4_status fs4_lora_realign(void *U, void *V, float *R, int64_t N, int64_t K, int r, float beta,
+                            const float *Omega, int l, int power_iters, float *sigma,
+                            void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace size for any of the calls above, dispatched on the operation:
  *   FS4_OP_QUANTIZE   d0 = rows, d1 = cols
  *   FS4_OP_GEMM       d0 = M, d1 = N, d2 = K
@@ -199,9 +224,11 @@ fs4_status fs4_lora_project(const void *U, const void *V, int64_t N, int64_t K, 
  *   FS4_OP_LINEAR_BWD d0 = M, d1 = N, d2 = K, r
  *   FS4_OP_NS         d0 = m, d1 = n
  *   FS4_OP_LORA_PROJECT d0 = N, d1 = K, r
+ *   FS4_OP_LORA_REALIGN d0 = N, d1 = K, d2 = l
  * Returns 0 for an unknown op. */
 typedef enum { FS4_OP_QUANTIZE = 0, FS4_OP_GEMM = 1, FS4_OP_LINEAR_FWD = 2,
-               FS4_OP_LINEAR_BWD = 3, FS4_OP_NS = 4, FS4_OP_LORA_PROJECT = 5 } fs4_op;
+               FS4_OP_LINEAR_BWD = 3, FS4_OP_NS = 4, FS4_OP_LORA_PROJECT = 5,
+               FS4_OP_LORA_REALIGN = 6 } fs4_op;
 size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r);
 
 /* Human-readable name of a status code (static storage). */

@@ -14,6 +14,7 @@ Names follow the C ABI in include/fs4.h:
     linear_bwd(dY, X, X_col, R_col, U, V, T)  -> LinearBwd(dX, dW, dU, dV)
     newton_schulz(G, steps, abc, ...)         -> X (and traces)
     lora_project(U, V, dU, dV)                -> (dU, dV) projected in place
+    lora_realign(U, V, R, Omega, ...)         -> sigma; U, V, R realigned in place
 """
 from __future__ import annotations
 
@@ -34,7 +35,8 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 FS4_BF16, FS4_FP32 = 0, 1
-FS4_OP_QUANTIZE, FS4_OP_GEMM, FS4_OP_LINEAR_FWD, FS4_OP_LINEAR_BWD, FS4_OP_NS, FS4_OP_LORA_PROJECT = range(6)
+FS4_OP_QUANTIZE, FS4_OP_GEMM, FS4_OP_LINEAR_FWD, FS4_OP_LINEAR_BWD, FS4_OP_NS, FS4_OP_LORA_PROJECT, \
+    FS4_OP_LORA_REALIGN = range(7)
 MUON_ABC = (3.4445, -4.7750, 2.0315)
 
 EXPORTS = [
@@ -42,6 +44,7 @@ EXPORTS = [
     "fs4_linear_fwd_workspace_bytes", "fs4_linear_fwd", "fs4_linear_bwd_workspace_bytes",
     "fs4_linear_bwd", "fs4_newton_schulz_workspace_bytes", "fs4_newton_schulz",
     "fs4_lora_project_workspace_bytes", "fs4_lora_project",
+    "fs4_lora_realign_workspace_bytes", "fs4_lora_realign",
     "fs4_workspace_bytes", "fs4_status_str", "fs4_version",
 ]
 
@@ -85,6 +88,9 @@ _sig("fs4_linear_bwd", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _VP, _VP, _P, _P
 _sig("fs4_newton_schulz_workspace_bytes", _SZ, [_I64, _I64])
 _sig("fs4_lora_project_workspace_bytes", _SZ, [_I64, _I64, ctypes.c_int])
 _sig("fs4_lora_project", ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P, _SZ, _P])
+_sig("fs4_lora_realign_workspace_bytes", _SZ, [_I64, _I64, ctypes.c_int])
+_sig("fs4_lora_realign", ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int, _F, _P, ctypes.c_int,
+                                        ctypes.c_int, _P, _P, _SZ, _P])
 _sig("fs4_newton_schulz", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_int, _F, _F, _F,
                                          ctypes.c_int, _F, _P, _P, _P, _P, _P, _SZ, _P])
 
@@ -292,10 +298,28 @@ def lora_project(U: torch.Tensor, V: torch.Tensor, dU: Optional[torch.Tensor] = 
     return dU, dV
 
 
+def lora_realign(U: torch.Tensor, V: torch.Tensor, R: torch.Tensor, Omega: torch.Tensor,
+                 beta: float = 1.0, power_iters: int = 1) -> torch.Tensor:
+    """Randomized-SVD realignment of W = beta U V + R, in place: U bf16
+    [N, r], V bf16 [r, K], R fp32 [N, K]; Omega fp32 [l, K] Gaussian test
+    vectors (r <= l <= 64).  Returns sigma, the r leading singular values."""
+    N, r = U.shape
+    K = V.shape[1]
+    l = Omega.shape[0]
+    dev = U.device
+    sigma = torch.empty(r, dtype=torch.float32, device=dev)
+    nbytes = _lib.fs4_lora_realign_workspace_bytes(N, K, l)
+    ws = _workspace(nbytes, dev)
+    _check(_lib.fs4_lora_realign(U.data_ptr(), V.data_ptr(), R.data_ptr(), N, K, r, beta, Omega.data_ptr(),
+                                 l, power_iters, sigma.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)),
+           "fs4_lora_realign")
+    return sigma
+
+
 def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> int:
     return _lib.fs4_workspace_bytes(op, d0, d1, d2, r)
 
 
 __all__ = ["NVFP4", "quantize", "gemm_nt", "linear_fwd", "LinearFwd", "linear_bwd", "LinearBwd",
-           "newton_schulz", "lora_project", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
+           "newton_schulz", "lora_project", "lora_realign", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
            "EXPORTS", "MUON_ABC"]

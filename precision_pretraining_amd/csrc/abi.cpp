@@ -427,6 +427,27 @@ fs4_status fs4_lora_project(const void *U, const void *V, int64_t N, int64_t K, 
                              do_v ? dV : nullptr, ws, as_stream(stream));
 }
 
+size_t fs4_lora_realign_workspace_bytes(int64_t N, int64_t K, int l) {
+  if (!dim_ok(N) || !dim_ok(K) || l < 1 || l > kMaxRank) return 0;
+  return lora_realign_ws_bytes(N, K, l);
+}
+
+fs4_status fs4_lora_realign(void *U, void *V, float *R, int64_t N, int64_t K, int r, float beta,
+                            const float *Omega, int l, int power_iters, float *sigma, void *ws,
+                            size_t ws_bytes, void *stream) {
+  if (r < 1 || r > kMaxRank || l < r || l > kMaxRank) return FS4_ERR_RANK;
+  if (!dim_ok(N) || !dim_ok(K) || l > N || l > K) return FS4_ERR_SHAPE;
+  if (power_iters < 0 || power_iters > 16 || !(beta > 0.0f) || !(beta < 3.0e38f)) return FS4_ERR_ARG;
+  FS4_TRY(check_ptr(U));
+  FS4_TRY(check_ptr(V));
+  FS4_TRY(check_ptr(R));
+  FS4_TRY(check_ptr(Omega));
+  if (sigma && ((uintptr_t)sigma & 3u)) return FS4_ERR_ALIGN;
+  FS4_TRY(check_ws(ws, ws_bytes, lora_realign_ws_bytes(N, K, l)));
+  return launch_lora_realign((uint16_t *)U, (uint16_t *)V, R, N, K, r, beta, Omega, l, power_iters,
+                             sigma, ws, as_stream(stream));
+}
+
 size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r) {
   switch (op) {
     case FS4_OP_QUANTIZE: return fs4_quantize_workspace_bytes(d0, d1);
@@ -435,6 +456,7 @@ size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r)
     case FS4_OP_LINEAR_BWD: return fs4_linear_bwd_workspace_bytes(d0, d1, d2, r);
     case FS4_OP_NS: return fs4_newton_schulz_workspace_bytes(d0, d1);
     case FS4_OP_LORA_PROJECT: return fs4_lora_project_workspace_bytes(d0, d1, r);
+    case FS4_OP_LORA_REALIGN: return fs4_lora_realign_workspace_bytes(d0, d1, (int)d2);
   }
   return 0;
 }

@@ -175,6 +175,16 @@ fs4_status launch_transpose_f32(const void *src, fs4_dtype dt, int64_t rows, int
 // nullable), fp64 Gram matrices, Cholesky and solves; `ws` needs
 // lora_project_ws_bytes(N, K, r).
 size_t lora_project_ws_bytes(int64_t N, int64_t K, int r);
+// red [l][2l] = [A^T A | A^T A] in fp64 for A fp32 [L][l] (l <= 64);
+// `part` needs gram_f32_ws_bytes(L, l)
+size_t gram_f32_ws_bytes(int64_t L, int l);
+fs4_status launch_gram_f32(const float *A, int64_t L, int l, double *part, double *red, hipStream_t s);
+// Randomized-SVD realignment of W = beta U V + R (U, V and R updated in
+// place); `ws` needs lora_realign_ws_bytes(N, K, l)
+size_t lora_realign_ws_bytes(int64_t N, int64_t K, int l);
+fs4_status launch_lora_realign(uint16_t *U, uint16_t *V, float *R, int64_t N, int64_t K, int r,
+                               float beta, const float *Omega, int l, int power_iters, float *sigma,
+                               void *ws, hipStream_t s);
 fs4_status launch_lora_project(const uint16_t *U, const uint16_t *V, int64_t N, int64_t K, int r,
                                float *dU, float *dV, void *ws, hipStream_t s);
 

@@ -41,7 +41,7 @@ constexpr int kChunk = 64;        // samples staged in LDS per pass
 constexpr int kMaxGroups = 256;   // partial-sum workgroups per side
 
 struct Side {
-  const uint16_t *A;    // bf16: a(s, i) = A[s * a_ss + i * a_si]
+  const uint16_t *A;    // bf16: a(s, i) = A[s * a_ss + i * a_si] (or fp32 from Af)
   int64_t a_ss, a_si;
   float *G;             // fp32: g(s, j) = G[s * g_ss + j * g_si], updated in place
   int64_t g_ss, g_si;
@@ -50,6 +50,7 @@ struct Side {
   double *part;         // [groups][r][2r]
   double *red;          // [r][2r]: [S | M]
   double *Z;            // [r][r]
+  const float *Af;      // when set, a(s, i) = Af[s * a_ss + i * a_si] in fp32
 };
 struct Sides {
   Side s[2];
@@ -109,7 +110,8 @@ __global__ __launch_bounds__(kThreads) void gram_partial_kernel(Sides args) {
       const int s = s_fast ? e % kChunk : e / r, i = s_fast ? e / kChunk : e % r;
       const int64_t gs = c0 + s;
       const bool in = gs < sd.L;
-      st[s * kRow + i] = in ? (double)bf16_bits_to_float(sd.A[gs * sd.a_ss + i * sd.a_si]) : 0.0;
+      const int64_t ai = gs * sd.a_ss + i * sd.a_si;
+      st[s * kRow + i] = in ? (sd.Af ? (double)sd.Af[ai] : (double)bf16_bits_to_float(sd.A[ai])) : 0.0;
       st[s * kRow + r + i] = in ? (double)sd.G[gs * sd.g_ss + i * sd.g_si] : 0.0;
     }
     __syncthreads();
@@ -250,6 +252,29 @@ int groups_for(int64_t L) {
 
 }  // namespace
 
+size_t gram_f32_ws_bytes(int64_t L, int l) {
+  return (size_t)groups_for(L) * l * 2 * l * sizeof(double);
+}
+
+fs4_status launch_gram_f32(const float *A, int64_t L, int l, double *part, double *red, hipStream_t s) {
+  Sides a;
+  a.r = l;
+  // the same matrix on both sides of [S | M]: red = [A^T A | A^T A]
+  a.s[0] = Side{nullptr, l, 1, const_cast<float *>(A), l, 1, L, groups_for(L), part, red, nullptr, A};
+  const int nq = nq_for(l);
+#define FS4_GRAMF(NQ)                                                                        \
+  case NQ:                                                                                   \
+    gram_partial_kernel<NQ><<<dim3(a.s[0].groups, 1), kThreads, 0, s>>>(a);                  \
+    break;
+  switch (nq) {
+    FS4_GRAMF(1) FS4_GRAMF(2) FS4_GRAMF(4) FS4_GRAMF(8) FS4_GRAMF(16) FS4_GRAMF(32)
+    default: return FS4_ERR_RANK;
+  }
+#undef FS4_GRAMF
+  gram_reduce_kernel<<<dim3((2 * l * l + kThreads - 1) / kThreads, 1), kThreads, 0, s>>>(a);
+  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+}
+
 size_t lora_project_ws_bytes(int64_t N, int64_t K, int r) {
   Carver c(nullptr);
   const int rr = r > 0 ? r : 1;
@@ -276,10 +301,10 @@ fs4_status launch_lora_project(const uint16_t *U, const uint16_t *V, int64_t N, 
   a.r = r;
   int n = 0;
   if (dU && N > 0) {
-    a.s[n++] = Side{U, r, 1, dU, r, 1, N, groups_for(N), part_u, red_u, z_u};
+    a.s[n++] = Side{U, r, 1, dU, r, 1, N, groups_for(N), part_u, red_u, z_u, nullptr};
   }
   if (dV && K > 0) {
-    a.s[n++] = Side{V, 1, K, dV, 1, K, K, groups_for(K), part_v, red_v, z_v};
+    a.s[n++] = Side{V, 1, K, dV, 1, K, K, groups_for(K), part_v, red_v, z_v, nullptr};
   }
   if (n == 0) return FS4_OK;
   int gmax = 1;

@@ -177,3 +177,28 @@ def test_lora_project_workspace():
     assert lib.fs4_workspace_bytes(fs4.FS4_OP_LORA_PROJECT, 8192, 3072, 0, 32) == n
     assert lib.fs4_lora_project_workspace_bytes(64, 64, 65) == 0
     assert lib.fs4_lora_project_workspace_bytes(8192, 8192, 64) >= n
+
+
+def ra(N=64, K=48, r=8, l=12, beta=1.0, q=1, U=A16, V=A16 * 2, R=A16 * 3, Om=A16 * 5, sig=None, wsb=1 << 30):
+    return lib.fs4_lora_realign(U, V, R, N, K, r, beta, Om, l, q, sig, A16 * 16, wsb, None)
+
+
+def test_lora_realign_validation():
+    assert ra(r=0) == RANK
+    assert ra(l=7) == RANK                                 # l < r
+    assert ra(l=65) == RANK
+    assert ra(N=40) == SHAPE                               # not a multiple of 16
+    assert ra(K=0) == SHAPE
+    assert ra(N=16, l=17, r=8) == SHAPE                    # l > min(N, K)
+    assert ra(q=-1) == ARG
+    assert ra(q=17) == ARG
+    assert ra(beta=0.0) == ARG
+    assert ra(beta=float("nan")) == ARG
+    assert ra(U=None) == NULL
+    assert ra(Om=A16 + 8) == ALIGN
+    assert ra(sig=A16 + 2) == ALIGN
+    assert ra(wsb=1) == WORKSPACE
+    assert lib.fs4_lora_realign_workspace_bytes(8192, 3072, 40) > 8192 * 3072 * 4
+    assert lib.fs4_workspace_bytes(fs4.FS4_OP_LORA_REALIGN, 8192, 3072, 40, 0) == \
+        lib.fs4_lora_realign_workspace_bytes(8192, 3072, 40)
+    assert lib.fs4_lora_realign_workspace_bytes(8192, 3072, 65) == 0

@@ -130,3 +130,89 @@ def test_rank_deficient_side_is_nan():
     assert np.all(np.isnan(got_u))
     _, ref_v = oracle.subspace_project(f32(u), f32(v), None, dv)
     _close(got_v, ref_v, "dV beside a singular U")
+
+
+# ---- realignment ------------------------------------------------------------
+# Same algorithm on both sides with the same test vectors; the library's
+# products with W use fp32 operands (~16-bit products), so the basis it finds
+# differs from the fp64 oracle's by ~1e-5, and BF16 rounding of the factors
+# can then land one BF16 step apart.  Compared: the singular values (1e-4,
+# or 1e-3 for the flat 3B spectrum), the reconstruction beta U V + R = W
+# (strict: fp32 rounding only), the rank-r part beta U V (within two BF16
+# steps of its largest entry), and the residual's norm.
+
+def _realign_case(fs4, u, v, res, om, beta, q):
+    U, V, R = dev_bf16(u), dev_bf16(v), dev_f32(res)
+    sig = fs4.lora_realign(U, V, R, dev_f32(om), beta=beta, power_iters=q)
+    torch.cuda.synchronize()
+    ub = U.view(torch.int16).cpu().numpy().view(np.uint16)
+    vb = V.view(torch.int16).cpu().numpy().view(np.uint16)
+    return f32(ub).astype(np.float64), f32(vb).astype(np.float64), R.cpu().numpy(), sig.cpu().numpy()
+
+
+def _check_realign(got, ref, w, beta, s_rtol):
+    gu, gv, gr, gs = got
+    ou, ov, orr, os_ = ref
+    assert np.all(np.isfinite(gu)) and np.all(np.isfinite(gv)) and np.all(np.isfinite(gr))
+    assert np.allclose(gs, os_, rtol=s_rtol, atol=0), (gs[:4], os_[:4])
+    # the split holds W exactly up to fp32 rounding
+    assert np.abs(beta * (gu @ gv) + gr - w).max() <= 1e-6 * np.abs(w).max()
+    lr_g, lr_o = beta * (gu @ gv), beta * (ou @ ov)
+    assert np.abs(lr_g - lr_o).max() <= 2 ** -7 * np.abs(lr_o).max()
+    assert abs(np.linalg.norm(gr) - np.linalg.norm(orr)) <= 1e-3 * np.linalg.norm(orr)
+
+
+def _bf16_bits(x):
+    return synth.bf16_round(np.asarray(x, np.float64))
+
+
+@pytest.mark.parametrize("N,K,r,l,q,beta", [(256, 192, 8, 16, 1, 1.0), (512, 160, 5, 13, 2, 0.5),
+                                            (144, 304, 16, 24, 0, 2.0)])
+def test_realign_matches_oracle_with_a_gap(N, K, r, l, q, beta):
+    fs4 = need_gpu()
+    print_case(test="lora_realign", N=N, K=K, r=r, l=l, q=q, beta=beta)
+    rng = np.random.default_rng(N + K + r)
+    a, _ = np.linalg.qr(rng.standard_normal((N, r + 30)))
+    b, _ = np.linalg.qr(rng.standard_normal((K, r + 30)))
+    sig = np.concatenate([np.linspace(4, 2, r), 0.02 * np.exp(-np.arange(30) / 8)])
+    w_true = (a * sig) @ b.T
+    u = _bf16_bits(rng.standard_normal((N, r)) * 0.05)
+    v = _bf16_bits(rng.standard_normal((r, K)) * 0.05)
+    res = (w_true - beta * f32(u).astype(np.float64) @ f32(v).astype(np.float64)).astype(np.float32)
+    w = beta * f32(u).astype(np.float64) @ f32(v).astype(np.float64) + res.astype(np.float64)
+    om = rng.standard_normal((l, K)).astype(np.float32)
+    got = _realign_case(fs4, u, v, res, om, beta, q)
+    ref = oracle.lora_realign(f32(u), f32(v), res, beta, om, q)
+    _check_realign(got, ref, w, beta, 1e-4)
+
+
+def test_realign_exactly_low_rank():
+    fs4 = need_gpu()
+    N, K, r, l = 320, 256, 6, 12
+    rng = np.random.default_rng(21)
+    w_true = (rng.standard_normal((N, r)) * [5, 4, 3, 2, 1, 0.5]) @ rng.standard_normal((r, K))
+    u = _bf16_bits(rng.standard_normal((N, r)) * 0.1)
+    v = _bf16_bits(rng.standard_normal((r, K)) * 0.1)
+    res = (w_true - f32(u).astype(np.float64) @ f32(v).astype(np.float64)).astype(np.float32)
+    w = f32(u).astype(np.float64) @ f32(v).astype(np.float64) + res.astype(np.float64)
+    om = rng.standard_normal((l, K)).astype(np.float32)
+    gu, gv, gr, gs = _realign_case(fs4, u, v, res, om, 1.0, 1)
+    s_true = np.linalg.svd(w, compute_uv=False)[:r]
+    assert np.allclose(gs, s_true, rtol=1e-5)
+    assert np.abs(gr).max() <= 2 ** -7 * np.abs(w).max()      # only the factors' BF16 rounding
+    assert np.abs(gu @ gv + gr - w).max() <= 1e-6 * np.abs(w).max()
+
+
+def test_realign_3b_shapes():
+    """The 3B weight (N 8192, K 3072, rank 32), l = 40 test vectors, one
+    power iteration."""
+    fs4 = need_gpu()
+    print_case(test="lora_realign_3b")
+    d = synth.linear3b()
+    u, v, res = d["U"], d["V"], d["R"]
+    rng = synth.rng_for(1234)
+    om = rng.standard_normal((40, 3072)).astype(np.float32)
+    w = f32(u).astype(np.float64) @ f32(v).astype(np.float64) + res.astype(np.float64)
+    got = _realign_case(fs4, u, v, res, om, 1.0, 1)
+    ref = oracle.lora_realign(f32(u), f32(v), res, 1.0, om, 1)
+    _check_realign(got, ref, w, 1.0, 1e-3)
