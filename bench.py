@@ -24,7 +24,9 @@ Extra fields: the dominant kernel's roofline (the block-scaled GEMM, timed
 with HIP events around its own launches at the three step shapes), the
 quantizer's HBM GB/s on the 4096 x 4096 workload (both layouts, inputs rotated
 through 12 copies so every call reads from HBM), the 5-step NVFP4
-Newton-Schulz on 3072 x 8192, and the CPU oracle timed on a bounded sample.
+Newton-Schulz on 3072 x 8192, the two LoRA-SVD training-side calls at the
+3B shapes (the subspace projection of dU and dV, and the randomized-SVD
+realignment of the branch), and the CPU oracle timed on a bounded sample.
 
 The GEMM's HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
 counter runs of ``--only gemm``, scaled by what the same counters read for a
@@ -300,6 +302,16 @@ def main():
                                "us_per_call": round(lp_ms * 1e3, 2), "bound": "latency",
                                "algorithmic_bytes": lp_bytes,
                                "achieved_GBps": round(lp_bytes / (lp_ms * 1e-3) / 1e9, 1)}
+
+        # ---- randomized-SVD realignment of the branch (every 2048 steps) ------
+        U2, V2, R2 = U.clone(), V.clone(), Rw.clone()
+        omega = torch.randn((40, K), device=dev, generator=torch.Generator(device=dev).manual_seed(9))
+        ra_call = lambda: fs4.lora_realign(U2, V2, R2, omega, power_iters=1)
+        ra_call()
+        ra_ms = time_calls(ra_call, 3)
+        out["lora_realign"] = {"workload": "W 8192x3072 = U V + R (rank 32), 40 test vectors, 1 power iteration",
+                               "ms_per_call": round(ra_ms, 3),
+                               "us_per_step_every_2048": round(ra_ms * 1e3 / 2048, 2)}
 
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
