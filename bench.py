@@ -1,7 +1,7 @@
 """Benchmark of the NVFP4 linear-projection hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
-    python bench.py --only {gemm,quantizer,copy}     (one leg alone, for profilers)
+    python bench.py --only {gemm,quantizer,copy,lora} (one leg alone, for profilers)
 
 One step is one pass of the whole hot path over one batch of synthetic input
 at the 3B-shape projection (X 8192 x 3072 bf16, W 8192 x 3072 with a rank-32
@@ -81,7 +81,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-extra", action="store_true", help="skip the quantizer/NS/roofline legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gemm", "quantizer", "copy"],
+    ap.add_argument("--only", choices=["gemm", "quantizer", "copy", "lora"],
                     help="run one leg alone (for counter runs under a profiler) and exit")
     return ap.parse_args()
 
@@ -257,6 +257,38 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    def lora_legs():
+        out = {}
+        # ---- subspace-constrained rank-r gradients at the 3B shapes ----------
+        # (the step's dU [N, r] and dV [r, K], projected in place; latency-
+        # bound: the r x r eliminations are sequential)
+        gu = torch.randn((N, r), device=dev, generator=torch.Generator(device=dev).manual_seed(7))
+        gv = torch.randn((r, K), device=dev, generator=torch.Generator(device=dev).manual_seed(8))
+        lp_call = lambda: fs4.lora_project(U, V, gu, gv)
+        for _ in range(5):
+            lp_call()
+        lp_ms = time_calls(lp_call, 50)
+        lp_bytes = N * r * 2 + r * K * 2 + 2 * (N * r * 4 + r * K * 4)
+        out["lora_project"] = {"workload": "U 8192x32, V 32x3072 bf16; dU, dV fp32, projected in place",
+                               "us_per_call": round(lp_ms * 1e3, 2), "bound": "latency",
+                               "algorithmic_bytes": lp_bytes,
+                               "achieved_GBps": round(lp_bytes / (lp_ms * 1e-3) / 1e9, 1)}
+
+        # ---- randomized-SVD realignment of the branch (every 2048 steps) ------
+        U2, V2, R2 = U.clone(), V.clone(), Rw.clone()
+        omega = torch.randn((40, K), device=dev, generator=torch.Generator(device=dev).manual_seed(9))
+        ra_call = lambda: fs4.lora_realign(U2, V2, R2, omega, power_iters=1)
+        ra_call()
+        ra_ms = time_calls(ra_call, 3)
+        out["lora_realign"] = {"workload": "W 8192x3072 = U V + R (rank 32), 40 test vectors, 1 power iteration",
+                               "ms_per_call": round(ra_ms, 3),
+                               "us_per_step_every_2048": round(ra_ms * 1e3 / 2048, 2)}
+        return out
+
+    if a.only == "lora":
+        print(json.dumps({"only": "lora", **lora_legs()}), flush=True)
+        return
+
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -288,30 +320,7 @@ def main():
                                 "achieved": round(ns_tf, 2), "unit": "TFLOP/s",
                                 "frac": round(ns_tf / PEAK_BF16_TFLOPS, 4), "ms_per_call": round(ns_ms, 4)}
 
-        # ---- subspace-constrained rank-r gradients at the 3B shapes ----------
-        # (the step's dU [N, r] and dV [r, K], projected in place; latency-
-        # bound: the r x r eliminations are sequential)
-        gu = torch.randn((N, r), device=dev, generator=torch.Generator(device=dev).manual_seed(7))
-        gv = torch.randn((r, K), device=dev, generator=torch.Generator(device=dev).manual_seed(8))
-        lp_call = lambda: fs4.lora_project(U, V, gu, gv)
-        for _ in range(5):
-            lp_call()
-        lp_ms = time_calls(lp_call, 50)
-        lp_bytes = N * r * 2 + r * K * 2 + 2 * (N * r * 4 + r * K * 4)
-        out["lora_project"] = {"workload": "U 8192x32, V 32x3072 bf16; dU, dV fp32, projected in place",
-                               "us_per_call": round(lp_ms * 1e3, 2), "bound": "latency",
-                               "algorithmic_bytes": lp_bytes,
-                               "achieved_GBps": round(lp_bytes / (lp_ms * 1e-3) / 1e9, 1)}
-
-        # ---- randomized-SVD realignment of the branch (every 2048 steps) ------
-        U2, V2, R2 = U.clone(), V.clone(), Rw.clone()
-        omega = torch.randn((40, K), device=dev, generator=torch.Generator(device=dev).manual_seed(9))
-        ra_call = lambda: fs4.lora_realign(U2, V2, R2, omega, power_iters=1)
-        ra_call()
-        ra_ms = time_calls(ra_call, 3)
-        out["lora_realign"] = {"workload": "W 8192x3072 = U V + R (rank 32), 40 test vectors, 1 power iteration",
-                               "ms_per_call": round(ra_ms, 3),
-                               "us_per_step_every_2048": round(ra_ms * 1e3 / 2048, 2)}
+        out.update(lora_legs())
 
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
