@@ -38,7 +38,7 @@ from .formats import (E2M1_GRID, e2m1_decode, e2m1_rne_index, e4m3_decode, e4m3_
                       tensor_scale_from_amax)
 from .quantize import NVFP4, quantize, quantize_rows, dequantize, block_values
 from .linear import gemm_nt, gemm_nt_abs, linear_fwd, linear_bwd, rel_err
-from .newton_schulz import ns_normalize, ns_step, newton_schulz, newton_schulz_fp64
+from .newton_schulz import ns_normalize, ns_step, newton_schulz, newton_schulz_fp64, abs_quantile, clip_abs
 from .lora import cholesky_qr, subspace_project, lora_realign, bf16_rne
 
 __all__ = [

@@ -3,9 +3,15 @@ infrastructure only).
 
 [FS4 §2.3]: the Root/Muon optimizer's Newton-Schulz matrix products run
 directly on NVFP4 operands rather than on a mixed-precision path.  The pages
-tune (a, b, c) per aspect ratio and clip at the 99th percentile but print
-neither; this oracle takes the fixed quintic used by Muon,
-(a, b, c) = (3.4445, -4.7750, 2.0315), and no clipping.
+tune (a, b, c) per aspect ratio and clip outliers at the 99th percentile but
+print neither the coefficients nor where the clip applies.  Readings: the
+caller passes (a, b, c), by default the fixed quintic used by Muon,
+(a, b, c) = (3.4445, -4.7750, 2.0315); with clipping on (clip_q, e.g. 0.99),
+the iterate X is clipped at the nearest-rank clip_q quantile of |X| before
+each of its quantizations, and only that quantized copy is clipped (the
+float32 state and the a X term keep the outliers).  A and B are quantized
+unclipped: A = X X^T carries its largest entries on the diagonal by
+construction.
 
 Iteration on X [m, n], m <= n:
 
@@ -38,14 +44,38 @@ def ns_normalize(g, eps: float = NS_EPS):
     return x64.astype(np.float32), x64
 
 
-def ns_step(x, a: float, b: float, c: float):
-    """One quantized Newton-Schulz step from float32 X.
+def abs_quantile(x, q: float) -> np.float32:
+    """Nearest-rank q-quantile of |x|: the k-th smallest magnitude, k =
+    ceil(q n) computed in float64 (1 <= k <= n), as float32."""
+    mag = np.abs(np.asarray(x, dtype=np.float32)).reshape(-1)
+    n = mag.size
+    k = int(np.ceil(float(q) * n))
+    k = min(max(k, 1), n)
+    return np.float32(np.partition(mag, k - 1)[k - 1])
+
+
+def clip_abs(x, p) -> np.ndarray:
+    """Clips float32 values to magnitude p, keeping each value's sign."""
+    x = np.asarray(x, dtype=np.float32)
+    p = np.float32(p)
+    return np.where(np.abs(x) > p, np.copysign(p, x), x).astype(np.float32)
+
+
+def ns_step(x, a: float, b: float, c: float, clip_q: float | None = None):
+    """One quantized Newton-Schulz step from float32 X (X clipped at the
+    clip_q quantile of |X| for its quantization when clip_q is given).
 
     Returns dict: A, B, X (float32 results), A64, B64, X64 (float64 before
-    rounding) and the error normalisers A_D, B_D, X_D.
+    rounding), the error normalisers A_D, B_D, X_D, and P, the clip value
+    (None without clipping).
     """
     x = np.asarray(x, dtype=np.float32)
-    x_row, x_col, _ = quantize(x, rowwise=True, colwise=True)
+    p = None
+    xq = x
+    if clip_q is not None:
+        p = abs_quantile(x, clip_q)
+        xq = clip_abs(x, p)
+    x_row, x_col, _ = quantize(xq, rowwise=True, colwise=True)
     a64 = gemm_nt(x_row, x_row)
     a_d = gemm_nt_abs(x_row, x_row)
     a32 = a64.astype(np.float32)
@@ -59,17 +89,18 @@ def ns_step(x, a: float, b: float, c: float):
     x64 = a * x.astype(np.float64) + bx
     x_d = abs(a) * np.abs(x.astype(np.float64)) + gemm_nt_abs(b_row, x_col)
     return {"A": a32, "A64": a64, "A_D": a_d, "B": b32, "B64": b64, "B_D": b_d,
-            "X": x64.astype(np.float32), "X64": x64, "X_D": x_d}
+            "X": x64.astype(np.float32), "X64": x64, "X_D": x_d, "P": p}
 
 
-def newton_schulz(g, steps: int = 5, abc=MUON_ABC, eps: float = NS_EPS, normalize: bool = True):
+def newton_schulz(g, steps: int = 5, abc=MUON_ABC, eps: float = NS_EPS, normalize: bool = True,
+                  clip_q: float | None = None):
     """Quantized NS from G.  Returns the list of float32 iterates X_0..X_steps
     and the list of per-step dicts from ``ns_step``."""
     a, b, c = abc
     x0 = ns_normalize(g, eps)[0] if normalize else np.asarray(g, dtype=np.float32)
     xs, steps_out = [x0], []
     for _ in range(steps):
-        st = ns_step(xs[-1], a, b, c)
+        st = ns_step(xs[-1], a, b, c, clip_q)
         steps_out.append(st)
         xs.append(st["X"])
     return xs, steps_out

@@ -129,3 +129,45 @@ def test_ns_normalize():
     g = np.array([[3.0, 4.0]], dtype=np.float32)
     x32, x64 = oracle.ns_normalize(g, eps=0.0)
     np.testing.assert_allclose(x64, [[0.6, 0.8]], rtol=1e-15)
+
+
+# ---- p99 outlier clipping ---------------------------------------------------
+from oracle.newton_schulz import MUON_ABC, abs_quantile, clip_abs
+
+
+def test_abs_quantile_hand_example_and_brute_force():
+    x = np.array([3.0, -1.0, 2.0, -5.0, 4.0], dtype=np.float32)
+    assert abs_quantile(x, 0.6) == np.float32(3.0)          # k = ceil(3.0) = 3rd smallest of 1..5
+    assert abs_quantile(x, 0.61) == np.float32(4.0)         # k = ceil(3.05) = 4
+    assert abs_quantile(x, 1.0) == np.float32(5.0)
+    assert abs_quantile(x, 1e-9) == np.float32(1.0)         # k = 1
+    rng = np.random.default_rng(0)
+    for n in (1, 7, 100, 1001):
+        v = (rng.standard_normal(n) * 3).astype(np.float32)
+        v[rng.random(n) < 0.3] = 0.0                        # ties at zero
+        v[:n // 4] = np.round(v[:n // 4])                   # and ties elsewhere
+        for q in (0.5, 0.9, 0.99, 1.0):
+            k = int(np.ceil(q * n))
+            assert abs_quantile(v, q) == np.sort(np.abs(v))[k - 1]
+
+
+def test_clip_keeps_signs_and_small_values():
+    x = np.array([3.0, -1.0, 2.0, -5.0, 4.0, -0.0, 0.0], dtype=np.float32)
+    got = clip_abs(x, np.float32(3.0))
+    assert got.tolist() == [3.0, -1.0, 2.0, -3.0, 3.0, 0.0, 0.0]
+    assert np.signbit(got[5]) and not np.signbit(got[6])
+
+
+def test_clipping_at_the_maximum_is_the_plain_step():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((32, 64)) * 0.05).astype(np.float32)
+    x[3, 5] = 2.0
+    plain = oracle.ns_step(x, *MUON_ABC)
+    same = oracle.ns_step(x, *MUON_ABC, clip_q=1.0)
+    for key in ("A", "B", "X"):
+        assert np.array_equal(plain[key], same[key])
+    clipped = oracle.ns_step(x, *MUON_ABC, clip_q=0.99)
+    assert clipped["P"] < 2.0
+    # the clip changes only the quantized copy: with a representable X the
+    # unclipped and clipped A differ only through the clipped entries
+    assert not np.array_equal(clipped["A"], plain["A"])
