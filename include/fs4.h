@@ -162,12 +162,41 @@ fs4_status fs4_linear_bwd(const void *dY, int64_t M, int64_t N, int64_t K,
  * The Frobenius norm is accumulated in fp64.  steps >= 0.  X_out holds
  * intermediate iterates during the call, so it may not overlap G or a trace
  * buffer (FS4_ERR_ARG).
+ * clip_q: 0 for none, else in (0, 1] (FS4_ERR_ARG): the outlier clipping of
+ * the Q-Root variant, [FS4 §2.3].  Before each quantization of X, its copy is
+ * clipped at p = the nearest-rank clip_q quantile of |X| (as
+ * fs4_abs_quantile); the fp32 state, A and B are not clipped.  The pages'
+ * shape-dependent (a, b, c) are the caller's (a, b, c).
  */
 size_t fs4_newton_schulz_workspace_bytes(int64_t m, int64_t n);
 fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, int steps,
-                             float a, float b, float c, int normalize, float eps,
+                             float a, float b, float c, int normalize, float eps, double clip_q,
                              float *X_out, float *trace_X, float *trace_A, float *trace_B,
                              void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * fs4_abs_quantile — the nearest-rank q-quantile of |x| for the outlier
+ * clipping of [FS4 §2.3] (Q-Root, p99): *out = the k-th smallest |x[i]|,
+ * k = ceil(q n) computed in fp64 and clamped to [1, n].  Exact: a radix
+ * selection over the magnitudes' bit patterns (three passes over x).
+ *   x   bf16 or fp32 [n], 1 <= n <= 2^31 (FS4_ERR_SHAPE)
+ *   q   in (0, 1] (FS4_ERR_ARG)
+ *   out one fp32 on the device (4-byte aligned)
+ */
+size_t fs4_abs_quantile_workspace_bytes(int64_t n);
+fs4_status fs4_abs_quantile(const void *x, fs4_dtype dt, int64_t n, double q, float *out,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * fs4_quantize_clipped — fs4_quantize of clip(x, p), p = the nearest-rank
+ * q-quantile of |x| (fs4_abs_quantile): magnitudes above p become p, signs
+ * kept, and p is the amax that sets the tensor scale.  Arguments and errors
+ * as fs4_quantize, plus q in (0, 1] (FS4_ERR_ARG) and rows * cols <= 2^31.
+ */
+size_t fs4_quantize_clipped_workspace_bytes(int64_t rows, int64_t cols);
+fs4_status fs4_quantize_clipped(const void *x, fs4_dtype dt, int64_t rows, int64_t cols, double q,
+                                const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
+                                void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * fs4_lora_project — subspace-constrained gradients of the rank-r branch,

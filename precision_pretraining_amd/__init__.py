@@ -45,6 +45,8 @@ EXPORTS = [
     "fs4_linear_bwd", "fs4_newton_schulz_workspace_bytes", "fs4_newton_schulz",
     "fs4_lora_project_workspace_bytes", "fs4_lora_project",
     "fs4_lora_realign_workspace_bytes", "fs4_lora_realign",
+    "fs4_abs_quantile_workspace_bytes", "fs4_abs_quantile",
+    "fs4_quantize_clipped_workspace_bytes", "fs4_quantize_clipped",
     "fs4_workspace_bytes", "fs4_status_str", "fs4_version",
 ]
 
@@ -92,7 +94,12 @@ _sig("fs4_lora_realign_workspace_bytes", _SZ, [_I64, _I64, ctypes.c_int])
 _sig("fs4_lora_realign", ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int, _F, _P, ctypes.c_int,
                                         ctypes.c_int, _P, _P, _SZ, _P])
 _sig("fs4_newton_schulz", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_int, _F, _F, _F,
-                                         ctypes.c_int, _F, _P, _P, _P, _P, _P, _SZ, _P])
+                                         ctypes.c_int, _F, ctypes.c_double, _P, _P, _P, _P, _P, _SZ, _P])
+_sig("fs4_abs_quantile_workspace_bytes", _SZ, [_I64])
+_sig("fs4_abs_quantile", ctypes.c_int, [_P, ctypes.c_int, _I64, ctypes.c_double, _P, _P, _SZ, _P])
+_sig("fs4_quantize_clipped_workspace_bytes", _SZ, [_I64, _I64])
+_sig("fs4_quantize_clipped", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_double, _VP, _VP, _P,
+                                            _SZ, _P])
 
 
 class FS4Error(RuntimeError):
@@ -261,10 +268,11 @@ def linear_bwd(dY: torch.Tensor, X: Optional[torch.Tensor], X_col: NVFP4, R_col:
 
 
 def newton_schulz(G: torch.Tensor, steps: int = 5, abc=MUON_ABC, normalize: bool = True, eps: float = 1e-7,
-                  trace: bool = False, out: Optional[torch.Tensor] = None):
+                  trace: bool = False, out: Optional[torch.Tensor] = None, clip_q: float = 0.0):
     """NVFP4 Newton-Schulz on G [m, n] (m <= n).  Returns X, or with
     trace=True (X, trace_X [steps+1, m, n], trace_A [steps, m, m],
-    trace_B [steps, m, m])."""
+    trace_B [steps, m, m]).  clip_q (e.g. 0.99): clip each quantized copy
+    of the iterate at that quantile of its magnitudes (0: off)."""
     m, n = G.shape
     dev = G.device
     X = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
@@ -275,7 +283,7 @@ def newton_schulz(G: torch.Tensor, steps: int = 5, abc=MUON_ABC, normalize: bool
     nbytes = _lib.fs4_newton_schulz_workspace_bytes(m, n)
     ws = _workspace(nbytes, dev)
     _check(_lib.fs4_newton_schulz(G.data_ptr(), _dtype_code(G), m, n, steps, a, b, c, int(normalize), eps,
-                                  X.data_ptr(), _ptr(tX), _ptr(tA), _ptr(tB), ws.data_ptr(), ws.numel(),
+                                  clip_q, X.data_ptr(), _ptr(tX), _ptr(tA), _ptr(tB), ws.data_ptr(), ws.numel(),
                                   _stream(dev)), "fs4_newton_schulz")
     if trace:
         return X, tX, tA, tB
@@ -316,10 +324,36 @@ def lora_realign(U: torch.Tensor, V: torch.Tensor, R: torch.Tensor, Omega: torch
     return sigma
 
 
+def abs_quantile(x: torch.Tensor, q: float) -> torch.Tensor:
+    """The nearest-rank q-quantile of |x| (a 1-element fp32 tensor)."""
+    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = _workspace(_lib.fs4_abs_quantile_workspace_bytes(x.numel()), x.device)
+    _check(_lib.fs4_abs_quantile(x.data_ptr(), _dtype_code(x), x.numel(), q, out.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), _stream(x.device)), "fs4_abs_quantile")
+    return out
+
+
+def quantize_clipped(x: torch.Tensor, q: float, rowwise: bool = True, colwise: bool = True):
+    """quantize() of x clipped at the nearest-rank q-quantile of |x|."""
+    rows, cols = x.shape
+    dev = x.device
+    orow = NVFP4.empty(rows, cols, dev) if rowwise else None
+    ocol = NVFP4.empty(cols, rows, dev, tscale=orow.tscale if orow is not None else None) if colwise else None
+    rv = orow.c() if orow is not None else None
+    cv = ocol.c() if ocol is not None else None
+    ws = _workspace(_lib.fs4_quantize_clipped_workspace_bytes(rows, cols), dev)
+    _check(_lib.fs4_quantize_clipped(x.data_ptr(), _dtype_code(x), rows, cols, q,
+                                     ctypes.byref(rv) if rv is not None else None,
+                                     ctypes.byref(cv) if cv is not None else None,
+                                     ws.data_ptr(), ws.numel(), _stream(dev)), "fs4_quantize_clipped")
+    return orow, ocol
+
+
 def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> int:
     return _lib.fs4_workspace_bytes(op, d0, d1, d2, r)
 
 
 __all__ = ["NVFP4", "quantize", "gemm_nt", "linear_fwd", "LinearFwd", "linear_bwd", "LinearBwd",
-           "newton_schulz", "lora_project", "lora_realign", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
+           "newton_schulz", "lora_project", "lora_realign", "abs_quantile", "quantize_clipped",
+           "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
            "EXPORTS", "MUON_ABC"]

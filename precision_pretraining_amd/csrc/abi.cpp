@@ -97,6 +97,8 @@ struct NsWs {
   uint32_t *amax;   // per-workgroup max |.| of the tensor about to be quantized
   float *split;     // split-k partials of the GEMMs
   int64_t split_floats;
+  void *sel_ws;     // the |x| quantile's histogram and state
+  float *clip;      // the clip value of the iterate (clipped runs)
 };
 NsWs carve_ns(void *ws, int64_t m, int64_t n, size_t *total) {
   Carver c(ws);
@@ -121,9 +123,13 @@ NsWs carve_ns(void *ws, int64_t m, int64_t n, size_t *total) {
     w.split_floats = std::min<int64_t>(kGemmSplitFloats, 8 * r256 * c256);
     w.split = (float *)c.take((size_t)w.split_floats * sizeof(float));
   }
+  w.sel_ws = c.take(abs_quantile_ws_bytes());
+  w.clip = (float *)c.take(sizeof(float));
   if (total) *total = c.off;
   return w;
 }
+
+bool quantile_ok(double q) { return q > 0.0 && q <= 1.0; }
 
 }  // namespace
 
@@ -172,6 +178,53 @@ fs4_status fs4_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
   }
   FS4_TRY(check_ws(ws, ws_bytes, quantize_ws_bytes()));
   return launch_quantize(x, dt, rows, cols, rowwise, colwise, ws, as_stream(stream));
+}
+
+size_t fs4_abs_quantile_workspace_bytes(int64_t) { return abs_quantile_ws_bytes(); }
+
+fs4_status fs4_abs_quantile(const void *x, fs4_dtype dt, int64_t n, double q, float *out, void *ws,
+                            size_t ws_bytes, void *stream) {
+  if (dt != FS4_BF16 && dt != FS4_FP32) return FS4_ERR_DTYPE;
+  if (n < 1 || n > ((int64_t)1 << 31)) return FS4_ERR_SHAPE;
+  if (!quantile_ok(q)) return FS4_ERR_ARG;
+  FS4_TRY(check_ptr(x));
+  if (!out) return FS4_ERR_NULL;
+  if ((uintptr_t)out & 3u) return FS4_ERR_ALIGN;
+  FS4_TRY(check_ws(ws, ws_bytes, abs_quantile_ws_bytes()));
+  return launch_abs_quantile(x, dt, n, q, out, ws, as_stream(stream));
+}
+
+size_t fs4_quantize_clipped_workspace_bytes(int64_t, int64_t) {
+  Carver c(nullptr);
+  c.take(quantize_ws_bytes());
+  c.take(abs_quantile_ws_bytes());
+  c.take(sizeof(float));
+  return c.off;
+}
+
+fs4_status fs4_quantize_clipped(const void *x, fs4_dtype dt, int64_t rows, int64_t cols, double q,
+                                const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise, void *ws,
+                                size_t ws_bytes, void *stream) {
+  if (!quantile_ok(q)) return FS4_ERR_ARG;
+  if (rows * cols > ((int64_t)1 << 31)) return FS4_ERR_SHAPE;
+  const size_t need = fs4_quantize_clipped_workspace_bytes(rows, cols);
+  if (ws_bytes < need) return FS4_ERR_WORKSPACE;
+  if (rows == 0 || cols == 0)   // nothing to clip: the plain call's checks and zero scales
+    return fs4_quantize(x, dt, rows, cols, rowwise, colwise, ws, ws_bytes, stream);
+  if (dt != FS4_BF16 && dt != FS4_FP32) return FS4_ERR_DTYPE;
+  if (rows < 0 || cols < 0) return FS4_ERR_SHAPE;
+  if (!rowwise && !colwise) return FS4_ERR_NULL;
+  FS4_TRY(check_ptr(x));
+  if (rowwise) FS4_TRY(check_view(rowwise, rows, cols));
+  if (colwise) FS4_TRY(check_view(colwise, cols, rows));
+  FS4_TRY(check_ws(ws, ws_bytes, need));
+  Carver c(ws);
+  c.take(quantize_ws_bytes());
+  void *sel = c.take(abs_quantile_ws_bytes());
+  float *clip = (float *)c.take(sizeof(float));
+  hipStream_t s = as_stream(stream);
+  FS4_TRY(launch_abs_quantile(x, dt, rows * cols, q, clip, sel, s));
+  return launch_quantize_encode(x, dt, rows, cols, rowwise, colwise, nullptr, 0, s, clip);
 }
 
 size_t fs4_gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
@@ -324,12 +377,14 @@ size_t fs4_newton_schulz_workspace_bytes(int64_t m, int64_t n) {
 }
 
 fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, int steps, float a,
-                             float b, float c, int normalize, float eps, float *X_out,
+                             float b, float c, int normalize, float eps, double clip_q, float *X_out,
                              float *trace_X, float *trace_A, float *trace_B, void *ws,
                              size_t ws_bytes, void *stream) {
   if (dt != FS4_BF16 && dt != FS4_FP32) return FS4_ERR_DTYPE;
   if (!dim_ok(m) || !dim_ok(n) || m > n) return FS4_ERR_SHAPE;
   if (steps < 0) return FS4_ERR_ARG;
+  if (clip_q != 0.0 && !quantile_ok(clip_q)) return FS4_ERR_ARG;
+  if (clip_q != 0.0 && m * n > ((int64_t)1 << 31)) return FS4_ERR_SHAPE;
   FS4_TRY(check_ptr(G));
   FS4_TRY(check_ptr(X_out));
   if (trace_X) FS4_TRY(check_ptr(trace_X));
@@ -387,7 +442,13 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
     // A = Q(X) Q(X)^T is computed (and stored) exactly symmetric, so its
     // column-wise quantization is its row-wise one bit for bit, and
     // A^2 = Q_row(A) Q_col(A)^T = Q(A) Q(A)^T is symmetric as well.
-    FS4_TRY(quantize(cur, n, m, &w.x_col, &w.x_row));
+    if (clip_q != 0.0) {
+      // the iterate's quantized copy is clipped at the clip_q quantile of |X|
+      FS4_TRY(launch_abs_quantile(cur, FS4_FP32, mn, clip_q, w.clip, w.sel_ws, s));
+      FS4_TRY(launch_quantize_encode(cur, FS4_FP32, n, m, &w.x_col, &w.x_row, nullptr, 0, s, w.clip));
+    } else {
+      FS4_TRY(quantize(cur, n, m, &w.x_col, &w.x_row));
+    }
     FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s, w.amax, &np, true,
                            w.split, w.split_floats));
     FS4_TRY(quantize(A, m, m, &w.a_row, nullptr));

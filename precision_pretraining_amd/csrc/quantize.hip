@@ -305,9 +305,10 @@ __device__ inline void tile_gload(const void *x, int64_t rows, int64_t cols, int
   }
 }
 
-template <bool BF16>
+// With CLIP, magnitudes above clipv are clipped to it (signs kept).
+template <bool BF16, bool CLIP = false>
 __device__ inline void tile_store(const TileRegs<BF16> &g, int64_t rows, int64_t cols, int64_t r0,
-                                  int64_t c0, float (*tile)[kTile + 1]) {
+                                  int64_t c0, float (*tile)[kTile + 1], float clipv = 0.0f) {
   constexpr int kPerRow = BF16 ? 8 : 16;
   constexpr int kElems = BF16 ? 8 : 4;
 #pragma unroll
@@ -320,12 +321,21 @@ __device__ inline void tile_store(const TileRegs<BF16> &g, int64_t rows, int64_t
     if constexpr (BF16) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        tile[r][ch * 8 + 2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu);
-        tile[r][ch * 8 + 2 * j + 1] = bf16_bits_to_float(w[j] >> 16);
+        float lo = bf16_bits_to_float(w[j] & 0xFFFFu), hi = bf16_bits_to_float(w[j] >> 16);
+        if constexpr (CLIP) {
+          lo = __builtin_copysignf(__builtin_fminf(__builtin_fabsf(lo), clipv), lo);
+          hi = __builtin_copysignf(__builtin_fminf(__builtin_fabsf(hi), clipv), hi);
+        }
+        tile[r][ch * 8 + 2 * j] = lo;
+        tile[r][ch * 8 + 2 * j + 1] = hi;
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) tile[r][ch * 4 + j] = __builtin_bit_cast(float, w[j]);
+      for (int j = 0; j < 4; ++j) {
+        float v = __builtin_bit_cast(float, w[j]);
+        if constexpr (CLIP) v = __builtin_copysignf(__builtin_fminf(__builtin_fabsf(v), clipv), v);
+        tile[r][ch * 4 + j] = v;
+      }
     }
   }
 }
@@ -381,19 +391,28 @@ struct TileOrder {
   __device__ int64_t c0(int sc) const { return (int64_t)(sc * 4 + sub_c) * kTile; }
 };
 
-template <bool BF16, bool ROW, bool COL>
+// With CLIP, *clip replaces the tensor amax and every element is clipped to
+// magnitude *clip before it is encoded (the partials are not read).
+template <bool BF16, bool ROW, bool COL, bool CLIP = false>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restrict__ x, int64_t rows,
                                                             int64_t cols,
                                                             const uint32_t *__restrict__ partials,
-                                                            int npart, fs4_nvfp4 rv, fs4_nvfp4 cv) {
+                                                            int npart, fs4_nvfp4 rv, fs4_nvfp4 cv,
+                                                            const float *clip = nullptr) {
   __shared__ float tile[kTile][kTile + 1];
   __shared__ Tables tab;
   __shared__ uint32_t red[kThreads / 64];
   // tensor scale from the amax partials (every workgroup reduces them itself)
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < npart; i += kThreads) m = m > partials[i] ? m : partials[i];
-  m = block_max_u32(m, red);
-  const float amax = __builtin_bit_cast(float, m);
+  float amax, clipv = 0.0f;
+  if constexpr (CLIP) {
+    clipv = *clip;
+    amax = clipv;
+  } else {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npart; i += kThreads) m = m > partials[i] ? m : partials[i];
+    m = block_max_u32(m, red);
+    amax = __builtin_bit_cast(float, m);
+  }
   const float s_t = (float)((double)amax / kTensorDiv);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (ROW) *rv.tscale = s_t;
@@ -414,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
   // 1/(6 s_t) only seeds the scale-code estimate; the tables make it exact
   const float inv6st = s_t > 0.0f ? (float)(1.0 / (6.0 * (double)s_t)) : 0.0f;   // may be inf
   const bool inv_finite = inv6st < __builtin_huge_valf();
-  tile_store<BF16>(g0, rows, cols, order.r0(sr), order.c0(sc), tile);
+  tile_store<BF16, CLIP>(g0, rows, cols, order.r0(sr), order.c0(sc), tile, clipv);
   __syncthreads();
 
   const int t = threadIdx.x;
@@ -442,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
       sbc = encode16([&](int i) { return src[i * (kTile + 1)]; }, inv6st, inv_finite, tab, pc);
     }
     __syncthreads();
-    tile_store<BF16>(nxt, rows, cols, order.r0(sr1), order.c0(sc1), tile);   // unread past the last tile
+    tile_store<BF16, CLIP>(nxt, rows, cols, order.r0(sr1), order.c0(sc1), tile, clipv);   // unread past the last tile
     if (ROW) {
       const int64_t gr = r0 + line, gc = c0 + blk * kBlock;
       if (gr < rows && gc < cols) {
@@ -479,7 +498,8 @@ size_t quantize_ws_bytes() { return kAmaxPartials * sizeof(uint32_t); }
 
 fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                                   const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
-                                  const uint32_t *partials, int npart, hipStream_t s) {
+                                  const uint32_t *partials, int npart, hipStream_t s,
+                                  const float *clip) {
   const fs4_nvfp4 none = {nullptr, nullptr, nullptr, 0, 0};
   const fs4_nvfp4 rv = rowwise ? *rowwise : none;
   const fs4_nvfp4 cv = colwise ? *colwise : none;
@@ -491,7 +511,13 @@ fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int
   static_assert(kEncodeGridBf16 % 128 == 0 && kEncodeGridF32 % 128 == 0,
                 "the tile walk needs a multiple of 16, whole super-tiles per XCD a multiple of 128");
   const bool row = rv.codes != nullptr, col = cv.codes != nullptr;
-#define FS4_QK(B, R, C) quantize_kernel<B, R, C><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv)
+#define FS4_QK(B, R, C)                                                                            \
+  do {                                                                                             \
+    if (clip)                                                                                      \
+      quantize_kernel<B, R, C, true><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv, clip); \
+    else                                                                                           \
+      quantize_kernel<B, R, C><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv);  \
+  } while (0)
   if (bf16) {
     if (row && col) FS4_QK(true, true, true);
     else if (row) FS4_QK(true, true, false);

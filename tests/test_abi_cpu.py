@@ -125,8 +125,8 @@ def test_linear_bwd_validation():
     assert bwd(wsb=1) == WORKSPACE
 
 
-def ns(G=A16, dt=0, m=64, n=128, steps=5, X=A16 * 4, wsb=1 << 30, tX=None):
-    return lib.fs4_newton_schulz(G, dt, m, n, steps, 3.4445, -4.775, 2.0315, 1, 1e-7, X, tX, None, None,
+def ns(G=A16, dt=0, m=64, n=128, steps=5, X=A16 * 4, wsb=1 << 30, tX=None, clip=0.0):
+    return lib.fs4_newton_schulz(G, dt, m, n, steps, 3.4445, -4.775, 2.0315, 1, 1e-7, clip, X, tX, None, None,
                                  A16 * 16, wsb, None)
 
 
@@ -141,6 +141,9 @@ def test_newton_schulz_validation():
     assert ns(X=A16) == ARG                                # X_out overlapping G (bf16 64 x 128)
     assert ns(X=A16 + 64 * 128 * 2 - 16) == ARG
     assert ns(X=A16 * 4 + 64 * 128 * 4 * 3, tX=A16 * 4) == ARG   # X_out inside trace_X
+    assert ns(clip=1.5) == ARG
+    assert ns(clip=-0.5) == ARG
+    assert ns(clip=float("nan")) == ARG
 
 
 def test_workspace_sizes_grow_with_shape():
@@ -202,3 +205,35 @@ def test_lora_realign_validation():
     assert lib.fs4_workspace_bytes(fs4.FS4_OP_LORA_REALIGN, 8192, 3072, 40, 0) == \
         lib.fs4_lora_realign_workspace_bytes(8192, 3072, 40)
     assert lib.fs4_lora_realign_workspace_bytes(8192, 3072, 65) == 0
+
+
+def test_abs_quantile_validation():
+    f = lambda x=A16, dt=1, n=100, q=0.99, out=A16 * 2, wsb=1 << 20: lib.fs4_abs_quantile(
+        x, dt, n, q, out, A16 * 16, wsb, None)
+    assert f(dt=5) == DTYPE
+    assert f(n=0) == SHAPE
+    assert f(n=(1 << 31) + 1) == SHAPE
+    assert f(q=0.0) == ARG
+    assert f(q=1.0000001) == ARG
+    assert f(x=None) == NULL
+    assert f(out=None) == NULL
+    assert f(out=A16 + 2) == ALIGN
+    assert f(x=A16 + 4) == ALIGN
+    assert f(wsb=8) == WORKSPACE
+    assert lib.fs4_abs_quantile_workspace_bytes(100) > 0
+
+
+def test_quantize_clipped_validation():
+    def qc(x=A16, dt=0, rows=64, cols=64, q=0.99, rv="ok", cv="ok", wsb=1 << 20):
+        r = view(rows, cols) if rv == "ok" else rv
+        c = view(cols, rows) if cv == "ok" else cv
+        return lib.fs4_quantize_clipped(x, dt, rows, cols, q, ctypes.byref(r) if r is not None else None,
+                                        ctypes.byref(c) if c is not None else None, A16 * 16, wsb, None)
+    assert qc(q=0.0) == ARG
+    assert qc(q=2.0) == ARG
+    assert qc(dt=9) == DTYPE
+    assert qc(rows=-16) == SHAPE
+    assert qc(rv=None, cv=None) == NULL
+    assert qc(rv=view(64, 48)) == SHAPE
+    assert qc(wsb=16) == WORKSPACE
+    assert lib.fs4_quantize_clipped_workspace_bytes(64, 64) > lib.fs4_quantize_workspace_bytes(64, 64)
