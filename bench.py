@@ -24,7 +24,8 @@ Extra fields: the dominant kernel's roofline (the block-scaled GEMM, timed
 with HIP events around its own launches at the three step shapes), the
 quantizer's HBM GB/s on the 4096 x 4096 workload (both layouts, inputs rotated
 through 12 copies so every call reads from HBM), the 5-step NVFP4
-Newton-Schulz on 3072 x 8192, the two LoRA-SVD training-side calls at the
+Newton-Schulz on 3072 x 8192 (plain, and with the iterate clipped at its
+p99 as in the Q-Root variant), the two LoRA-SVD training-side calls at the
 3B shapes (the subspace projection of dU and dV, and the randomized-SVD
 realignment of the branch), and the CPU oracle timed on a bounded sample.
 
@@ -319,6 +320,13 @@ def main():
         out["newton_schulz"] = {"workload": "G 3072x8192 bf16 ~N(0,1), 5 quintic steps, all GEMM operands NVFP4",
                                 "achieved": round(ns_tf, 2), "unit": "TFLOP/s",
                                 "frac": round(ns_tf / PEAK_BF16_TFLOPS, 4), "ms_per_call": round(ns_ms, 4)}
+        # the Q-Root variant: the iterate's quantized copy clipped at its p99
+        nsc_call = lambda: fs4.newton_schulz(G, steps=5, out=Xns, clip_q=0.99)
+        nsc_call()
+        nsc_ms = time_calls(nsc_call, 5)
+        out["newton_schulz_clip_p99"] = {"ms_per_call": round(nsc_ms, 4),
+                                         "achieved": round(ns_flops() / (nsc_ms * 1e-3) / 1e12, 2),
+                                         "unit": "TFLOP/s"}
 
         out.update(lora_legs())
 
