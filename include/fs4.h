@@ -246,6 +246,31 @@ fs4_status fs4_lora_realign(void *U, void *V, float *R, int64_t N, int64_t K, in
                             const float *Omega, int l, int power_iters, float *sigma,
                             void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * fs4_vstate_encode / fs4_vstate_decode — the Q-AdamW second-moment state
+ * codec, [FS4 §2.2]: sqrt, removal of a BF16 tile mean, Hadamard transform,
+ * NVFP4; decoding inverts each step and squares.
+ *   encode: s = sqrt(v); mu = bf16(mean of s over each 16 x 16 tile);
+ *           h = fp32(H/4 (s - mu)) on each 16-element row group (H the
+ *           16-point Sylvester Hadamard matrix; H/4 is orthonormal and its own
+ *           inverse); q = row-wise NVFP4 of h (one tensor scale).
+ *   decode: v_out = fp32((H/4 dequant(q) + mu)^2).
+ * Sums run in fp64 in a fixed order (butterflies with strides 1, 2, 4, 8; a
+ * tile's sum adds its 16 row-group sums in row order); mu rounds fp64 ->
+ * fp32 -> BF16, each to nearest even.
+ *   v      fp32 [R][C], non-negative and finite (else unspecified)
+ *   q      NVFP4 view, rows = R, cols = C (out of encode, in to decode)
+ *   means  bf16 [R/16][C/16]
+ *   v_out  fp32 [R][C]
+ * R and C positive multiples of 16 (FS4_ERR_SHAPE).  Decode needs no
+ * workspace.
+ */
+size_t fs4_vstate_encode_workspace_bytes(int64_t R, int64_t C);
+fs4_status fs4_vstate_encode(const float *v, int64_t R, int64_t C, const fs4_nvfp4 *q, void *means,
+                             void *ws, size_t ws_bytes, void *stream);
+fs4_status fs4_vstate_decode(const fs4_nvfp4 *q, const void *means, int64_t R, int64_t C, float *v_out,
+                             void *stream);
+
 /* Workspace size for any of the calls above, dispatched on the operation:
  *   FS4_OP_QUANTIZE   d0 = rows, d1 = cols
  *   FS4_OP_GEMM       d0 = M, d1 = N, d2 = K

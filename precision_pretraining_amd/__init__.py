@@ -15,6 +15,7 @@ Names follow the C ABI in include/fs4.h:
     newton_schulz(G, steps, abc, ...)         -> X (and traces)
     lora_project(U, V, dU, dV)                -> (dU, dV) projected in place
     lora_realign(U, V, R, Omega, ...)         -> sigma; U, V, R realigned in place
+    vstate_encode(v) / vstate_decode(q, mu)   -> the Q-AdamW second-moment codec
 """
 from __future__ import annotations
 
@@ -47,6 +48,7 @@ EXPORTS = [
     "fs4_lora_realign_workspace_bytes", "fs4_lora_realign",
     "fs4_abs_quantile_workspace_bytes", "fs4_abs_quantile",
     "fs4_quantize_clipped_workspace_bytes", "fs4_quantize_clipped",
+    "fs4_vstate_encode_workspace_bytes", "fs4_vstate_encode", "fs4_vstate_decode",
     "fs4_workspace_bytes", "fs4_status_str", "fs4_version",
 ]
 
@@ -88,6 +90,9 @@ _sig("fs4_linear_bwd_workspace_bytes", _SZ, [_I64, _I64, _I64, ctypes.c_int])
 _sig("fs4_linear_bwd", ctypes.c_int, [_P, _I64, _I64, _I64, _P, _VP, _VP, _P, _P, ctypes.c_int, _F,
                                       _P, _P, _P, _P, _P, _P, _SZ, _P])
 _sig("fs4_newton_schulz_workspace_bytes", _SZ, [_I64, _I64])
+_sig("fs4_vstate_encode_workspace_bytes", _SZ, [_I64, _I64])
+_sig("fs4_vstate_encode", ctypes.c_int, [_P, _I64, _I64, _VP, _P, _P, _SZ, _P])
+_sig("fs4_vstate_decode", ctypes.c_int, [_VP, _P, _I64, _I64, _P, _P])
 _sig("fs4_lora_project_workspace_bytes", _SZ, [_I64, _I64, ctypes.c_int])
 _sig("fs4_lora_project", ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P, _SZ, _P])
 _sig("fs4_lora_realign_workspace_bytes", _SZ, [_I64, _I64, ctypes.c_int])
@@ -349,11 +354,34 @@ def quantize_clipped(x: torch.Tensor, q: float, rowwise: bool = True, colwise: b
     return orow, ocol
 
 
+def vstate_encode(v: torch.Tensor):
+    """Q-AdamW second-moment codec: fp32 v [R, C] -> (NVFP4 view of the
+    transformed residual, BF16 tile means [R/16, C/16])."""
+    R, C = v.shape
+    dev = v.device
+    q = NVFP4.empty(R, C, dev)
+    means = torch.empty((R // 16, C // 16), dtype=torch.bfloat16, device=dev)
+    qv = q.c()
+    ws = _workspace(_lib.fs4_vstate_encode_workspace_bytes(R, C), dev)
+    _check(_lib.fs4_vstate_encode(v.data_ptr(), R, C, ctypes.byref(qv), means.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), _stream(dev)), "fs4_vstate_encode")
+    return q, means
+
+
+def vstate_decode(q: NVFP4, means: torch.Tensor) -> torch.Tensor:
+    """The fp32 second moment back from vstate_encode's outputs."""
+    out = torch.empty((q.rows, q.cols), dtype=torch.float32, device=means.device)
+    qv = q.c()
+    _check(_lib.fs4_vstate_decode(ctypes.byref(qv), means.data_ptr(), q.rows, q.cols, out.data_ptr(),
+                                  _stream(means.device)), "fs4_vstate_decode")
+    return out
+
+
 def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> int:
     return _lib.fs4_workspace_bytes(op, d0, d1, d2, r)
 
 
 __all__ = ["NVFP4", "quantize", "gemm_nt", "linear_fwd", "LinearFwd", "linear_bwd", "LinearBwd",
            "newton_schulz", "lora_project", "lora_realign", "abs_quantile", "quantize_clipped",
-           "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
+           "vstate_encode", "vstate_decode", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
            "EXPORTS", "MUON_ABC"]

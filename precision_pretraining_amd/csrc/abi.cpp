@@ -227,6 +227,30 @@ fs4_status fs4_quantize_clipped(const void *x, fs4_dtype dt, int64_t rows, int64
   return launch_quantize_encode(x, dt, rows, cols, rowwise, colwise, nullptr, 0, s, clip);
 }
 
+size_t fs4_vstate_encode_workspace_bytes(int64_t R, int64_t C) {
+  if (!dim_ok(R) || !dim_ok(C)) return 0;
+  return vstate_encode_ws_bytes(R, C);
+}
+
+fs4_status fs4_vstate_encode(const float *v, int64_t R, int64_t C, const fs4_nvfp4 *q, void *means, void *ws,
+                             size_t ws_bytes, void *stream) {
+  if (!dim_ok(R) || !dim_ok(C)) return FS4_ERR_SHAPE;
+  FS4_TRY(check_ptr(v));
+  FS4_TRY(check_view(q, R, C));
+  FS4_TRY(check_ptr(means));
+  FS4_TRY(check_ws(ws, ws_bytes, vstate_encode_ws_bytes(R, C)));
+  return launch_vstate_encode(v, R, C, *q, (uint16_t *)means, ws, as_stream(stream));
+}
+
+fs4_status fs4_vstate_decode(const fs4_nvfp4 *q, const void *means, int64_t R, int64_t C, float *v_out,
+                             void *stream) {
+  if (!dim_ok(R) || !dim_ok(C)) return FS4_ERR_SHAPE;
+  FS4_TRY(check_view(q, R, C));
+  FS4_TRY(check_ptr(means));
+  FS4_TRY(check_ptr(v_out));
+  return launch_vstate_decode(*q, (const uint16_t *)means, R, C, v_out, as_stream(stream));
+}
+
 size_t fs4_gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
 fs4_status fs4_gemm_nt(const fs4_nvfp4 *A, const fs4_nvfp4 *B, float alpha, const float *E,

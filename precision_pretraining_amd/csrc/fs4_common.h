@@ -109,6 +109,13 @@ fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int
 // fp64 clamped to [1, n], by exact radix selection; ws needs
 // abs_quantile_ws_bytes().  n >= 1.
 size_t abs_quantile_ws_bytes();
+// Q-AdamW second-moment codec: v fp32 [R][C] -> NVFP4 view q of h and BF16
+// tile means [R/16][C/16]; decode back to fp32 (R, C multiples of 16)
+size_t vstate_encode_ws_bytes(int64_t R, int64_t C);
+fs4_status launch_vstate_encode(const float *v, int64_t R, int64_t C, const fs4_nvfp4 &q,
+                                uint16_t *means, void *ws, hipStream_t s);
+fs4_status launch_vstate_decode(const fs4_nvfp4 &q, const uint16_t *means, int64_t R, int64_t C, float *out,
+                                hipStream_t s);
 fs4_status launch_abs_quantile(const void *x, fs4_dtype dt, int64_t n, double q, float *out, void *ws,
                                hipStream_t s);
 

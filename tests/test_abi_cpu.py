@@ -237,3 +237,22 @@ def test_quantize_clipped_validation():
     assert qc(rv=view(64, 48)) == SHAPE
     assert qc(wsb=16) == WORKSPACE
     assert lib.fs4_quantize_clipped_workspace_bytes(64, 64) > lib.fs4_quantize_workspace_bytes(64, 64)
+
+
+def test_vstate_validation():
+    enc = lambda R=64, C=48, v=A16, q="ok", mu=A16 * 3, wsb=1 << 30: lib.fs4_vstate_encode(
+        v, R, C, ctypes.byref(view(R, C) if q == "ok" else q), mu, A16 * 16, wsb, None)
+    assert enc(R=40) == SHAPE
+    assert enc(C=0) == SHAPE
+    assert enc(v=None) == NULL
+    assert enc(v=A16 + 4) == ALIGN
+    assert enc(q=view(64, 32)) == SHAPE
+    assert enc(mu=None) == NULL
+    assert enc(wsb=64) == WORKSPACE
+    dec = lambda R=64, C=48, out=A16 * 5, mu=A16 * 3: lib.fs4_vstate_decode(
+        ctypes.byref(view(R, C)), mu, R, C, out, None)
+    assert dec(R=17) == SHAPE
+    assert dec(out=None) == NULL
+    assert dec(mu=A16 + 2) == ALIGN
+    assert lib.fs4_vstate_encode_workspace_bytes(8192, 3072) >= 8192 * 3072 * 4
+    assert lib.fs4_vstate_encode_workspace_bytes(8192, 3070) == 0
