@@ -27,7 +27,9 @@ through 12 copies so every call reads from HBM), the 5-step NVFP4
 Newton-Schulz on 3072 x 8192 (plain, and with the iterate clipped at its
 p99 as in the Q-Root variant), the two LoRA-SVD training-side calls at the
 3B shapes (the subspace projection of dU and dV, and the randomized-SVD
-realignment of the branch), and the CPU oracle timed on a bounded sample.
+realignment of the branch), the Q-AdamW second-moment codec's encode and
+decode on the same weight's state, and the CPU oracle timed on a bounded
+sample.
 
 The GEMM's HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
 counter runs of ``--only gemm``, scaled by what the same counters read for a
@@ -329,6 +331,18 @@ def main():
                                          "unit": "TFLOP/s"}
 
         out.update(lora_legs())
+
+        # ---- Q-AdamW second-moment codec on the 8192 x 3072 weight's state ---
+        vst = (torch.randn((N, K), device=dev, generator=torch.Generator(device=dev).manual_seed(10)) ** 2) * 1e-8
+        qv, mv = fs4.vstate_encode(vst)
+        enc_ms = time_calls(lambda: fs4.vstate_encode(vst), 20)
+        dec_ms = time_calls(lambda: fs4.vstate_decode(qv, mv), 20)
+        vbytes = N * K * (4 + 0.5 + 1 / 16) + (N // 16) * (K // 16) * 2
+        out["adamw_vstate"] = {"workload": "v 8192x3072 fp32 <-> NVFP4 + BF16 16x16 tile means",
+                               "encode_us": round(enc_ms * 1e3, 2), "decode_us": round(dec_ms * 1e3, 2),
+                               "encode_GBps": round(vbytes / (enc_ms * 1e-3) / 1e9, 1),
+                               "decode_GBps": round(vbytes / (dec_ms * 1e-3) / 1e9, 1),
+                               "algorithmic_bytes": int(vbytes)}
 
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
