@@ -33,6 +33,7 @@ linear          block-scaled NT GEMM, LoRA-SVD linear forward and backward
 newton_schulz   NVFP4 Newton-Schulz iteration (and the unquantized fp64 one)
 lora            Cholesky-QR, the subspace-constrained low-rank gradients and
                 the randomized-SVD realignment
+adamw           the Q-AdamW optimizer-state codecs (second and first moment)
 """
 from .formats import (E2M1_GRID, e2m1_decode, e2m1_rne_index, e4m3_decode, e4m3_rne_satfinite,
                       tensor_scale_from_amax)
@@ -40,6 +41,7 @@ from .quantize import NVFP4, quantize, quantize_rows, dequantize, block_values
 from .linear import gemm_nt, gemm_nt_abs, linear_fwd, linear_bwd, rel_err
 from .newton_schulz import ns_normalize, ns_step, newton_schulz, newton_schulz_fp64, abs_quantile, clip_abs
 from .lora import cholesky_qr, subspace_project, lora_realign, bf16_rne
+from .adamw import vstate_encode, vstate_decode, mstate_encode, mstate_decode
 
 __all__ = [
     "E2M1_GRID", "e2m1_decode", "e2m1_rne_index", "e4m3_decode", "e4m3_rne_satfinite",

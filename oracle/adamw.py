@@ -1,4 +1,5 @@
-"""Q-AdamW second-moment state codec (oracle; test infrastructure only).
+"""Q-AdamW optimizer-state codecs (oracle; test infrastructure only): the
+second moment below, the first moment at the end of the module.
 
 [FS4 §2.2]: the AdamW second moment v_t is stored in NVFP4 after three
 steps: a square root that shortens its heavy tail, the removal of a tile
@@ -90,3 +91,78 @@ def vstate_decode(view: NVFP4, mu) -> np.ndarray:
     h_hat = dequantize(view)
     s_hat = hadamard16(h_hat) + np.repeat(np.repeat(np.asarray(mu, np.float64), TILE, axis=0), TILE, axis=1)
     return (s_hat * s_hat).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# First moment, [FS4 §2.2]: Hadamard mixing, then stochastic rounding and
+# adaptive 4/6 quantization.  Readings:
+#
+# * h = fp32(H/4 m) on each 16-element row group (as for v, no root, no mean);
+#   one tensor scale s_t = RNE_fp32(amax(h) / 2688) as in NVFP4.
+# * Adaptive 4/6 ("four over six"): each block tries the E4M3 scale that maps
+#   its amax to 6 and the one that maps it to 4, s_k = E4M3(amax_b / (k s_t)),
+#   quantizes the block to nearest with each, and keeps the one with the
+#   smaller sum of squared errors (6 on a tie).
+# * Stochastic rounding with the kept scale: y = |h| / (s_b s_t); at or above
+#   6 the code saturates; otherwise y lies in [g_lo, g_hi) between two E2M1
+#   magnitudes and rounds up exactly when u < (y - g_lo) / (g_hi - g_lo),
+#   u = r * 2^-32 for a caller-supplied uint32 r per element.
+# * Decode: m_hat = fp32(H/4 dequant).
+# All of it in fp64 with the divisions and comparisons stated.
+
+from .formats import E2M1_GRID, e2m1_rne_index, e4m3_decode, e4m3_rne_satfinite
+from .quantize import tensor_scale
+
+
+def _sse_rne(mag, step):
+    """Sum over the last axis of squared errors of round-to-nearest E2M1 at
+    the given step (float64; zero step gives the magnitudes' own squares)."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(step[..., None] > 0, mag / step[..., None], 0.0)
+    val = E2M1_GRID[e2m1_rne_index(ratio)] * step[..., None]
+    err = (mag - val) ** 2
+    tot = np.zeros(err.shape[:-1])
+    for k in range(err.shape[-1]):          # the elements of a block in order
+        tot = tot + err[..., k]
+    return tot
+
+
+def mstate_encode(m, rnd):
+    """First-moment codec.  m fp32 [R, C] (C % 16 == 0), rnd uint32 [R, C].
+    Returns (NVFP4 row view, h float32)."""
+    m = np.asarray(m, dtype=np.float32)
+    rows, cols = m.shape
+    h = hadamard16(m.astype(np.float64)).astype(np.float32)
+    s_t = tensor_scale(h)
+    st64 = float(s_t)
+    blocks = h.astype(np.float64).reshape(rows, cols // 16, 16)
+    mag = np.abs(blocks)
+    amax_b = mag.max(axis=2)
+    if st64 > 0.0:
+        s6 = e4m3_rne_satfinite(amax_b / (6.0 * st64))
+        s4 = e4m3_rne_satfinite(amax_b / (4.0 * st64))
+    else:
+        s6 = s4 = np.zeros(amax_b.shape, dtype=np.uint8)
+    e6 = _sse_rne(mag, e4m3_decode(s6) * st64)
+    e4 = _sse_rne(mag, e4m3_decode(s4) * st64)
+    sb = np.where(e4 < e6, s4, s6).astype(np.uint8)
+    step = e4m3_decode(sb) * st64
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.where(step[..., None] > 0, mag / step[..., None], 0.0)
+    lo = np.searchsorted(E2M1_GRID, y, side="right") - 1          # largest grid value <= y
+    lo = np.clip(lo, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    g_lo, g_hi = E2M1_GRID[lo], E2M1_GRID[hi]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(hi > lo, (y - g_lo) / (g_hi - g_lo), 0.0)
+    u = np.asarray(rnd, dtype=np.uint32).astype(np.float64).reshape(y.shape) * 2.0 ** -32
+    idx = np.where(u < p, hi, lo)
+    idx = np.where(step[..., None] > 0, idx, 0)
+    sign = np.signbit(blocks).astype(np.int64) << 3
+    codes = (idx | sign).reshape(rows, cols)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return NVFP4(packed, sb, np.float32(st64), rows, cols), h
+
+
+def mstate_decode(view: NVFP4) -> np.ndarray:
+    return hadamard16(dequantize(view)).astype(np.float32)

@@ -76,3 +76,88 @@ def test_codec_keeps_small_entries_of_a_heavy_tail():
     direct, _, _ = quantize(v, rowwise=True, colwise=False)
     med_direct = np.median(np.abs(dequantize(direct) - v) / v)
     assert med_direct > 0.9 and med_codec < 0.3, (med_codec, med_direct)
+
+
+# ---- first moment -------------------------------------------------------------
+from oracle.adamw import mstate_decode, mstate_encode
+from oracle.formats import E2M1_GRID, e4m3_decode
+from oracle.quantize import unpack_codes
+
+GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _m(shape, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(shape) * np.exp(rng.uniform(-3, 1, (shape[0], 1))) * 1e-3).astype(np.float32)
+
+
+def test_extreme_random_words_give_ceiling_and_floor():
+    m = _m((8, 64), 0)
+    view0, h = mstate_encode(m, np.zeros(m.shape, np.uint32))                 # u = 0: up whenever off-grid
+    view1, _ = mstate_encode(m, np.full(m.shape, 0xFFFFFFFF, np.uint32))      # u ~ 1: never up
+    step = np.repeat(e4m3_decode(view0.scales), 16, axis=1) * float(view0.tscale)
+    assert np.array_equal(view0.scales, view1.scales)
+    y = np.abs(h.astype(np.float64)) / step
+    for (i, j), yy in np.ndenumerate(y):
+        c0 = int(unpack_codes(view0.codes)[i, j]) & 7
+        c1 = int(unpack_codes(view1.codes)[i, j]) & 7
+        floor_i = max(k for k in range(8) if GRID[k] <= min(yy, 6.0))
+        ceil_i = min(k for k in range(8) if GRID[k] >= min(yy, 6.0))
+        assert c1 == floor_i and c0 == ceil_i, (yy, c0, c1)
+
+
+def test_stochastic_rounding_is_unbiased():
+    m = _m((4, 32), 1)
+    rng = np.random.default_rng(2)
+    acc = np.zeros(m.shape)
+    n = 400
+    for _ in range(n):
+        view, h = mstate_encode(m, rng.integers(0, 2 ** 32, m.shape, dtype=np.uint64).astype(np.uint32))
+        acc += oracle_dequant(view)
+    mean_err = acc / n - h.astype(np.float64)
+    step = np.repeat(e4m3_decode(view.scales), 16, axis=1) * float(view.tscale)
+    # the standard error of the mean of n draws within one grid gap (<= 2 steps) is <= step / sqrt(n)
+    assert np.all(np.abs(mean_err) <= 5 * 2 * step / np.sqrt(n) + 1e-30)
+
+
+def oracle_dequant(view):
+    from oracle.quantize import dequantize
+    return dequantize(view)
+
+
+def test_four_over_six_choice_by_brute_force():
+    m = _m((16, 128), 3)
+    view, h = mstate_encode(m, np.zeros(m.shape, np.uint32))
+    st = float(view.tscale)
+    from oracle.formats import e4m3_rne_satfinite
+    blocks = np.abs(h.astype(np.float64)).reshape(16, 8, 16)
+    n4 = 0
+    for i in range(16):
+        for b in range(8):
+            mag = blocks[i, b]
+            amax = mag.max()
+            cands = []
+            for k in (6.0, 4.0):
+                sb = int(e4m3_rne_satfinite(np.array([amax / (k * st)]))[0])
+                step = float(e4m3_decode(np.array([sb]))[0]) * st
+                err = 0.0
+                for x in mag:
+                    best = min(GRID, key=lambda g: (abs(x - g * step), GRID.index(g) % 2))
+                    err += (x - best * step) ** 2
+                cands.append((err, sb))
+            want = cands[1][1] if cands[1][0] < cands[0][0] else cands[0][1]
+            assert view.scales[i, b] == want, (i, b)
+            n4 += want != cands[0][1]
+    assert n4 > 0                                  # some blocks do prefer the 4-scale
+
+
+def test_first_moment_round_trip_parseval():
+    m = _m((32, 64), 4)
+    rng = np.random.default_rng(5)
+    view, h = mstate_encode(m, rng.integers(0, 2 ** 32, m.shape, dtype=np.uint64).astype(np.uint32))
+    m_hat = mstate_decode(view)
+    from oracle.quantize import dequantize
+    h_hat = dequantize(view)
+    e_m = np.linalg.norm((m_hat.astype(np.float64) - m).reshape(-1, 16), axis=1)
+    e_h = np.linalg.norm((h_hat - h).reshape(-1, 16), axis=1)
+    assert np.allclose(e_m, e_h, rtol=1e-5, atol=1e-6 * np.abs(m).max())
