@@ -271,6 +271,30 @@ fs4_status fs4_vstate_encode(const float *v, int64_t R, int64_t C, const fs4_nvf
 fs4_status fs4_vstate_decode(const fs4_nvfp4 *q, const void *means, int64_t R, int64_t C, float *v_out,
                              void *stream);
 
+/* ---------------------------------------------------------------------------
+ * fs4_mstate_encode / fs4_mstate_decode — the Q-AdamW first-moment state
+ * codec, [FS4 §2.2]: Hadamard mixing, then stochastic rounding and adaptive
+ * 4/6 block scales.
+ *   encode: h = fp32(H/4 m) on each 16-element row group (as for v);
+ *           s_t = RNE_fp32(amax(h) / 2688); per block the E4M3 scales for
+ *           amax_b / (6 s_t) and amax_b / (4 s_t) are tried and the one whose
+ *           round-to-nearest squared error (fp64, summed over the block in
+ *           order) is smaller is kept (6 on a tie); every element then rounds
+ *           stochastically: y = |h| / (s_b s_t), between E2M1 magnitudes
+ *           g_lo <= y < g_hi it takes g_hi exactly when
+ *           rnd * 2^-32 < (y - g_lo) / (g_hi - g_lo); y >= 6 gives 6.
+ *   decode: m_out = fp32(H/4 dequant(q)).
+ *   m      fp32 [R][C], finite
+ *   rnd    uint32 [R][C]: one uniform random word per element (the caller
+ *          draws them; the same words give the same codes)
+ *   q      NVFP4 view, rows = R, cols = C
+ * R and C positive multiples of 16 (FS4_ERR_SHAPE).
+ */
+size_t fs4_mstate_encode_workspace_bytes(int64_t R, int64_t C);
+fs4_status fs4_mstate_encode(const float *m, const uint32_t *rnd, int64_t R, int64_t C, const fs4_nvfp4 *q,
+                             void *ws, size_t ws_bytes, void *stream);
+fs4_status fs4_mstate_decode(const fs4_nvfp4 *q, int64_t R, int64_t C, float *m_out, void *stream);
+
 /* Workspace size for any of the calls above, dispatched on the operation:
  *   FS4_OP_QUANTIZE   d0 = rows, d1 = cols
  *   FS4_OP_GEMM       d0 = M, d1 = N, d2 = K

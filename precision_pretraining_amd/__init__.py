@@ -16,6 +16,7 @@ Names follow the C ABI in include/fs4.h:
     lora_project(U, V, dU, dV)                -> (dU, dV) projected in place
     lora_realign(U, V, R, Omega, ...)         -> sigma; U, V, R realigned in place
     vstate_encode(v) / vstate_decode(q, mu)   -> the Q-AdamW second-moment codec
+    mstate_encode(m, rnd) / mstate_decode(q)  -> the Q-AdamW first-moment codec
 """
 from __future__ import annotations
 
@@ -49,6 +50,7 @@ EXPORTS = [
     "fs4_abs_quantile_workspace_bytes", "fs4_abs_quantile",
     "fs4_quantize_clipped_workspace_bytes", "fs4_quantize_clipped",
     "fs4_vstate_encode_workspace_bytes", "fs4_vstate_encode", "fs4_vstate_decode",
+    "fs4_mstate_encode_workspace_bytes", "fs4_mstate_encode", "fs4_mstate_decode",
     "fs4_workspace_bytes", "fs4_status_str", "fs4_version",
 ]
 
@@ -93,6 +95,9 @@ _sig("fs4_newton_schulz_workspace_bytes", _SZ, [_I64, _I64])
 _sig("fs4_vstate_encode_workspace_bytes", _SZ, [_I64, _I64])
 _sig("fs4_vstate_encode", ctypes.c_int, [_P, _I64, _I64, _VP, _P, _P, _SZ, _P])
 _sig("fs4_vstate_decode", ctypes.c_int, [_VP, _P, _I64, _I64, _P, _P])
+_sig("fs4_mstate_encode_workspace_bytes", _SZ, [_I64, _I64])
+_sig("fs4_mstate_encode", ctypes.c_int, [_P, _P, _I64, _I64, _VP, _P, _SZ, _P])
+_sig("fs4_mstate_decode", ctypes.c_int, [_VP, _I64, _I64, _P, _P])
 _sig("fs4_lora_project_workspace_bytes", _SZ, [_I64, _I64, ctypes.c_int])
 _sig("fs4_lora_project", ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P, _SZ, _P])
 _sig("fs4_lora_realign_workspace_bytes", _SZ, [_I64, _I64, ctypes.c_int])
@@ -377,11 +382,32 @@ def vstate_decode(q: NVFP4, means: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def mstate_encode(m: torch.Tensor, rnd: torch.Tensor) -> NVFP4:
+    """Q-AdamW first-moment codec: fp32 m [R, C] and one random 32-bit word
+    per element (int32 or uint32 tensor, bits used as given) -> NVFP4 view."""
+    R, C = m.shape
+    dev = m.device
+    q = NVFP4.empty(R, C, dev)
+    qv = q.c()
+    ws = _workspace(_lib.fs4_mstate_encode_workspace_bytes(R, C), dev)
+    _check(_lib.fs4_mstate_encode(m.data_ptr(), rnd.data_ptr(), R, C, ctypes.byref(qv), ws.data_ptr(),
+                                  ws.numel(), _stream(dev)), "fs4_mstate_encode")
+    return q
+
+
+def mstate_decode(q: NVFP4) -> torch.Tensor:
+    out = torch.empty((q.rows, q.cols), dtype=torch.float32, device=q.codes.device)
+    qv = q.c()
+    _check(_lib.fs4_mstate_decode(ctypes.byref(qv), q.rows, q.cols, out.data_ptr(), _stream(q.codes.device)),
+           "fs4_mstate_decode")
+    return out
+
+
 def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> int:
     return _lib.fs4_workspace_bytes(op, d0, d1, d2, r)
 
 
 __all__ = ["NVFP4", "quantize", "gemm_nt", "linear_fwd", "LinearFwd", "linear_bwd", "LinearBwd",
            "newton_schulz", "lora_project", "lora_realign", "abs_quantile", "quantize_clipped",
-           "vstate_encode", "vstate_decode", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
+           "vstate_encode", "vstate_decode", "mstate_encode", "mstate_decode", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
            "EXPORTS", "MUON_ABC"]

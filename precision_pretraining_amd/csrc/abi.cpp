@@ -251,6 +251,28 @@ fs4_status fs4_vstate_decode(const fs4_nvfp4 *q, const void *means, int64_t R, i
   return launch_vstate_decode(*q, (const uint16_t *)means, R, C, v_out, as_stream(stream));
 }
 
+size_t fs4_mstate_encode_workspace_bytes(int64_t R, int64_t C) {
+  if (!dim_ok(R) || !dim_ok(C)) return 0;
+  return mstate_encode_ws_bytes(R, C);
+}
+
+fs4_status fs4_mstate_encode(const float *m, const uint32_t *rnd, int64_t R, int64_t C, const fs4_nvfp4 *q,
+                             void *ws, size_t ws_bytes, void *stream) {
+  if (!dim_ok(R) || !dim_ok(C)) return FS4_ERR_SHAPE;
+  FS4_TRY(check_ptr(m));
+  FS4_TRY(check_ptr(rnd));
+  FS4_TRY(check_view(q, R, C));
+  FS4_TRY(check_ws(ws, ws_bytes, mstate_encode_ws_bytes(R, C)));
+  return launch_mstate_encode(m, rnd, R, C, *q, ws, as_stream(stream));
+}
+
+fs4_status fs4_mstate_decode(const fs4_nvfp4 *q, int64_t R, int64_t C, float *m_out, void *stream) {
+  if (!dim_ok(R) || !dim_ok(C)) return FS4_ERR_SHAPE;
+  FS4_TRY(check_view(q, R, C));
+  FS4_TRY(check_ptr(m_out));
+  return launch_mstate_decode(*q, R, C, m_out, as_stream(stream));
+}
+
 size_t fs4_gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
 fs4_status fs4_gemm_nt(const fs4_nvfp4 *A, const fs4_nvfp4 *B, float alpha, const float *E,

@@ -1,4 +1,5 @@
-// Q-AdamW second-moment state codec for gfx950.
+// Q-AdamW optimizer-state codecs for gfx950: the second moment first, the
+// first moment further below.
 //
 // Full-Stack FP4 [FS4 §2.2] stores the AdamW second moment v in NVFP4 after
 // s = sqrt(v), the removal of a BF16 mean per 16 x 16 tile, and a Hadamard
@@ -159,6 +160,197 @@ __global__ __launch_bounds__(kThreads) void vstate_decode_kernel(const uint8_t *
   }
 }
 
+// ---- first moment --------------------------------------------------------
+// [FS4 §2.2] mixes the first moment with the Hadamard transform, then
+// quantizes it with stochastic rounding and adaptive 4/6 block scales:
+//   h = fp32(H/4 m) per 16-element group; s_t = RNE_fp32(amax(h) / 2688);
+//   per block, s_k = E4M3(amax_b / (k s_t)) for k = 6 and 4, keeping s_4 only
+//   when its round-to-nearest squared error (summed over the block in order)
+//   is smaller; each element then rounds up from the E2M1 magnitude below
+//   y = |h| / (s_b s_t) exactly when u < (y - g_lo) / (g_hi - g_lo), with
+//   u = r 2^-32 from the caller's uint32 r (saturating at 6);
+//   decode: m_hat = fp32(H/4 dequant).
+
+__device__ inline double e2m1_mag(int i) {
+  // 0, 0.5, 1, 1.5, 2, 3, 4, 6
+  return i < 4 ? 0.5 * (double)i : (double)(2 << ((i - 4) >> 1)) * ((i & 1) ? 1.5 : 1.0);
+}
+
+// index of the E2M1 magnitude nearest to y >= 0 (ties to the even index)
+__device__ inline int e2m1_rne_idx(double y) {
+  int i = 0;
+  i += y > 0.25;    // 0 | 0.5   tie -> 0
+  i += y >= 0.75;   // 0.5 | 1   tie -> 1.0 (index 2)
+  i += y > 1.25;    // 1 | 1.5   tie -> 1.0
+  i += y >= 1.75;   // 1.5 | 2   tie -> 2.0 (index 4)
+  i += y > 2.5;     // 2 | 3     tie -> 2.0
+  i += y >= 3.5;    // 3 | 4     tie -> 4.0 (index 6)
+  i += y > 5.0;     // 4 | 6     tie -> 4.0
+  return i;
+}
+
+__global__ __launch_bounds__(kThreads) void mstate_prep_kernel(const float *__restrict__ m, int64_t R,
+                                                               int64_t C, float *__restrict__ h,
+                                                               uint32_t *__restrict__ amax_parts) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t total = R * (C / 16);
+  float amax = 0.0f;
+  for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < total;
+       gi += (int64_t)gridDim.x * kThreads) {
+    const float4 *src = (const float4 *)(m + gi * 16);
+    double y[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 w = src[q];
+      y[4 * q] = w.x;
+      y[4 * q + 1] = w.y;
+      y[4 * q + 2] = w.z;
+      y[4 * q + 3] = w.w;
+    }
+    fwht16(y);
+    float o[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      o[k] = (float)(y[k] * 0.25);
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(o[k]));
+    }
+    float4 *dst = (float4 *)(h + gi * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  }
+  uint32_t ub = __builtin_bit_cast(uint32_t, amax);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)ub, off, 64);
+    ub = ub > o ? ub : o;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ub;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t mx = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) mx = mx > red[w] ? mx : red[w];
+    amax_parts[blockIdx.x] = mx;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void mstate_encode_kernel(const float *__restrict__ h, int64_t R, int64_t C,
+                                                                 const uint32_t *__restrict__ rnd,
+                                                                 const uint32_t *__restrict__ amax_parts,
+                                                                 int nparts, fs4_nvfp4 q) {
+  __shared__ uint32_t red[kThreads / 64];
+  uint32_t mx = 0;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) mx = mx > amax_parts[i] ? mx : amax_parts[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)mx, off, 64);
+    mx = mx > o ? mx : o;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  uint32_t am = red[0];
+  for (int w = 1; w < kThreads / 64; ++w) am = am > red[w] ? am : red[w];
+  const float s_t = (float)((double)__builtin_bit_cast(float, am) / kTensorDiv);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *q.tscale = s_t;
+  const double st = (double)s_t;
+  const int64_t groups_c = C / 16, total = R * groups_c;
+  for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < total;
+       gi += (int64_t)gridDim.x * kThreads) {
+    const float4 *src = (const float4 *)(h + gi * 16);
+    float x[16];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const float4 w = src[qq];
+      x[4 * qq] = w.x;
+      x[4 * qq + 1] = w.y;
+      x[4 * qq + 2] = w.z;
+      x[4 * qq + 3] = w.w;
+    }
+    double mag[16], amax_b = 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      mag[k] = __builtin_fabs((double)x[k]);
+      amax_b = amax_b > mag[k] ? amax_b : mag[k];
+    }
+    uint32_t sb = 0;
+    if (st > 0.0) {
+      const uint32_t s6 = e4m3_rne_satfinite(amax_b / (6.0 * st));
+      const uint32_t s4 = e4m3_rne_satfinite(amax_b / (4.0 * st));
+      double err[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const double step = (double)e4m3_to_float(c == 0 ? s6 : s4) * st;
+        double tot = 0.0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const double val = step > 0.0 ? e2m1_mag(e2m1_rne_idx(mag[k] / step)) * step : 0.0;
+          const double d = mag[k] - val;
+          tot = tot + d * d;
+        }
+        err[c] = tot;
+      }
+      sb = err[1] < err[0] ? s4 : s6;
+    }
+    const double step = (double)e4m3_to_float(sb) * st;
+    const uint4 rw0 = *(const uint4 *)(rnd + gi * 16), rw1 = *(const uint4 *)(rnd + gi * 16 + 4);
+    const uint4 rw2 = *(const uint4 *)(rnd + gi * 16 + 8), rw3 = *(const uint4 *)(rnd + gi * 16 + 12);
+    const uint32_t rr[16] = {rw0.x, rw0.y, rw0.z, rw0.w, rw1.x, rw1.y, rw1.z, rw1.w,
+                             rw2.x, rw2.y, rw2.z, rw2.w, rw3.x, rw3.y, rw3.z, rw3.w};
+    uint32_t lo32 = 0, hi32 = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      uint32_t idx = 0;
+      if (step > 0.0) {
+        const double y = mag[k] / step;
+        int lo = 0;
+#pragma unroll
+        for (int g = 1; g < 8; ++g) lo += e2m1_mag(g) <= y;     // largest magnitude <= y
+        if (lo < 7) {
+          const double glo = e2m1_mag(lo), ghi = e2m1_mag(lo + 1);
+          const double p = (y - glo) / (ghi - glo);
+          const double u = (double)rr[k] * 0x1p-32;
+          idx = (uint32_t)(u < p ? lo + 1 : lo);
+        } else {
+          idx = 7;
+        }
+      }
+      const uint32_t code = idx | ((__builtin_bit_cast(uint32_t, x[k]) >> 28) & 8u);
+      if (k < 8) lo32 |= code << (4 * k);
+      else hi32 |= code << (4 * (k - 8));
+    }
+    const int64_t row = gi / groups_c, g = gi % groups_c;
+    *(uint2 *)(q.codes + row * (C / 2) + g * 8) = make_uint2(lo32, hi32);
+    q.scales[row * groups_c + g] = (uint8_t)sb;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void mstate_decode_kernel(const uint8_t *__restrict__ codes,
+                                                                 const uint8_t *__restrict__ scales,
+                                                                 const float *__restrict__ tscale, int64_t R,
+                                                                 int64_t C, float *__restrict__ out) {
+  const int64_t groups_c = C / 16, total = R * groups_c;
+  const double st = (double)*tscale;
+  for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < total;
+       gi += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = gi / groups_c, g = gi % groups_c;
+    const uint2 cw = *(const uint2 *)(codes + row * (C / 2) + g * 8);
+    const double sb = (double)e4m3_to_float(scales[row * groups_c + g]);
+    double y[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t code = ((k < 8 ? cw.x : cw.y) >> (4 * (k & 7))) & 15u;
+      const double e = e2m1_mag((int)(code & 7u));
+      y[k] = ((code & 8u) ? -e : e) * sb * st;
+    }
+    fwht16(y);
+    float o[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o[k] = (float)(y[k] * 0.25);
+    float4 *dst = (float4 *)(out + row * C + g * 16);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) dst[qq] = make_float4(o[4 * qq], o[4 * qq + 1], o[4 * qq + 2], o[4 * qq + 3]);
+  }
+}
+
 int prep_groups(int64_t R, int64_t C) {
   const int64_t units = (R / 16) * ((C / 16 + 15) / 16);
   return (int)(units < 1 ? 1 : (units > kMaxGroups ? kMaxGroups : units));
@@ -182,6 +374,27 @@ fs4_status launch_vstate_encode(const float *v, int64_t R, int64_t C, const fs4_
   vstate_prep_kernel<<<g, kThreads, 0, s>>>(v, R, C, h, means, parts);
   if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
   return launch_quantize_encode(h, FS4_FP32, R, C, &q, nullptr, parts, g, s);
+}
+
+size_t mstate_encode_ws_bytes(int64_t R, int64_t C) { return vstate_encode_ws_bytes(R, C); }
+
+fs4_status launch_mstate_encode(const float *m, const uint32_t *rnd, int64_t R, int64_t C, const fs4_nvfp4 &q,
+                                void *ws, hipStream_t s) {
+  Carver c(ws);
+  float *h = (float *)c.take((size_t)(R * C) * sizeof(float));
+  uint32_t *parts = (uint32_t *)c.take((size_t)kMaxGroups * sizeof(uint32_t));
+  int64_t g = (R * (C / 16) + kThreads - 1) / kThreads;
+  g = g < 1 ? 1 : (g > kMaxGroups ? kMaxGroups : g);
+  mstate_prep_kernel<<<(unsigned)g, kThreads, 0, s>>>(m, R, C, h, parts);
+  mstate_encode_kernel<<<(unsigned)g, kThreads, 0, s>>>(h, R, C, rnd, parts, (int)g, q);
+  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+}
+
+fs4_status launch_mstate_decode(const fs4_nvfp4 &q, int64_t R, int64_t C, float *out, hipStream_t s) {
+  int64_t blocks = (R * (C / 16) + kThreads - 1) / kThreads;
+  blocks = blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks);
+  mstate_decode_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(q.codes, q.scales, q.tscale, R, C, out);
+  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 
 fs4_status launch_vstate_decode(const fs4_nvfp4 &q, const uint16_t *means, int64_t R, int64_t C, float *out,

@@ -116,6 +116,12 @@ fs4_status launch_vstate_encode(const float *v, int64_t R, int64_t C, const fs4_
                                 uint16_t *means, void *ws, hipStream_t s);
 fs4_status launch_vstate_decode(const fs4_nvfp4 &q, const uint16_t *means, int64_t R, int64_t C, float *out,
                                 hipStream_t s);
+// Q-AdamW first-moment codec: m fp32 [R][C] with one uint32 random word per
+// element -> NVFP4 view q (stochastic rounding, adaptive 4/6 scales); decode
+size_t mstate_encode_ws_bytes(int64_t R, int64_t C);
+fs4_status launch_mstate_encode(const float *m, const uint32_t *rnd, int64_t R, int64_t C, const fs4_nvfp4 &q,
+                                void *ws, hipStream_t s);
+fs4_status launch_mstate_decode(const fs4_nvfp4 &q, int64_t R, int64_t C, float *out, hipStream_t s);
 fs4_status launch_abs_quantile(const void *x, fs4_dtype dt, int64_t n, double q, float *out, void *ws,
                                hipStream_t s);
 

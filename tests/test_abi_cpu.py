@@ -256,3 +256,16 @@ def test_vstate_validation():
     assert dec(mu=A16 + 2) == ALIGN
     assert lib.fs4_vstate_encode_workspace_bytes(8192, 3072) >= 8192 * 3072 * 4
     assert lib.fs4_vstate_encode_workspace_bytes(8192, 3070) == 0
+
+
+def test_mstate_validation():
+    enc = lambda R=64, C=48, m=A16, rnd=A16 * 2, q="ok", wsb=1 << 30: lib.fs4_mstate_encode(
+        m, rnd, R, C, ctypes.byref(view(R, C) if q == "ok" else q), A16 * 16, wsb, None)
+    assert enc(R=8) == SHAPE
+    assert enc(m=None) == NULL
+    assert enc(rnd=None) == NULL
+    assert enc(rnd=A16 + 4) == ALIGN
+    assert enc(q=view(64, 16)) == SHAPE
+    assert enc(wsb=4) == WORKSPACE
+    assert lib.fs4_mstate_decode(ctypes.byref(view(64, 48)), 64, 48, None, None) == NULL
+    assert lib.fs4_mstate_decode(ctypes.byref(view(64, 48)), 64, 40, A16, None) == SHAPE

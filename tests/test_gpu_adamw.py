@@ -77,3 +77,43 @@ def test_3b_weight_state_sampled():
         h_hat = oracle.dequantize(ref)[0]
         s_hat = hadamard16(h_hat) + np.repeat(mu[r // 16], 16)
         assert np.array_equal(v_hat[r].view(np.uint32), (s_hat * s_hat).astype(np.float32).view(np.uint32)), r
+
+
+# ---- first moment ---------------------------------------------------------------
+from oracle.adamw import mstate_decode, mstate_encode
+
+
+def _m(shape, seed):
+    rng = np.random.default_rng(seed)
+    m = rng.standard_normal(shape) * np.exp(rng.uniform(-4, 1, (shape[0], 1))) * 1e-3
+    m[:, ::37] *= 30.0                                   # outlier columns the Hadamard mixing spreads
+    return m.astype(np.float32)
+
+
+def _words(shape, seed):
+    return np.random.default_rng(seed).integers(0, 2 ** 32, shape, dtype=np.uint64).astype(np.uint32)
+
+
+@pytest.mark.parametrize("R,C", [(16, 16), (48, 80), (272, 400), (1024, 3072)])
+def test_first_moment_bit_exact(R, C):
+    fs4 = need_gpu()
+    print_case(test="mstate", R=R, C=C)
+    m = _m((R, C), R + C)
+    w = _words((R, C), R * C)
+    q = fs4.mstate_encode(dev_f32(m), torch.from_numpy(w.view(np.int32)).cuda())
+    ref, _ = mstate_encode(m, w)
+    assert_view_equal(q, ref, "m")
+    got = fs4.mstate_decode(q).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), mstate_decode(ref).view(np.uint32))
+
+
+def test_first_moment_extreme_words():
+    """All-zero words round every off-grid magnitude up, all-ones words down,
+    as in the oracle."""
+    fs4 = need_gpu()
+    m = _m((64, 128), 5)
+    for fill in (0, 0xFFFFFFFF):
+        w = np.full(m.shape, fill, dtype=np.uint32)
+        q = fs4.mstate_encode(dev_f32(m), torch.from_numpy(w.view(np.int32)).cuda())
+        ref, _ = mstate_encode(m, w)
+        assert_view_equal(q, ref, "fill %x" % fill)
