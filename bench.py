@@ -27,8 +27,8 @@ through 12 copies so every call reads from HBM), the 5-step NVFP4
 Newton-Schulz on 3072 x 8192 (plain, and with the iterate clipped at its
 p99 as in the Q-Root variant), the two LoRA-SVD training-side calls at the
 3B shapes (the subspace projection of dU and dV, and the randomized-SVD
-realignment of the branch), the Q-AdamW second-moment codec's encode and
-decode on the same weight's state, and the CPU oracle timed on a bounded
+realignment of the branch), the Q-AdamW state codecs' encode and decode
+(second and first moment) on the same weight's state, and the CPU oracle timed on a bounded
 sample.
 
 The GEMM's HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
@@ -343,6 +343,17 @@ def main():
                                "encode_GBps": round(vbytes / (enc_ms * 1e-3) / 1e9, 1),
                                "decode_GBps": round(vbytes / (dec_ms * 1e-3) / 1e9, 1),
                                "algorithmic_bytes": int(vbytes)}
+        mst = torch.randn((N, K), device=dev, generator=torch.Generator(device=dev).manual_seed(11)) * 1e-3
+        words = torch.randint(-2 ** 31, 2 ** 31 - 1, (N, K), dtype=torch.int32, device=dev,
+                              generator=torch.Generator(device=dev).manual_seed(12))
+        qm = fs4.mstate_encode(mst, words)
+        menc_ms = time_calls(lambda: fs4.mstate_encode(mst, words), 20)
+        mdec_ms = time_calls(lambda: fs4.mstate_decode(qm), 20)
+        mbytes = N * K * (4 + 4 + 0.5 + 1 / 16)
+        out["adamw_mstate"] = {"workload": "m 8192x3072 fp32 + 32-bit random words -> NVFP4 (SR, 4/6 scales)",
+                               "encode_us": round(menc_ms * 1e3, 2), "decode_us": round(mdec_ms * 1e3, 2),
+                               "encode_GBps": round(mbytes / (menc_ms * 1e-3) / 1e9, 1),
+                               "decode_GBps": round(N * K * (4 + 0.5 + 1 / 16) / (mdec_ms * 1e-3) / 1e9, 1)}
 
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
