@@ -170,28 +170,35 @@ __global__ __launch_bounds__(kThreads) void vstate_decode_kernel(const uint8_t *
 //   y = |h| / (s_b s_t) exactly when u < (y - g_lo) / (g_hi - g_lo), with
 //   u = r 2^-32 from the caller's uint32 r (saturating at 6);
 //   decode: m_hat = fp32(H/4 dequant).
+// Encode is two passes over m: the amax of h, then h again (the same fp64
+// butterflies, so the same fp32 values) and its codes.
 
 __device__ inline double e2m1_mag(int i) {
   // 0, 0.5, 1, 1.5, 2, 3, 4, 6
   return i < 4 ? 0.5 * (double)i : (double)(2 << ((i - 4) >> 1)) * ((i & 1) ? 1.5 : 1.0);
 }
 
-// index of the E2M1 magnitude nearest to y >= 0 (ties to the even index)
-__device__ inline int e2m1_rne_idx(double y) {
+// Index of the E2M1 magnitude nearest to mag / step (ties to the even
+// index), decided as mag against midpoint * step: both products are exact in
+// fp64 (a midpoint has <= 3 significant bits, step = e4m3 * s_t <= 28), and
+// since mag has <= 24 significant bits a quotient that is not exactly a
+// midpoint lies at least ~2^-31 (relative) away from it, far beyond the
+// rounding of an fp64 quotient, so this is the decision the fp64 quotient
+// mag / step makes, without the division.
+__device__ inline int e2m1_rne_idx_scaled(double mag, double step) {
   int i = 0;
-  i += y > 0.25;    // 0 | 0.5   tie -> 0
-  i += y >= 0.75;   // 0.5 | 1   tie -> 1.0 (index 2)
-  i += y > 1.25;    // 1 | 1.5   tie -> 1.0
-  i += y >= 1.75;   // 1.5 | 2   tie -> 2.0 (index 4)
-  i += y > 2.5;     // 2 | 3     tie -> 2.0
-  i += y >= 3.5;    // 3 | 4     tie -> 4.0 (index 6)
-  i += y > 5.0;     // 4 | 6     tie -> 4.0
+  i += mag > 0.25 * step;    // 0 | 0.5   tie -> 0
+  i += mag >= 0.75 * step;   // 0.5 | 1   tie -> 1.0 (index 2)
+  i += mag > 1.25 * step;    // 1 | 1.5   tie -> 1.0
+  i += mag >= 1.75 * step;   // 1.5 | 2   tie -> 2.0 (index 4)
+  i += mag > 2.5 * step;     // 2 | 3     tie -> 2.0
+  i += mag >= 3.5 * step;    // 3 | 4     tie -> 4.0 (index 6)
+  i += mag > 5.0 * step;     // 4 | 6     tie -> 4.0
   return i;
 }
 
 __global__ __launch_bounds__(kThreads) void mstate_prep_kernel(const float *__restrict__ m, int64_t R,
-                                                               int64_t C, float *__restrict__ h,
-                                                               uint32_t *__restrict__ amax_parts) {
+                                                               int64_t C, uint32_t *__restrict__ amax_parts) {
   __shared__ uint32_t red[kThreads / 64];
   const int64_t total = R * (C / 16);
   float amax = 0.0f;
@@ -208,15 +215,8 @@ __global__ __launch_bounds__(kThreads) void mstate_prep_kernel(const float *__re
       y[4 * q + 3] = w.w;
     }
     fwht16(y);
-    float o[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      o[k] = (float)(y[k] * 0.25);
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(o[k]));
-    }
-    float4 *dst = (float4 *)(h + gi * 16);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    for (int k = 0; k < 16; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf((float)(y[k] * 0.25)));
   }
   uint32_t ub = __builtin_bit_cast(uint32_t, amax);
 #pragma unroll
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void mstate_prep_kernel(const float *__re
   }
 }
 
-__global__ __launch_bounds__(kThreads) void mstate_encode_kernel(const float *__restrict__ h, int64_t R, int64_t C,
+__global__ __launch_bounds__(kThreads) void mstate_encode_kernel(const float *__restrict__ m, int64_t R, int64_t C,
                                                                  const uint32_t *__restrict__ rnd,
                                                                  const uint32_t *__restrict__ amax_parts,
                                                                  int nparts, fs4_nvfp4 q) {
@@ -255,16 +255,21 @@ __global__ __launch_bounds__(kThreads) void mstate_encode_kernel(const float *__
   const int64_t groups_c = C / 16, total = R * groups_c;
   for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < total;
        gi += (int64_t)gridDim.x * kThreads) {
-    const float4 *src = (const float4 *)(h + gi * 16);
-    float x[16];
+    // h of this group, recomputed from m exactly as the first pass did
+    const float4 *src = (const float4 *)(m + gi * 16);
+    double y[16];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const float4 w = src[qq];
-      x[4 * qq] = w.x;
-      x[4 * qq + 1] = w.y;
-      x[4 * qq + 2] = w.z;
-      x[4 * qq + 3] = w.w;
+      y[4 * qq] = w.x;
+      y[4 * qq + 1] = w.y;
+      y[4 * qq + 2] = w.z;
+      y[4 * qq + 3] = w.w;
     }
+    fwht16(y);
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = (float)(y[k] * 0.25);
     double mag[16], amax_b = 0.0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void mstate_encode_kernel(const float *__
         double tot = 0.0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const double val = step > 0.0 ? e2m1_mag(e2m1_rne_idx(mag[k] / step)) * step : 0.0;
+          const double val = step > 0.0 ? e2m1_mag(e2m1_rne_idx_scaled(mag[k], step)) * step : 0.0;
           const double d = mag[k] - val;
           tot = tot + d * d;
         }
@@ -305,8 +310,11 @@ __global__ __launch_bounds__(kThreads) void mstate_encode_kernel(const float *__
 #pragma unroll
         for (int g = 1; g < 8; ++g) lo += e2m1_mag(g) <= y;     // largest magnitude <= y
         if (lo < 7) {
-          const double glo = e2m1_mag(lo), ghi = e2m1_mag(lo + 1);
-          const double p = (y - glo) / (ghi - glo);
+          // the gap to the next magnitude is 0.5, 1 or 2: multiplying by its
+          // inverse is the division, exactly
+          const double glo = e2m1_mag(lo);
+          const double inv_gap = lo < 4 ? 2.0 : (lo < 6 ? 1.0 : 0.5);
+          const double p = (y - glo) * inv_gap;
           const double u = (double)rr[k] * 0x1p-32;
           idx = (uint32_t)(u < p ? lo + 1 : lo);
         } else {
@@ -376,17 +384,16 @@ fs4_status launch_vstate_encode(const float *v, int64_t R, int64_t C, const fs4_
   return launch_quantize_encode(h, FS4_FP32, R, C, &q, nullptr, parts, g, s);
 }
 
-size_t mstate_encode_ws_bytes(int64_t R, int64_t C) { return vstate_encode_ws_bytes(R, C); }
+size_t mstate_encode_ws_bytes(int64_t, int64_t) { return (size_t)kMaxGroups * sizeof(uint32_t); }
 
 fs4_status launch_mstate_encode(const float *m, const uint32_t *rnd, int64_t R, int64_t C, const fs4_nvfp4 &q,
                                 void *ws, hipStream_t s) {
-  Carver c(ws);
-  float *h = (float *)c.take((size_t)(R * C) * sizeof(float));
-  uint32_t *parts = (uint32_t *)c.take((size_t)kMaxGroups * sizeof(uint32_t));
+  uint32_t *parts = (uint32_t *)ws;
   int64_t g = (R * (C / 16) + kThreads - 1) / kThreads;
   g = g < 1 ? 1 : (g > kMaxGroups ? kMaxGroups : g);
-  mstate_prep_kernel<<<(unsigned)g, kThreads, 0, s>>>(m, R, C, h, parts);
-  mstate_encode_kernel<<<(unsigned)g, kThreads, 0, s>>>(h, R, C, rnd, parts, (int)g, q);
+  // pass 1: amax of h; pass 2: h again from m, then the codes
+  mstate_prep_kernel<<<(unsigned)g, kThreads, 0, s>>>(m, R, C, parts);
+  mstate_encode_kernel<<<(unsigned)g, kThreads, 0, s>>>(m, R, C, rnd, parts, (int)g, q);
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 
