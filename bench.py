@@ -1,7 +1,7 @@
 """Benchmark of the NVFP4 linear-projection hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
-    python bench.py --only {gemm,quantizer,copy,lora} (one leg alone, for profilers)
+    python bench.py --only {gemm,quantizer,copy,lora,adamw} (one leg alone, for profilers)
 
 One step is one pass of the whole hot path over one batch of synthetic input
 at the 3B-shape projection (X 8192 x 3072 bf16, W 8192 x 3072 with a rank-32
@@ -84,7 +84,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-extra", action="store_true", help="skip the quantizer/NS/roofline legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gemm", "quantizer", "copy", "lora"],
+    ap.add_argument("--only", choices=["gemm", "quantizer", "copy", "lora", "adamw"],
                     help="run one leg alone (for counter runs under a profiler) and exit")
     return ap.parse_args()
 
@@ -288,8 +288,37 @@ def main():
                                "us_per_step_every_2048": round(ra_ms * 1e3 / 2048, 2)}
         return out
 
+    def adamw_legs():
+        out = {}
+        # ---- Q-AdamW second-moment codec on the 8192 x 3072 weight's state ---
+        vst = (torch.randn((N, K), device=dev, generator=torch.Generator(device=dev).manual_seed(10)) ** 2) * 1e-8
+        qv, mv = fs4.vstate_encode(vst)
+        enc_ms = time_calls(lambda: fs4.vstate_encode(vst), 20)
+        dec_ms = time_calls(lambda: fs4.vstate_decode(qv, mv), 20)
+        vbytes = N * K * (4 + 0.5 + 1 / 16) + (N // 16) * (K // 16) * 2
+        out["adamw_vstate"] = {"workload": "v 8192x3072 fp32 <-> NVFP4 + BF16 16x16 tile means",
+                               "encode_us": round(enc_ms * 1e3, 2), "decode_us": round(dec_ms * 1e3, 2),
+                               "encode_GBps": round(vbytes / (enc_ms * 1e-3) / 1e9, 1),
+                               "decode_GBps": round(vbytes / (dec_ms * 1e-3) / 1e9, 1),
+                               "algorithmic_bytes": int(vbytes)}
+        mst = torch.randn((N, K), device=dev, generator=torch.Generator(device=dev).manual_seed(11)) * 1e-3
+        words = torch.randint(-2 ** 31, 2 ** 31 - 1, (N, K), dtype=torch.int32, device=dev,
+                              generator=torch.Generator(device=dev).manual_seed(12))
+        qm = fs4.mstate_encode(mst, words)
+        menc_ms = time_calls(lambda: fs4.mstate_encode(mst, words), 20)
+        mdec_ms = time_calls(lambda: fs4.mstate_decode(qm), 20)
+        mbytes = N * K * (4 + 4 + 0.5 + 1 / 16)
+        out["adamw_mstate"] = {"workload": "m 8192x3072 fp32 + 32-bit random words -> NVFP4 (SR, 4/6 scales)",
+                               "encode_us": round(menc_ms * 1e3, 2), "decode_us": round(mdec_ms * 1e3, 2),
+                               "encode_GBps": round(mbytes / (menc_ms * 1e-3) / 1e9, 1),
+                               "decode_GBps": round(N * K * (4 + 0.5 + 1 / 16) / (mdec_ms * 1e-3) / 1e9, 1)}
+        return out
+
     if a.only == "lora":
         print(json.dumps({"only": "lora", **lora_legs()}), flush=True)
+        return
+    if a.only == "adamw":
+        print(json.dumps({"only": "adamw", **adamw_legs()}), flush=True)
         return
 
     for _ in range(a.warmup):
@@ -332,28 +361,7 @@ def main():
 
         out.update(lora_legs())
 
-        # ---- Q-AdamW second-moment codec on the 8192 x 3072 weight's state ---
-        vst = (torch.randn((N, K), device=dev, generator=torch.Generator(device=dev).manual_seed(10)) ** 2) * 1e-8
-        qv, mv = fs4.vstate_encode(vst)
-        enc_ms = time_calls(lambda: fs4.vstate_encode(vst), 20)
-        dec_ms = time_calls(lambda: fs4.vstate_decode(qv, mv), 20)
-        vbytes = N * K * (4 + 0.5 + 1 / 16) + (N // 16) * (K // 16) * 2
-        out["adamw_vstate"] = {"workload": "v 8192x3072 fp32 <-> NVFP4 + BF16 16x16 tile means",
-                               "encode_us": round(enc_ms * 1e3, 2), "decode_us": round(dec_ms * 1e3, 2),
-                               "encode_GBps": round(vbytes / (enc_ms * 1e-3) / 1e9, 1),
-                               "decode_GBps": round(vbytes / (dec_ms * 1e-3) / 1e9, 1),
-                               "algorithmic_bytes": int(vbytes)}
-        mst = torch.randn((N, K), device=dev, generator=torch.Generator(device=dev).manual_seed(11)) * 1e-3
-        words = torch.randint(-2 ** 31, 2 ** 31 - 1, (N, K), dtype=torch.int32, device=dev,
-                              generator=torch.Generator(device=dev).manual_seed(12))
-        qm = fs4.mstate_encode(mst, words)
-        menc_ms = time_calls(lambda: fs4.mstate_encode(mst, words), 20)
-        mdec_ms = time_calls(lambda: fs4.mstate_decode(qm), 20)
-        mbytes = N * K * (4 + 4 + 0.5 + 1 / 16)
-        out["adamw_mstate"] = {"workload": "m 8192x3072 fp32 + 32-bit random words -> NVFP4 (SR, 4/6 scales)",
-                               "encode_us": round(menc_ms * 1e3, 2), "decode_us": round(mdec_ms * 1e3, 2),
-                               "encode_GBps": round(mbytes / (menc_ms * 1e-3) / 1e9, 1),
-                               "decode_GBps": round(N * K * (4 + 0.5 + 1 / 16) / (mdec_ms * 1e-3) / 1e9, 1)}
+        out.update(adamw_legs())
 
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline()

@@ -17,6 +17,8 @@
 // Encode is two launches: vstate_prep_kernel writes h (fp32 workspace), the
 // BF16 means and per-workgroup amax partials of h; the quantizer's encode
 // pass then quantizes h row-wise.  Decode is one launch.
+#include <atomic>
+
 #include "fs4_common.h"
 
 namespace fs4 {
@@ -255,6 +257,10 @@ __global__ __launch_bounds__(kThreads) void mstate_encode_kernel(const float *__
   const int64_t groups_c = C / 16, total = R * groups_c;
   for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < total;
        gi += (int64_t)gridDim.x * kThreads) {
+    // the random words are loaded first, so that their latency hides behind
+    // the transform and the scale choice
+    const uint4 rw0 = *(const uint4 *)(rnd + gi * 16), rw1 = *(const uint4 *)(rnd + gi * 16 + 4);
+    const uint4 rw2 = *(const uint4 *)(rnd + gi * 16 + 8), rw3 = *(const uint4 *)(rnd + gi * 16 + 12);
     // h of this group, recomputed from m exactly as the first pass did
     const float4 *src = (const float4 *)(m + gi * 16);
     double y[16];
@@ -296,8 +302,6 @@ __global__ __launch_bounds__(kThreads) void mstate_encode_kernel(const float *__
       sb = err[1] < err[0] ? s4 : s6;
     }
     const double step = (double)e4m3_to_float(sb) * st;
-    const uint4 rw0 = *(const uint4 *)(rnd + gi * 16), rw1 = *(const uint4 *)(rnd + gi * 16 + 4);
-    const uint4 rw2 = *(const uint4 *)(rnd + gi * 16 + 8), rw3 = *(const uint4 *)(rnd + gi * 16 + 12);
     const uint32_t rr[16] = {rw0.x, rw0.y, rw0.z, rw0.w, rw1.x, rw1.y, rw1.z, rw1.w,
                              rw2.x, rw2.y, rw2.z, rw2.w, rw3.x, rw3.y, rw3.z, rw3.w};
     uint32_t lo32 = 0, hi32 = 0;
@@ -386,6 +390,30 @@ fs4_status launch_vstate_encode(const float *v, int64_t R, int64_t C, const fs4_
 
 size_t mstate_encode_ws_bytes(int64_t, int64_t) { return (size_t)kMaxGroups * sizeof(uint32_t); }
 
+namespace {
+// Workgroups of the encode kernel that the current device holds at once (its
+// register use allows three waves per SIMD).  A grid of that size runs the
+// grid-stride loop in a single batch, where a larger one would leave a
+// partial second batch on a fraction of the CUs.  Asked once per device.
+int mstate_encode_resident() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kMaxGroups;
+  int r = cached[dev].load(std::memory_order_relaxed);
+  if (r == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, mstate_encode_kernel, kThreads, 0) == hipSuccess &&
+        cus > 0 && per > 0)
+      r = cus * per;
+    else
+      r = kMaxGroups;
+    cached[dev].store(r, std::memory_order_relaxed);
+  }
+  return r;
+}
+}  // namespace
+
 fs4_status launch_mstate_encode(const float *m, const uint32_t *rnd, int64_t R, int64_t C, const fs4_nvfp4 &q,
                                 void *ws, hipStream_t s) {
   uint32_t *parts = (uint32_t *)ws;
@@ -393,7 +421,10 @@ fs4_status launch_mstate_encode(const float *m, const uint32_t *rnd, int64_t R, 
   g = g < 1 ? 1 : (g > kMaxGroups ? kMaxGroups : g);
   // pass 1: amax of h; pass 2: h again from m, then the codes
   mstate_prep_kernel<<<(unsigned)g, kThreads, 0, s>>>(m, R, C, parts);
-  mstate_encode_kernel<<<(unsigned)g, kThreads, 0, s>>>(m, R, C, rnd, parts, (int)g, q);
+  int64_t ge = (R * (C / 16) + kThreads - 1) / kThreads;
+  const int64_t res = mstate_encode_resident();
+  ge = ge < 1 ? 1 : (ge > res ? res : ge);
+  mstate_encode_kernel<<<(unsigned)ge, kThreads, 0, s>>>(m, R, C, rnd, parts, (int)g, q);
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 
