@@ -176,8 +176,21 @@ __global__ __launch_bounds__(kThreads) void vstate_decode_kernel(const uint8_t *
 // butterflies, so the same fp32 values) and its codes.
 
 __device__ inline double e2m1_mag(int i) {
-  // 0, 0.5, 1, 1.5, 2, 3, 4, 6
-  return i < 4 ? 0.5 * (double)i : (double)(2 << ((i - 4) >> 1)) * ((i & 1) ? 1.5 : 1.0);
+  // 0, 0.5, 1, 1.5, 2, 3, 4, 6: in half units 0 1 2 3 4 6 8 12
+  const int h = i < 4 ? i : ((2 | (i & 1)) << ((i >> 1) - 1));
+  return 0.5 * (double)h;
+}
+
+// Index of the largest E2M1 magnitude <= y, for y >= 0 (an fp64 value): 0
+// below 0.5, 1 below 1; from 1 on the magnitudes are the values with one
+// mantissa bit, so the index follows from y's exponent e and its top mantissa
+// bit b as 2 + 2e + b, capped at 7.
+__device__ inline int e2m1_floor_idx(double y) {
+  const uint32_t yh = (uint32_t)(__builtin_bit_cast(uint64_t, y) >> 32);
+  if (yh < 0x3FE00000u) return 0;
+  if (yh < 0x3FF00000u) return 1;
+  const int i = 2 + 2 * ((int)(yh >> 20) - 1023) + (int)((yh >> 19) & 1u);
+  return i < 7 ? i : 7;
 }
 
 // Index of the E2M1 magnitude nearest to mag / step (ties to the even
@@ -310,9 +323,7 @@ __global__ __launch_bounds__(kThreads) void mstate_encode_kernel(const float *__
       uint32_t idx = 0;
       if (step > 0.0) {
         const double y = mag[k] / step;
-        int lo = 0;
-#pragma unroll
-        for (int g = 1; g < 8; ++g) lo += e2m1_mag(g) <= y;     // largest magnitude <= y
+        const int lo = e2m1_floor_idx(y);
         if (lo < 7) {
           // the gap to the next magnitude is 0.5, 1 or 2: multiplying by its
           // inverse is the division, exactly
