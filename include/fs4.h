@@ -108,6 +108,15 @@ fs4_status fs4_gemm_nt(const fs4_nvfp4 *A, const fs4_nvfp4 *B, float alpha,
                        void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * fs4_gemm_plan — introspection, launches nothing: the tile configuration
+ * fs4_gemm_nt (and the products of fs4_linear_fwd / fs4_linear_bwd) take for
+ * an M x N x K product.  out (host, 4 entries): tile rows, tile columns,
+ * tiles, k-splits of the last round's tiles (1: none).
+ * Errors: FS4_ERR_NULL (out), FS4_ERR_SHAPE (negative dims, K % 16 != 0).
+ */
+fs4_status fs4_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t *out);
+
+/* ---------------------------------------------------------------------------
  * fs4_linear_fwd — LoRA-SVD projection forward, [FS4 §2.1]: the weight is
  * W = R + beta U V with U = L2 [N][r], V = L1 [r][K] kept in BF16 and the
  * residual R held in NVFP4:
@@ -173,6 +182,16 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
                              float a, float b, float c, int normalize, float eps, double clip_q,
                              float *X_out, float *trace_X, float *trace_A, float *trace_B,
                              void *ws, size_t ws_bytes, void *stream);
+
+/* fs4_newton_schulz_plan — introspection, launches nothing: the tile plans of
+ * the three products of one fs4_newton_schulz step on an m x n iterate, in
+ * the order A = Q(X) Q(X)^T (m x m x n, symmetric), A^2 (m x m x m,
+ * symmetric), and the update, computed transposed (n x m x m).  out (host, 12
+ * entries): per product as fs4_gemm_plan's four (symmetric products count the
+ * upper triangle's tiles; a split last round has k-splits > 1).
+ * Errors: FS4_ERR_NULL, FS4_ERR_SHAPE (as fs4_newton_schulz).
+ */
+fs4_status fs4_newton_schulz_plan(int64_t m, int64_t n, int64_t *out);
 
 /* ---------------------------------------------------------------------------
  * fs4_abs_quantile — the nearest-rank q-quantile of |x| for the outlier

@@ -20,6 +20,7 @@ Names follow the C ABI in include/fs4.h:
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 from dataclasses import dataclass
@@ -51,7 +52,7 @@ EXPORTS = [
     "fs4_quantize_clipped_workspace_bytes", "fs4_quantize_clipped",
     "fs4_vstate_encode_workspace_bytes", "fs4_vstate_encode", "fs4_vstate_decode",
     "fs4_mstate_encode_workspace_bytes", "fs4_mstate_encode", "fs4_mstate_decode",
-    "fs4_workspace_bytes", "fs4_status_str", "fs4_version",
+    "fs4_workspace_bytes", "fs4_status_str", "fs4_version", "fs4_gemm_plan", "fs4_newton_schulz_plan",
 ]
 
 
@@ -107,6 +108,8 @@ _sig("fs4_newton_schulz", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_
                                          ctypes.c_int, _F, ctypes.c_double, _P, _P, _P, _P, _P, _SZ, _P])
 _sig("fs4_abs_quantile_workspace_bytes", _SZ, [_I64])
 _sig("fs4_abs_quantile", ctypes.c_int, [_P, ctypes.c_int, _I64, ctypes.c_double, _P, _P, _SZ, _P])
+_sig("fs4_gemm_plan", ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(_I64)])
+_sig("fs4_newton_schulz_plan", ctypes.c_int, [_I64, _I64, ctypes.POINTER(_I64)])
 _sig("fs4_quantize_clipped_workspace_bytes", _SZ, [_I64, _I64])
 _sig("fs4_quantize_clipped", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_double, _VP, _VP, _P,
                                             _SZ, _P])
@@ -139,6 +142,68 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+# ---- argument checks ------------------------------------------------------------
+# The C ABI sees raw device pointers and the sizes passed beside them, never
+# the buffers' extents: a tensor of the wrong dtype or shape would make a
+# kernel read or write past its allocation.  Every tensor is therefore checked
+# here, before any call into the library.
+
+_U32_LIKE = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
+def _tensor(t, name: str, dtypes, shape=None, device=None) -> torch.Tensor:
+    """Checks one tensor argument: dtype, exact shape, contiguity, a CUDA
+    device (the same one as ``device`` when given)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor, got %s" % (name, type(t).__name__))
+    if t.dtype not in dtypes:
+        raise TypeError("%s must have dtype %s, got %s" % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(int(d) for d in shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a CUDA device, got %s" % (name, t.device))
+    if device is not None and t.device != torch.device(device):
+        raise ValueError("%s is on %s, the call runs on %s" % (name, t.device, device))
+    return t
+
+
+def _opt_tensor(t, name, dtypes, shape, device):
+    return None if t is None else _tensor(t, name, dtypes, shape, device)
+
+
+def _matrix(t, name: str, dtypes, device=None):
+    """A 2-D tensor of any shape; returns (rows, cols)."""
+    if isinstance(t, torch.Tensor) and t.dim() != 2:
+        raise ValueError("%s must be 2-D, got %d dimensions" % (name, t.dim()))
+    _tensor(t, name, dtypes, None, device)
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _view(v, name: str, rows=None, cols=None, device=None):
+    """Checks an NVFP4 view's three tensors against its rows/cols (and the
+    expected rows/cols when given)."""
+    if not isinstance(v, NVFP4):
+        raise TypeError("%s must be an NVFP4 view, got %s" % (name, type(v).__name__))
+    if rows is not None and v.rows != rows or cols is not None and v.cols != cols:
+        raise ValueError("%s must be a %s x %s view, got %d x %d" % (name, rows, cols, v.rows, v.cols))
+    if v.rows < 0 or v.cols < 0 or v.cols % 16:
+        raise ValueError("%s: cols must be a non-negative multiple of 16, got %d x %d" % (name, v.rows, v.cols))
+    empty = v.rows == 0 or v.cols == 0     # nothing is read or written but the tensor scale
+    _tensor(v.codes, name + ".codes", (torch.uint8,), None if empty else (v.rows, v.cols // 2), device)
+    _tensor(v.scales, name + ".scales", (torch.uint8,), None if empty else (v.rows, v.cols // 16), device)
+    _tensor(v.tscale, name + ".tscale", (torch.float32,), None, v.codes.device)
+    if v.tscale.numel() < 1:
+        raise ValueError("%s.tscale must hold one float" % name)
+    return v
+
+
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_FLOAT = (torch.bfloat16, torch.float32)
+
+
 _WS = {}
 
 
@@ -150,6 +215,29 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws
+
+
+def release_workspaces() -> None:
+    """Waits for the work queued on the cached workspaces' devices, then
+    drops the workspaces and returns torch's cached device memory.  Runs at
+    interpreter exit, so that every device buffer is released while the HIP
+    runtime (and any profiler attached to it) is still up, rather than during
+    the C-level teardown that follows."""
+    if not _WS:
+        return
+    devices = {k[0] for k in _WS}
+    try:
+        for d in devices:
+            torch.cuda.synchronize(torch.device(d))
+    finally:
+        _WS.clear()
+        try:
+            torch.cuda.empty_cache()
+        except RuntimeError:
+            pass
+
+
+atexit.register(release_workspaces)
 
 
 @dataclass
@@ -187,9 +275,7 @@ def quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, out_ro
              out_col: Optional[NVFP4] = None):
     """NVFP4-quantize a 2-D bf16/fp32 CUDA tensor; returns (row view, col view)
     (None for a layout not asked for).  Both views share one tscale tensor."""
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("quantize takes a contiguous 2-D tensor")
-    rows, cols = x.shape
+    rows, cols = _matrix(x, "x", _FLOAT)
     dev = x.device
     ts = None
     if rowwise and out_row is None:
@@ -197,6 +283,10 @@ def quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, out_ro
         ts = out_row.tscale
     if colwise and out_col is None:
         out_col = NVFP4.empty(cols, rows, dev, ts)
+    if rowwise:
+        _view(out_row, "out_row", rows, cols, dev)
+    if colwise:
+        _view(out_col, "out_col", cols, rows, dev)
     rv = out_row.c() if rowwise else None
     cv = out_col.c() if colwise else None
     nbytes = _lib.fs4_quantize_workspace_bytes(rows, cols)
@@ -211,8 +301,12 @@ def quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, out_ro
 def gemm_nt(A: NVFP4, B: NVFP4, alpha: float = 1.0, E: Optional[torch.Tensor] = None, beta_e: float = 0.0,
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C = alpha s_tA s_tB A_hat B_hat^T + beta_e E (fp32 [A.rows, B.rows])."""
+    _view(A, "A")
     dev = A.codes.device
+    _view(B, "B", None, A.cols, dev)
+    _opt_tensor(E, "E", _F32, (A.rows, B.rows), dev)
     C = out if out is not None else torch.empty((A.rows, B.rows), dtype=torch.float32, device=dev)
+    _tensor(C, "out", _F32, (A.rows, B.rows), dev)
     av, bv = A.c(), B.c()
     _check(_lib.fs4_gemm_nt(ctypes.byref(av), ctypes.byref(bv), alpha, _ptr(E), beta_e, C.data_ptr(),
                             None, 0, _stream(dev)), "fs4_gemm_nt")
@@ -229,11 +323,19 @@ class LinearFwd:
 def linear_fwd(X: torch.Tensor, R_row: NVFP4, U: Optional[torch.Tensor], V: Optional[torch.Tensor],
                beta: float = 1.0, save_for_backward: bool = True, out: Optional[torch.Tensor] = None) -> LinearFwd:
     """Y = Q(X) Q(R)^T + beta (X V^T) U^T.  X bf16 [M, K]; U bf16 [N, r]; V bf16 [r, K]."""
-    M, K = X.shape
-    N = R_row.rows
-    r = 0 if U is None else U.shape[1]
+    M, K = _matrix(X, "X", _BF16)
     dev = X.device
+    _view(R_row, "R_row", None, K, dev)
+    N = R_row.rows
+    if (U is None) != (V is None):
+        raise ValueError("U and V are given together or not at all")
+    r = 0
+    if U is not None:
+        r = _matrix(U, "U", _BF16, dev)[1]
+        _tensor(U, "U", _BF16, (N, r), dev)
+        _tensor(V, "V", _BF16, (r, K), dev)
     Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    _tensor(Y, "out", _F32, (M, N), dev)
     T = torch.empty((M, r), dtype=torch.float32, device=dev) if (save_for_backward and r > 0) else None
     X_col = NVFP4.empty(K, M, dev) if save_for_backward else None
     rv = R_row.c()
@@ -259,10 +361,21 @@ def linear_bwd(dY: torch.Tensor, X: Optional[torch.Tensor], X_col: NVFP4, R_col:
                beta: float = 1.0, need_factor_grads: bool = True) -> LinearBwd:
     """dX = Q(dY) Q(R^T)^T + beta (dY U) V; dW = Q(dY^T) Q(X^T)^T;
     dU = beta dY^T T; dV = beta (dY U)^T X."""
-    M, N = dY.shape
-    K = X_col.rows
-    r = 0 if U is None else U.shape[1]
+    M, N = _matrix(dY, "dY", _BF16)
     dev = dY.device
+    _view(X_col, "X_col", None, M, dev)
+    K = X_col.rows
+    _view(R_col, "R_col", K, N, dev)
+    if (U is None) != (V is None):
+        raise ValueError("U and V are given together or not at all")
+    r = 0
+    if U is not None:
+        r = _matrix(U, "U", _BF16, dev)[1]
+        _tensor(U, "U", _BF16, (N, r), dev)
+        _tensor(V, "V", _BF16, (r, K), dev)
+        _tensor(T, "T", _F32, (M, r), dev)
+    if X is not None or (r > 0 and need_factor_grads):
+        _tensor(X, "X", _BF16, (M, K), dev)
     dX = torch.empty((M, K), dtype=torch.float32, device=dev)
     dW = torch.empty((N, K), dtype=torch.float32, device=dev)
     dU = torch.empty((N, r), dtype=torch.float32, device=dev) if (need_factor_grads and r > 0) else None
@@ -283,9 +396,10 @@ def newton_schulz(G: torch.Tensor, steps: int = 5, abc=MUON_ABC, normalize: bool
     trace=True (X, trace_X [steps+1, m, n], trace_A [steps, m, m],
     trace_B [steps, m, m]).  clip_q (e.g. 0.99): clip each quantized copy
     of the iterate at that quantile of its magnitudes (0: off)."""
-    m, n = G.shape
+    m, n = _matrix(G, "G", _FLOAT)
     dev = G.device
     X = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=dev)
+    _tensor(X, "out", _F32, (m, n), dev)
     tX = torch.empty((steps + 1, m, n), dtype=torch.float32, device=dev) if trace else None
     tA = torch.empty((max(steps, 1), m, m), dtype=torch.float32, device=dev) if trace else None
     tB = torch.empty((max(steps, 1), m, m), dtype=torch.float32, device=dev) if trace else None
@@ -306,9 +420,12 @@ def lora_project(U: torch.Tensor, V: torch.Tensor, dU: Optional[torch.Tensor] = 
     dU <- Q_U Q_U^T dU, dV <- dV Q_V Q_V^T (Q_U = CholQR(U), Q_V = CholQR(V^T)).
     U bf16 [N, r], V bf16 [r, K]; dU fp32 [N, r], dV fp32 [r, K] (either may
     be None).  Returns (dU, dV)."""
-    N, r = U.shape
-    K = V.shape[1]
+    N, r = _matrix(U, "U", _BF16)
     dev = U.device
+    K = _matrix(V, "V", _BF16, dev)[1]
+    _tensor(V, "V", _BF16, (r, K), dev)
+    _opt_tensor(dU, "dU", _F32, (N, r), dev)
+    _opt_tensor(dV, "dV", _F32, (r, K), dev)
     nbytes = _lib.fs4_lora_project_workspace_bytes(N, K, r)
     ws = _workspace(nbytes, dev)
     _check(_lib.fs4_lora_project(U.data_ptr(), V.data_ptr(), N, K, r, _ptr(dU), _ptr(dV), ws.data_ptr(),
@@ -321,10 +438,13 @@ def lora_realign(U: torch.Tensor, V: torch.Tensor, R: torch.Tensor, Omega: torch
     """Randomized-SVD realignment of W = beta U V + R, in place: U bf16
     [N, r], V bf16 [r, K], R fp32 [N, K]; Omega fp32 [l, K] Gaussian test
     vectors (r <= l <= 64).  Returns sigma, the r leading singular values."""
-    N, r = U.shape
-    K = V.shape[1]
-    l = Omega.shape[0]
+    N, r = _matrix(U, "U", _BF16)
     dev = U.device
+    K = _matrix(V, "V", _BF16, dev)[1]
+    _tensor(V, "V", _BF16, (r, K), dev)
+    _tensor(R, "R", _F32, (N, K), dev)
+    l = _matrix(Omega, "Omega", _F32, dev)[0]
+    _tensor(Omega, "Omega", _F32, (l, K), dev)
     sigma = torch.empty(r, dtype=torch.float32, device=dev)
     nbytes = _lib.fs4_lora_realign_workspace_bytes(N, K, l)
     ws = _workspace(nbytes, dev)
@@ -336,6 +456,7 @@ def lora_realign(U: torch.Tensor, V: torch.Tensor, R: torch.Tensor, Omega: torch
 
 def abs_quantile(x: torch.Tensor, q: float) -> torch.Tensor:
     """The nearest-rank q-quantile of |x| (a 1-element fp32 tensor)."""
+    _tensor(x, "x", _FLOAT)
     out = torch.empty(1, dtype=torch.float32, device=x.device)
     ws = _workspace(_lib.fs4_abs_quantile_workspace_bytes(x.numel()), x.device)
     _check(_lib.fs4_abs_quantile(x.data_ptr(), _dtype_code(x), x.numel(), q, out.data_ptr(), ws.data_ptr(),
@@ -345,7 +466,7 @@ def abs_quantile(x: torch.Tensor, q: float) -> torch.Tensor:
 
 def quantize_clipped(x: torch.Tensor, q: float, rowwise: bool = True, colwise: bool = True):
     """quantize() of x clipped at the nearest-rank q-quantile of |x|."""
-    rows, cols = x.shape
+    rows, cols = _matrix(x, "x", _FLOAT)
     dev = x.device
     orow = NVFP4.empty(rows, cols, dev) if rowwise else None
     ocol = NVFP4.empty(cols, rows, dev, tscale=orow.tscale if orow is not None else None) if colwise else None
@@ -362,7 +483,7 @@ def quantize_clipped(x: torch.Tensor, q: float, rowwise: bool = True, colwise: b
 def vstate_encode(v: torch.Tensor):
     """Q-AdamW second-moment codec: fp32 v [R, C] -> (NVFP4 view of the
     transformed residual, BF16 tile means [R/16, C/16])."""
-    R, C = v.shape
+    R, C = _matrix(v, "v", _F32)
     dev = v.device
     q = NVFP4.empty(R, C, dev)
     means = torch.empty((R // 16, C // 16), dtype=torch.bfloat16, device=dev)
@@ -375,6 +496,8 @@ def vstate_encode(v: torch.Tensor):
 
 def vstate_decode(q: NVFP4, means: torch.Tensor) -> torch.Tensor:
     """The fp32 second moment back from vstate_encode's outputs."""
+    _view(q, "q")
+    _tensor(means, "means", _BF16, (q.rows // 16, q.cols // 16), q.codes.device)
     out = torch.empty((q.rows, q.cols), dtype=torch.float32, device=means.device)
     qv = q.c()
     _check(_lib.fs4_vstate_decode(ctypes.byref(qv), means.data_ptr(), q.rows, q.cols, out.data_ptr(),
@@ -385,7 +508,8 @@ def vstate_decode(q: NVFP4, means: torch.Tensor) -> torch.Tensor:
 def mstate_encode(m: torch.Tensor, rnd: torch.Tensor) -> NVFP4:
     """Q-AdamW first-moment codec: fp32 m [R, C] and one random 32-bit word
     per element (int32 or uint32 tensor, bits used as given) -> NVFP4 view."""
-    R, C = m.shape
+    R, C = _matrix(m, "m", _F32)
+    _tensor(rnd, "rnd", _U32_LIKE, (R, C), m.device)
     dev = m.device
     q = NVFP4.empty(R, C, dev)
     qv = q.c()
@@ -396,11 +520,28 @@ def mstate_encode(m: torch.Tensor, rnd: torch.Tensor) -> NVFP4:
 
 
 def mstate_decode(q: NVFP4) -> torch.Tensor:
+    _view(q, "q")
     out = torch.empty((q.rows, q.cols), dtype=torch.float32, device=q.codes.device)
     qv = q.c()
     _check(_lib.fs4_mstate_decode(ctypes.byref(qv), q.rows, q.cols, out.data_ptr(), _stream(q.codes.device)),
            "fs4_mstate_decode")
     return out
+
+
+def gemm_plan(M: int, N: int, K: int) -> dict:
+    """The tile plan the GEMM launcher picks for an M x N x K product."""
+    out = (_I64 * 4)()
+    _check(_lib.fs4_gemm_plan(M, N, K, out), "fs4_gemm_plan")
+    return {"tile": (out[0], out[1]), "tiles": out[2], "splits": out[3]}
+
+
+def newton_schulz_plan(m: int, n: int) -> dict:
+    """The tile plans of one Newton-Schulz step's products A, A^2 and the
+    (transposed) update on an m x n iterate."""
+    out = (_I64 * 12)()
+    _check(_lib.fs4_newton_schulz_plan(m, n, out), "fs4_newton_schulz_plan")
+    return {name: {"tile": (out[4 * i], out[4 * i + 1]), "tiles": out[4 * i + 2], "splits": out[4 * i + 3]}
+            for i, name in enumerate(("A", "A2", "update"))}
 
 
 def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> int:
@@ -410,4 +551,5 @@ def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> i
 __all__ = ["NVFP4", "quantize", "gemm_nt", "linear_fwd", "LinearFwd", "linear_bwd", "LinearBwd",
            "newton_schulz", "lora_project", "lora_realign", "abs_quantile", "quantize_clipped",
            "vstate_encode", "vstate_decode", "mstate_encode", "mstate_decode", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
-           "EXPORTS", "MUON_ABC"]
+           "EXPORTS", "MUON_ABC",
+           "release_workspaces", "gemm_plan", "newton_schulz_plan"]

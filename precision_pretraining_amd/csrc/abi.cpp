@@ -289,6 +289,17 @@ fs4_status fs4_gemm_nt(const fs4_nvfp4 *A, const fs4_nvfp4 *B, float alpha, cons
   return launch_gemm_nt(*A, *B, alpha, E, beta_e, C, LowRankEpilogue(), as_stream(stream));
 }
 
+fs4_status fs4_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t *out) {
+  if (!out) return FS4_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0 || K % kBlock) return FS4_ERR_SHAPE;
+  const GemmPlan p = plan_gemm(M, N, K, false, false, 0);
+  out[0] = p.bm;
+  out[1] = p.bn;
+  out[2] = p.tiles;
+  out[3] = p.s_tail;
+  return FS4_OK;
+}
+
 size_t fs4_linear_fwd_workspace_bytes(int64_t M, int64_t K, int64_t, int r) {
   size_t total = 0;
   carve_fwd(nullptr, M, K, r, &total);
@@ -420,6 +431,25 @@ size_t fs4_newton_schulz_workspace_bytes(int64_t m, int64_t n) {
   size_t total = 0;
   carve_ns(nullptr, m, n, &total);
   return total;
+}
+
+fs4_status fs4_newton_schulz_plan(int64_t m, int64_t n, int64_t *out) {
+  if (!out) return FS4_ERR_NULL;
+  if (!dim_ok(m) || !dim_ok(n) || m > n) return FS4_ERR_SHAPE;
+  size_t total = 0;
+  const NsWs w = carve_ns(nullptr, m, n, &total);
+  // the three products as fs4_newton_schulz launches them: A = Q(X) Q(X)^T and
+  // A^2 = Q(A) Q(A)^T (symmetric, m x m x n and m x m x m) and the transposed
+  // update X'^T = Q_col(X)^T Q_row(B)^T (n x m x m)
+  const int64_t shapes[3][3] = {{m, m, n}, {m, m, m}, {n, m, m}};
+  for (int i = 0; i < 3; ++i) {
+    const GemmPlan p = plan_gemm(shapes[i][0], shapes[i][1], shapes[i][2], i < 2, true, w.split_floats);
+    out[4 * i + 0] = p.bm;
+    out[4 * i + 1] = p.bn;
+    out[4 * i + 2] = p.tiles;
+    out[4 * i + 3] = p.s_tail;
+  }
+  return FS4_OK;
 }
 
 fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, int steps, float a,

@@ -132,6 +132,17 @@ struct LowRankEpilogue {
   int64_t r_sn = 0, r_sj = 1;
   float l_scale = 1.0f;
 };
+// The launcher's choice for an M x N x K product: tile configuration (0:
+// 256 x 256, 1: 256 x 192, 2: 128 x 128), the tile count, the tiles that run
+// whole and the k-splits of the rest; sym and can_split as for the launch
+// (can_split: a split workspace is given and there is no rank-r term).
+struct GemmPlan {
+  int cfg, bm, bn;
+  int64_t tiles, t_full;
+  int s_tail;
+  double cost;
+};
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, bool can_split, int64_t split_floats);
 // amax_parts (nullable) receives one max |C| per output tile (fp32 bits, the
 // form launch_quantize_encode reduces); *nwg (nullable) their count, which is
 // at most gemm_max_workgroups(M, N).  sym: B is the same view as A, there is

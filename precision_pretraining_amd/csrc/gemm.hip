@@ -848,26 +848,7 @@ fs4_status launch_cfg(GemmArgs g, int64_t tiles, int64_t t_full, int s_tail, hip
 
 }  // namespace
 
-fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
-                          float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
-                          uint32_t *amax_parts, int *nwg, bool sym, float *split_ws,
-                          int64_t split_floats) {
-  GemmArgs g;
-  g.t_full = 0;
-  g.s_tail = 1;
-  g.part = split_ws;
-  g.amax_parts = amax_parts;
-  if (nwg) *nwg = 0;
-  g.a_codes = A.codes; g.a_scales = A.scales; g.a_ts = A.tscale;
-  g.b_codes = B.codes; g.b_scales = B.scales; g.b_ts = B.tscale;
-  g.M = A.rows; g.N = B.rows; g.K = A.cols;
-  g.alpha = alpha; g.beta_e = beta_e; g.E = E; g.C = C;
-  g.L = lr.L; g.R = lr.R; g.r = lr.L ? lr.r : 0; g.l_scale = lr.l_scale;
-  g.r_sn = lr.r_sn; g.r_sj = lr.r_sj;
-  // a symmetric product (B the same view as A) stores only the upper
-  // triangle's tiles, each at both positions; not with a rank-r term
-  g.sym = sym && A.codes == B.codes && A.scales == B.scales && g.M == g.N && g.r == 0 ? 1 : 0;
-  if (g.M == 0 || g.N == 0) return FS4_OK;
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, bool can_split, int64_t split_floats) {
   // Plan: the tile shape and work split with the least estimated time.  One
   // k-tile (128 deep) of a 256 x 256 tile takes ~3.9 us on a CU (measured on
   // MI355X at the 3B shapes); the configurations' relative MFMA throughput:
@@ -882,18 +863,12 @@ fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, c
   // that fills at most half the chip are split along k so that it fills the
   // chip, for the price of writing and re-reading fp32 partials (counted at
   // 4 TB/s) and a reduce launch (~4 us).
-  const int64_t nk_all = (g.K + kBK - 1) / kBK;
-  const bool can_split = split_ws && g.r == 0 && g.K > 0 && g.K % kBK == 0;
-  struct Plan {
-    int cfg;
-    int64_t tiles, t_full;
-    int s_tail;
-    double cost;
-  };
+  const int64_t nk_all = (K + kBK - 1) / kBK;
+  can_split = can_split && K > 0 && K % kBK == 0;
   auto plan = [&](int cfg, int64_t bm, int64_t bn, double rate) {
-    Plan p{cfg, 0, 0, 1, 0.0};
-    const int64_t tm = (g.M + bm - 1) / bm, tn = (g.N + bn - 1) / bn;
-    p.tiles = g.sym ? tm * (tm + 1) / 2 : tm * tn;
+    GemmPlan p{cfg, (int)bm, (int)bn, 0, 0, 1, 0.0};
+    const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+    p.tiles = sym ? tm * (tm + 1) / 2 : tm * tn;
     p.t_full = p.tiles;
     const double tk = 3.9e-6 * (double)(bm * bn) / 65536.0 / rate;
     p.cost = (double)((p.tiles + 255) / 256) * (double)nk_all * tk;
@@ -916,13 +891,37 @@ fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, c
     }
     return p;
   };
-  Plan best = plan(0, 256, 256, 1.0);
-  if (!g.sym) {
-    const Plan p1 = plan(1, 256, 192, 0.83);
+  GemmPlan best = plan(0, 256, 256, 1.0);
+  if (!sym) {
+    const GemmPlan p1 = plan(1, 256, 192, 0.83);
     if (p1.cost < best.cost) best = p1;
   }
-  const Plan p2 = plan(2, 128, 128, 0.70);
+  const GemmPlan p2 = plan(2, 128, 128, 0.70);
   if (p2.cost < best.cost) best = p2;
+  return best;
+}
+
+fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
+                          float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
+                          uint32_t *amax_parts, int *nwg, bool sym, float *split_ws,
+                          int64_t split_floats) {
+  GemmArgs g;
+  g.t_full = 0;
+  g.s_tail = 1;
+  g.part = split_ws;
+  g.amax_parts = amax_parts;
+  if (nwg) *nwg = 0;
+  g.a_codes = A.codes; g.a_scales = A.scales; g.a_ts = A.tscale;
+  g.b_codes = B.codes; g.b_scales = B.scales; g.b_ts = B.tscale;
+  g.M = A.rows; g.N = B.rows; g.K = A.cols;
+  g.alpha = alpha; g.beta_e = beta_e; g.E = E; g.C = C;
+  g.L = lr.L; g.R = lr.R; g.r = lr.L ? lr.r : 0; g.l_scale = lr.l_scale;
+  g.r_sn = lr.r_sn; g.r_sj = lr.r_sj;
+  // a symmetric product (B the same view as A) stores only the upper
+  // triangle's tiles, each at both positions; not with a rank-r term
+  g.sym = sym && A.codes == B.codes && A.scales == B.scales && g.M == g.N && g.r == 0 ? 1 : 0;
+  if (g.M == 0 || g.N == 0) return FS4_OK;
+  const GemmPlan best = plan_gemm(g.M, g.N, g.K, g.sym != 0, split_ws && g.r == 0, split_floats);
   if (best.cfg == 0) return launch_cfg<2, 4, 4, 2>(g, best.tiles, best.t_full, best.s_tail, s, nwg);
   if (best.cfg == 1) return launch_cfg<2, 2, 4, 3>(g, best.tiles, best.t_full, best.s_tail, s, nwg);
   return launch_cfg<2, 2, 2, 2>(g, best.tiles, best.t_full, best.s_tail, s, nwg);

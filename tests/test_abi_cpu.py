@@ -269,3 +269,75 @@ def test_mstate_validation():
     assert enc(wsb=4) == WORKSPACE
     assert lib.fs4_mstate_decode(ctypes.byref(view(64, 48)), 64, 48, None, None) == NULL
     assert lib.fs4_mstate_decode(ctypes.byref(view(64, 48)), 64, 40, A16, None) == SHAPE
+
+
+# ---- the Python binding checks every tensor before calling the library ----------
+torch = pytest.importorskip("torch")
+
+
+def _cpu_view(rows, cols, dtype=None):
+    return fs4.NVFP4(torch.zeros((rows, cols // 2), dtype=dtype or torch.uint8),
+                     torch.zeros((rows, cols // 16), dtype=dtype or torch.uint8),
+                     torch.zeros(1), rows, cols)
+
+
+@pytest.mark.parametrize("call,exc,match", [
+    # wrong dtypes
+    (lambda: fs4.quantize(torch.zeros((64, 64), dtype=torch.float16)), TypeError, "x must have dtype"),
+    (lambda: fs4.quantize(torch.zeros((64, 64), dtype=torch.int32)), TypeError, "x must have dtype"),
+    (lambda: fs4.mstate_encode(torch.zeros((64, 64), dtype=torch.bfloat16),
+                               torch.zeros((64, 64), dtype=torch.int32)), TypeError, "m must have dtype"),
+    (lambda: fs4.vstate_encode(torch.zeros((64, 64), dtype=torch.float64)), TypeError, "v must have dtype"),
+    (lambda: fs4.linear_fwd(torch.zeros((64, 64)), _cpu_view(32, 64), None, None), TypeError, "X must have dtype"),
+    (lambda: fs4.gemm_nt(_cpu_view(64, 64, torch.int8), _cpu_view(32, 64)), TypeError, "A.codes must have dtype"),
+    # wrong shapes
+    (lambda: fs4.quantize(torch.zeros(64, dtype=torch.bfloat16)), ValueError, "x must be 2-D"),
+    (lambda: fs4.linear_fwd(torch.zeros((64, 64), dtype=torch.bfloat16), _cpu_view(32, 48), None, None),
+     ValueError, "must be on a CUDA device|R_row must be a"),
+    (lambda: fs4.vstate_decode(_cpu_view(64, 64), torch.zeros((4, 3), dtype=torch.bfloat16)), ValueError,
+     "q.codes must be on a CUDA device"),
+    # a view whose tensors disagree with its rows/cols
+    (lambda: fs4.gemm_nt(fs4.NVFP4(torch.zeros((64, 16), dtype=torch.uint8), torch.zeros((64, 4), dtype=torch.uint8),
+                                   torch.zeros(1), 64, 64), _cpu_view(32, 64)), ValueError,
+     r"A.codes must have shape \(64, 32\)"),
+    (lambda: fs4.gemm_nt(_cpu_view(64, 40), _cpu_view(32, 40)), ValueError, "cols must be a non-negative multiple"),
+    # non-contiguous
+    (lambda: fs4.quantize(torch.zeros((64, 128), dtype=torch.bfloat16)[:, ::2]), ValueError, "x must be contiguous"),
+    # right dtypes and shapes, but host memory
+    (lambda: fs4.quantize(torch.zeros((64, 64), dtype=torch.bfloat16)), ValueError, "x must be on a CUDA device"),
+    (lambda: fs4.mstate_encode(torch.zeros((64, 64)), torch.zeros((64, 64), dtype=torch.int32)), ValueError,
+     "m must be on a CUDA device"),
+    (lambda: fs4.abs_quantile(torch.zeros(100), 0.99), ValueError, "x must be on a CUDA device"),
+    (lambda: fs4.newton_schulz(torch.zeros((64, 128), dtype=torch.bfloat16)), ValueError, "G must be on a CUDA"),
+])
+def test_binding_rejects_bad_tensors_before_calling_the_library(call, exc, match):
+    """Host tensors can only reach the first argument's device check; the
+    checks of later arguments against the first are exercised on the GPU
+    (tests/test_gpu_binding.py)."""
+    with pytest.raises(exc, match=match):
+        call()
+
+
+def test_tensor_check_order_dtype_shape_layout_device():
+    """One argument's checks in order: dtype, shape, contiguity, device."""
+    chk = fs4._tensor
+    with pytest.raises(TypeError):
+        chk(torch.zeros((4, 4), dtype=torch.float64), "t", (torch.float32,), (4, 4))
+    with pytest.raises(ValueError, match="shape"):
+        chk(torch.zeros((4, 5)), "t", (torch.float32,), (4, 4))
+    with pytest.raises(ValueError, match="contiguous"):
+        chk(torch.zeros((4, 8))[:, ::2], "t", (torch.float32,), (4, 4))
+    with pytest.raises(ValueError, match="CUDA"):
+        chk(torch.zeros((4, 4)), "t", (torch.float32,), (4, 4))
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        chk(None, "t", (torch.float32,))
+
+
+def test_binding_rejects_mismatched_factor_shapes():
+    X = torch.zeros((64, 64), dtype=torch.bfloat16)
+    U = torch.zeros((32, 8), dtype=torch.bfloat16)
+    V = torch.zeros((4, 64), dtype=torch.bfloat16)     # rank disagrees with U
+    with pytest.raises(ValueError):
+        fs4.linear_fwd(X, _cpu_view(32, 64), U, V)
+    with pytest.raises(ValueError):
+        fs4.linear_fwd(X, _cpu_view(32, 64), U, None)

@@ -117,3 +117,73 @@ def test_first_moment_extreme_words():
         q = fs4.mstate_encode(dev_f32(m), torch.from_numpy(w.view(np.int32)).cuda())
         ref, _ = mstate_encode(m, w)
         assert_view_equal(q, ref, "fill %x" % fill)
+
+
+@pytest.mark.timeout(600)
+def test_first_moment_3b_weight_state_full():
+    """The 8192 x 3072 weight's first moment, every code, scale and decoded
+    value.  At this size the encode grid (the workgroups resident at once)
+    walks the 1.57 M groups of 16 in several grid-stride passes, which the
+    smaller cases (one pass) do not reach."""
+    fs4 = need_gpu()
+    print_case(test="mstate_3b", R=8192, C=3072)
+    m = _m((8192, 3072), 2024)
+    w = _words(m.shape, 2025)
+    q = fs4.mstate_encode(dev_f32(m), torch.from_numpy(w.view(np.int32)).cuda())
+    got = fs4.mstate_decode(q).cpu().numpy()
+    ref, _ = mstate_encode(m, w)
+    assert_view_equal(q, ref, "m 8192x3072")
+    assert np.array_equal(got.view(np.uint32), mstate_decode(ref).view(np.uint32))
+
+
+def _m_on_and_near_grid(R, C, seed):
+    """A first moment whose transformed values h = H/4 m sit on E2M1 grid
+    points and within a few ulps of them.
+
+    Every 16-group of h is g * m_b * 2^k with g on the E2M1 grid (one +-6 per
+    group sets the block amax 6 m_b 2^k), m_b an E4M3 value >= 1, and one group
+    holding 2688 * 2^k so that the tensor scale is exactly 2^k.  Those values
+    are multiples of 2^(k-4) below 2^(k+16), so m = H h / 4 and the transform
+    back are exact in fp32: the quotients |h| / (s_b s_t) land exactly on the
+    grid for the 6-scale candidate.  In every other row each value is nudged
+    by 0 to 2 ulps up or down before m is formed, so its quotient falls just
+    beside a grid point (the transform's rounding keeps it within a few
+    ulps)."""
+    rng = np.random.default_rng(seed)
+    k = -12
+    e4m3_ge1 = np.array([2.0 ** e * (1 + mm / 8) for e in range(0, 9) for mm in range(8)
+                         if 2.0 ** e * (1 + mm / 8) < 448])   # 448 only in the amax group
+    grid = oracle.E2M1_GRID
+    g = rng.choice(grid, size=(R, C // 16, 16)) * rng.choice([-1.0, 1.0], size=(R, C // 16, 16))
+    pos = rng.integers(0, 16, size=(R, C // 16))
+    np.put_along_axis(g, pos[..., None], 6.0 * rng.choice([-1.0, 1.0], size=(R, C // 16, 1)), axis=2)
+    mb = rng.choice(e4m3_ge1, size=(R, C // 16, 1))
+    mb[0, 0, 0] = 448.0
+    g[0, 0, :] = np.abs(g[0, 0, :])
+    g[0, 0, 0] = 6.0                                   # h = 2688 * 2^k: s_t = 2^k exactly
+    h = (g * mb * 2.0 ** k).astype(np.float32)
+    nudge = rng.integers(-2, 3, size=h.shape).astype(np.float32)
+    odd = (np.arange(R) % 2 == 1)[:, None, None]
+    h = np.where(odd & (h != 0), h + nudge * np.spacing(np.abs(h)) * np.sign(h), h).astype(np.float32)
+    h = h.reshape(R, C)
+    from oracle.adamw import hadamard16
+    return hadamard16(h.astype(np.float64)).astype(np.float32)
+
+
+def test_first_moment_on_and_near_grid_multi_pass():
+    """Transformed values exactly on and a few ulps beside the E2M1 grid
+    points, bit for bit, at 4096 x 1024 (262,144 groups: more than the
+    encode grid holds, so the grid-stride loop runs a second pass)."""
+    fs4 = need_gpu()
+    print_case(test="mstate_grid", R=4096, C=1024)
+    m = _m_on_and_near_grid(4096, 1024, 77)
+    from oracle.adamw import hadamard16
+    h = hadamard16(m.astype(np.float64))
+    assert np.float32(np.abs(h).max()) == np.float32(2688 * 2.0 ** -12)
+    for fill in (None, 0, 0xFFFFFFFF):
+        w = _words(m.shape, 78) if fill is None else np.full(m.shape, fill, dtype=np.uint32)
+        q = fs4.mstate_encode(dev_f32(m), torch.from_numpy(w.view(np.int32)).cuda())
+        ref, _ = mstate_encode(m, w)
+        assert_view_equal(q, ref, "grid words %s" % fill)
+        got = fs4.mstate_decode(q).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), mstate_decode(ref).view(np.uint32))

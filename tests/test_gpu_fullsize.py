@@ -1,0 +1,139 @@
+"""Parity at the full workload sizes, in the launch configurations the
+benchmark times: every element of every output, not samples.
+
+* The 3B-shape projection (X 8192 x 3072, W 8192 x 3072 = U V + R with rank
+  32, dY 8192 x 8192): the quantized views bit for bit; Y, dX, dW against the
+  oracle's fp64 products of the block values, normalised by sum |a||b| (the
+  path's error bound); dU, dV against fp64 BLAS.  These shapes take the
+  256 x 256 and 256 x 192 tiles with direct global-to-LDS operand staging,
+  which no smaller test reaches.
+* The same step run twice in one process: bit-identical outputs.
+* Newton-Schulz on the 3072 x 8192 momentum, teacher-forced one step at a
+  time from the oracle's iterates: A, B and X' element by element.  At this
+  shape A and A^2 take split upper-triangle 128 x 128 tiles and the update
+  takes 256 x 192 tiles with the a X term added in the epilogue.
+
+The GEMM bars: 1e-3 (the stated tolerance) and a tighter 1e-5 where both
+sides multiply the same quantized operands (only the fp32 summation order
+differs, observed ~1e-6).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (assert_view_equal, dev_bf16, dev_f32, f32, gemm_full_check, need_gpu, print_case,
+                      quantize_chunked)
+from oracle.newton_schulz import MUON_ABC
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+TIGHT = 1e-5
+M, K, N, R_RANK = 8192, 3072, 8192, 32
+
+
+def _run_step(fs4, Xd, Ud, Vd, Rw, dYd, T=None):
+    R_row, R_col = fs4.quantize(Rw)
+    f = fs4.linear_fwd(Xd, R_row, Ud, Vd)
+    b = fs4.linear_bwd(dYd, Xd, f.X_col, R_col, Ud, Vd, f.T if T is None else T)
+    return R_row, R_col, f, b
+
+
+@pytest.mark.timeout(900)
+def test_3b_linear_fwd_bwd_full(linear3b_inputs):
+    fs4 = need_gpu()
+    print_case(test="linear_3b_full", M=M, K=K, N=N, r=R_RANK)
+    assert fs4.gemm_plan(M, N, K)["tile"] == (256, 256)      # forward
+    assert fs4.gemm_plan(M, K, N)["tile"] == (256, 192)      # dX
+    assert fs4.gemm_plan(N, K, M)["tile"] == (256, 192)      # dW
+    d, dy = linear3b_inputs
+    x32, u32, v32, dy32 = f32(d["X"]), f32(d["U"]), f32(d["V"]), f32(dy)
+    R = d["R"]
+    # both sides take the oracle's T (fp32), so no HIP output feeds the oracle
+    T64 = x32.astype(np.float64) @ v32.astype(np.float64).T
+    T32 = T64.astype(np.float32)
+    Xd, Ud, Vd, dYd = dev_bf16(d["X"]), dev_bf16(d["U"]), dev_bf16(d["V"]), dev_bf16(dy)
+    R_row, R_col, f, b = _run_step(fs4, Xd, Ud, Vd, dev_f32(R), dYd, dev_f32(T32))
+    dY_row, dY_col = fs4.quantize(dYd)
+    torch.cuda.synchronize()
+    print("gpu done", flush=True)
+
+    qx_row, qx_col, _ = quantize_chunked(x32)
+    qr_row, qr_col, _ = quantize_chunked(R)
+    qdy_row, qdy_col, _ = quantize_chunked(dy32)
+    for got, want, what in ((R_row, qr_row, "R_row"), (R_col, qr_col, "R_col"), (f.X_col, qx_col, "X_col"),
+                            (dY_row, qdy_row, "dY_row"), (dY_col, qdy_col, "dY_col")):
+        assert_view_equal(got, want, what)
+    print("views bit-exact", flush=True)
+
+    u64, v64, dy64 = u32.astype(np.float64), v32.astype(np.float64), dy32.astype(np.float64)
+    T_abs = np.abs(T64)
+    e = gemm_full_check(f.Y.cpu().numpy(), qx_row, qr_row,
+                        extra=lambda i0, i1: T64[i0:i1] @ u64.T,
+                        extra_abs=lambda i0, i1: T_abs[i0:i1] @ np.abs(u64).T)
+    print("Y err %.3e" % e, flush=True)
+    assert e <= TOL and e <= TIGHT, ("Y", e)
+    P = dy64 @ u64
+    P_abs = np.abs(dy64) @ np.abs(u64)
+    e = gemm_full_check(b.dX.cpu().numpy(), qdy_row, qr_col,
+                        extra=lambda i0, i1: P[i0:i1] @ v64,
+                        extra_abs=lambda i0, i1: P_abs[i0:i1] @ np.abs(v64))
+    print("dX err %.3e" % e, flush=True)
+    assert e <= TOL and e <= TIGHT, ("dX", e)
+    e = gemm_full_check(b.dW.cpu().numpy(), qdy_col, qx_col)
+    print("dW err %.3e" % e, flush=True)
+    assert e <= TOL and e <= TIGHT, ("dW", e)
+    dU_ref = dy64.T @ T32.astype(np.float64)
+    dU_den = np.abs(dy64).T @ np.abs(T32.astype(np.float64))
+    assert oracle.rel_err(b.dU.cpu().numpy(), dU_ref, dU_den) <= TIGHT
+    dV_ref = P.T @ x32.astype(np.float64)
+    dV_den = P_abs.T @ np.abs(x32.astype(np.float64))
+    assert oracle.rel_err(b.dV.cpu().numpy(), dV_ref, dV_den) <= TIGHT
+
+
+def test_3b_step_is_bit_identical_when_run_twice(linear3b_inputs):
+    """Two runs of the full step (the benchmark's launch sequence, T from the
+    forward) in one process give bit-identical outputs and views: every
+    reduction has a fixed order and the only atomic is an order-free max."""
+    fs4 = need_gpu()
+    print_case(test="linear_3b_twice")
+    d, dy = linear3b_inputs
+    Xd, Ud, Vd, dYd, Rw = dev_bf16(d["X"]), dev_bf16(d["U"]), dev_bf16(d["V"]), dev_bf16(dy), dev_f32(d["R"])
+    runs = []
+    for _ in range(2):
+        R_row, R_col, f, b = _run_step(fs4, Xd, Ud, Vd, Rw, dYd)
+        runs.append([f.Y, f.T, b.dX, b.dW, b.dU, b.dV, R_row.codes, R_row.scales, R_col.codes,
+                     f.X_col.codes, f.X_col.scales, f.X_col.tscale])
+    torch.cuda.synchronize()
+    names = ["Y", "T", "dX", "dW", "dU", "dV", "R_row", "R_row.s", "R_col", "X_col", "X_col.s", "X_col.t"]
+    for name, a, b in zip(names, *runs):
+        assert torch.equal(a, b), name
+
+
+@pytest.mark.timeout(900)
+def test_ns_3072x8192_per_step_full():
+    """Steps 0 and 1 of the NVFP4 Newton-Schulz on the 3072 x 8192 momentum,
+    each started from the oracle's own iterate (normalize off, one step):
+    A, B and X' compared element by element; A is stored exactly symmetric
+    (the product quantizes it once on that premise)."""
+    fs4 = need_gpu()
+    print_case(test="ns_3072x8192_full")
+    plan = fs4.newton_schulz_plan(3072, 8192)
+    assert plan["update"]["tile"] == (256, 192) and plan["update"]["splits"] == 1
+    assert plan["A"]["splits"] > 1              # a split last round of upper-triangle tiles
+    g = synth.ns_input()
+    xs, steps = oracle.newton_schulz(f32(g), 2)
+    for k in range(2):
+        X, tX, tA, tB = fs4.newton_schulz(dev_f32(xs[k]), steps=1, normalize=False, trace=True)
+        A = tA[0]
+        assert torch.equal(A, A.T.contiguous()), k
+        st = steps[k]
+        eA = oracle.rel_err(A.cpu().numpy(), st["A64"], st["A_D"])
+        eB = oracle.rel_err(tB[0].cpu().numpy(), st["B64"], st["B_D"])
+        eX = oracle.rel_err(X.cpu().numpy(), st["X64"], st["X_D"])
+        print("step", k, "errA %.2e errB %.2e errX %.2e" % (eA, eB, eX), flush=True)
+        # A multiplies the same quantized operands on both sides; B and X' also
+        # carry the last-bit differences of each side's own fp32 A
+        assert eA <= TIGHT and eB <= TOL and eX <= TOL, (k, eA, eB, eX)

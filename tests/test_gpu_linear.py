@@ -163,61 +163,6 @@ def _sampled_gemm_check(got, a_rows_q, b_rows_q, pairs, extra=None):
     return max(errs)
 
 
-def test_3b_linear_fwd_bwd_sampled():
-    """The 3B-shape projection (X 8192 x 3072, W 8192 x 3072, rank 32,
-    dY 8192 x 8192) at full size, in the launch configuration the benchmark
-    times; outputs checked on sampled entries, quantized views on sampled
-    rows, low-rank factor gradients in full."""
-    fs4 = need_gpu()
-    print_case(test="linear_3b", M=8192, K=3072, N=8192, r=32)
-    d = synth.linear3b()
-    dY = synth.linear3b_dy()
-    X, U, V, R = d["X"], d["U"], d["V"], d["R"]
-    x32, u32, v32, dy32 = f32(X), f32(U), f32(V), f32(dY)
-    Xd, Ud, Vd, dYd = dev_bf16(X), dev_bf16(U), dev_bf16(V), dev_bf16(dY)
-    R_row, R_col = fs4.quantize(dev_f32(R))
-    fwd = fs4.linear_fwd(Xd, R_row, Ud, Vd)
-    T64 = x32.astype(np.float64) @ v32.astype(np.float64).T
-    T32 = T64.astype(np.float32)
-    bwd = fs4.linear_bwd(dYd, Xd, fwd.X_col, R_col, Ud, Vd, dev_f32(T32))
-    Y = fwd.Y.cpu().numpy()
-    dX, dW = bwd.dX.cpu().numpy(), bwd.dW.cpu().numpy()
-    s_x, s_r, s_dy = tensor_scale(x32), tensor_scale(R), tensor_scale(dy32)
-    rng = np.random.default_rng(7)
-    M, K, N = 8192, 3072, 8192
-    # Y[m, n] = Q(X)[m] . Q(R)[n] + (T U^T)[m, n]
-    ms, ns_ = rng.integers(0, M, 48), rng.integers(0, N, 48)
-    qa = [quantize_rows(x32[m:m + 1], s_x) for m in ms]
-    qb = [quantize_rows(R[n:n + 1], s_r) for n in ns_]
-    lr = lambda i, j: (float(T64[i] @ u32[j].astype(np.float64)), float(np.abs(T64[i]) @ np.abs(u32[j])))
-    e = _sampled_gemm_check(Y, qa, qb, list(zip(ms, ns_)), lr)
-    assert e <= TOL and e <= TIGHT, ("Y", e)
-    # dX[m, k] = Q_row(dY)[m] . Q_col(R)[k] + (P V)[m, k], P = dY U
-    ms, ks = rng.integers(0, M, 32), rng.integers(0, K, 32)
-    qa = [quantize_rows(dy32[m:m + 1], s_dy) for m in ms]
-    qb = [quantize_rows(np.ascontiguousarray(R[:, k:k + 1].T), s_r) for k in ks]
-    P_rows = {m: dy32[m].astype(np.float64) @ u32.astype(np.float64) for m in ms}
-    P_abs = {m: np.abs(dy32[m]).astype(np.float64) @ np.abs(u32).astype(np.float64) for m in ms}
-    lr = lambda i, j: (float(P_rows[i] @ v32[:, j]), float(P_abs[i] @ np.abs(v32[:, j])))
-    e = _sampled_gemm_check(dX, qa, qb, list(zip(ms, ks)), lr)
-    assert e <= TOL and e <= TIGHT, ("dX", e)
-    # dW[n, k] = Q_col(dY)[n] . Q_col(X)[k]
-    ns_, ks = rng.integers(0, N, 32), rng.integers(0, K, 32)
-    qa = [quantize_rows(np.ascontiguousarray(dy32[:, n:n + 1].T), s_dy) for n in ns_]
-    qb = [quantize_rows(np.ascontiguousarray(x32[:, k:k + 1].T), s_x) for k in ks]
-    e = _sampled_gemm_check(dW, qa, qb, list(zip(ns_, ks)))
-    assert e <= TOL and e <= TIGHT, ("dW", e)
-    # dU = dY^T T and dV = (dY U)^T X in full (float64 BLAS)
-    dy64 = dy32.astype(np.float64)
-    dU_ref = dy64.T @ T32.astype(np.float64)
-    dU_den = np.abs(dy64).T @ np.abs(T32.astype(np.float64))
-    assert _err(bwd.dU.cpu().numpy(), dU_ref, dU_den) <= TIGHT
-    P = dy64 @ u32.astype(np.float64)
-    dV_ref = P.T @ x32.astype(np.float64)
-    dV_den = (np.abs(dy64) @ np.abs(u32.astype(np.float64))).T @ np.abs(x32.astype(np.float64))
-    assert _err(bwd.dV.cpu().numpy(), dV_ref, dV_den) <= TIGHT
-
-
 @pytest.mark.parametrize("M,N,K", [(4096, 4096, 1040), (8192, 3008, 1040)])
 def test_gemm_large_tiles_ragged_k_sampled(M, N, K):
     """Shapes large enough for the wide tile configurations (4096 x 4096 takes

@@ -57,13 +57,12 @@ def test_projection_matches_oracle(N, K, r):
     _close(got_v, ref_v, "dV")
 
 
-def test_projection_3b_factors_and_linear_bwd_gradients():
+def test_projection_3b_factors_and_linear_bwd_gradients(linear3b_inputs):
     """The 3B-shape factors (rank 32, N 8192, K 3072) with the gradients
     fs4_linear_bwd produces for them."""
     fs4 = need_gpu()
     print_case(test="lora_project_3b")
-    d = synth.linear3b()
-    dy = synth.linear3b_dy()
+    d, dy = linear3b_inputs
     X, U, V = dev_bf16(d["X"]), dev_bf16(d["U"]), dev_bf16(d["V"])
     Rw = dev_f32(d["R"])
     R_row, R_col = fs4.quantize(Rw)
@@ -203,12 +202,12 @@ def test_realign_exactly_low_rank():
     assert np.abs(gu @ gv + gr - w).max() <= 1e-6 * np.abs(w).max()
 
 
-def test_realign_3b_shapes():
+def test_realign_3b_shapes(linear3b_inputs):
     """The 3B weight (N 8192, K 3072, rank 32), l = 40 test vectors, one
     power iteration."""
     fs4 = need_gpu()
     print_case(test="lora_realign_3b")
-    d = synth.linear3b()
+    d = linear3b_inputs[0]
     u, v, res = d["U"], d["V"], d["R"]
     rng = synth.rng_for(1234)
     om = rng.standard_normal((40, 3072)).astype(np.float32)

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import need_gpu, dev_bf16, dev_f32, assert_view_equal, host_view, print_case, f32
+from gpu_util import need_gpu, dev_bf16, dev_f32, assert_view_equal, host_view, print_case, f32, quantize_chunked
 
 pytestmark = pytest.mark.gpu
 
@@ -112,23 +112,13 @@ def test_quantizer_workload_full_size():
     _run(dev_bf16(b), f32(b), what="4096^2")
 
 
-def test_3b_gradient_sampled_rows_and_columns():
-    """8192 x 8192 dY (the backward's largest quantization): tensor scale
-    exact, and sampled rows / columns of both layouts bit-exact."""
+def test_3b_gradient_full(linear3b_inputs):
+    """8192 x 8192 dY (the backward's largest quantization): both layouts bit
+    for bit in full."""
     fs4 = need_gpu()
     print_case(test="quantize_dy_8192", shape=(8192, 8192))
-    b = synth.linear3b_dy()
-    x = f32(b)
+    b = linear3b_inputs[1]
     row, col = fs4.quantize(dev_bf16(b))
-    codes_r, scales_r, ts = host_view(row)
-    codes_c, scales_c, ts_c = host_view(col)
-    from oracle.quantize import tensor_scale, quantize_rows
-    s_t = tensor_scale(x)
-    assert ts == s_t and ts_c == s_t
-    rng = np.random.default_rng(0)
-    rows = rng.choice(8192, 24, replace=False)
-    ref = quantize_rows(np.ascontiguousarray(x[rows]), s_t)
-    assert np.array_equal(codes_r[rows], ref.codes) and np.array_equal(scales_r[rows], ref.scales)
-    cols = rng.choice(8192, 24, replace=False)
-    refc = quantize_rows(np.ascontiguousarray(x[:, cols].T), s_t)
-    assert np.array_equal(codes_c[cols], refc.codes) and np.array_equal(scales_c[cols], refc.scales)
+    ref_r, ref_c, _ = quantize_chunked(f32(b))
+    assert_view_equal(row, ref_r, "dY row")
+    assert_view_equal(col, ref_c, "dY col")

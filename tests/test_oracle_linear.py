@@ -151,3 +151,89 @@ def test_rel_err_metric():
     d = np.array([10.0, 10.0, 0.0])
     assert oracle.rel_err([1.0, 2.5, 0.0], ref, d) == 0.05
     assert oracle.rel_err([1.0, 2.0, 1e-30], ref, d) == float("inf")
+
+
+# ---- the error normalisers ------------------------------------------------------
+# Every GEMM parity bar divides by a normaliser D = sum |a||b| over the terms of
+# the output.  A mistake in D (a dropped term, a dropped tensor scale) would
+# make those bars vacuous, so D is pinned on its own: against the exact twin,
+# against |C| where no term can cancel, as an upper bound of |C|, and for its
+# scaling with each operand's tensor scale.
+
+def _nonneg_linear_inputs(rng, M, K, N, r):
+    x = synth.bf16_to_f32(synth.bf16_round(np.abs(rng.standard_normal((M, K)))))
+    u = synth.bf16_to_f32(synth.bf16_round(np.abs(rng.standard_normal((N, r))) * 0.1))
+    v = synth.bf16_to_f32(synth.bf16_round(np.abs(rng.standard_normal((r, K))) * 0.1))
+    w = np.abs(rng.standard_t(3, size=(N, K)) * 0.02).astype(np.float32)
+    dy = synth.bf16_to_f32(synth.bf16_round(np.abs(rng.standard_normal((M, N))) * 1e-3))
+    return x, u, v, w, dy
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 16, 32), (8, 24, 48)])
+def test_gemm_nt_abs_matches_rational_brute_force(m, n, k):
+    rng = np.random.default_rng(7 * m + n + k)
+    a = (rng.standard_normal((m, k)) * np.exp(rng.uniform(-2, 2, (m, 1)))).astype(np.float32)
+    b = rng.standard_t(3, size=(n, k)).astype(np.float32)
+    ra, _, _, _, sa = X.quantize_exact(a)
+    rb, _, _, _, sb = X.quantize_exact(b)
+    av = _exact_block_values(ra, X.quantize_rows_exact(a, sa)[1])
+    bv = _exact_block_values(rb, X.quantize_rows_exact(b, sb)[1])
+    qa, _, _ = oracle.quantize(a, colwise=False)
+    qb, _, _ = oracle.quantize(b, colwise=False)
+    got = oracle.gemm_nt_abs(qa, qb)
+    for i in range(m):
+        for j in range(n):
+            want = sa * sb * sum((abs(av[i][t]) * abs(bv[j][t]) for t in range(k)), Fraction(0))
+            assert abs(Fraction(float(got[i, j])) - want) <= want * Fraction(1, 2 ** 50)
+
+
+def test_gemm_nt_abs_bounds_and_equals_the_product_without_cancellation():
+    rng = np.random.default_rng(3)
+    a = rng.standard_normal((40, 96)).astype(np.float32)
+    b = rng.standard_t(3, size=(24, 96)).astype(np.float32)
+    qa, _, _ = oracle.quantize(a, colwise=False)
+    qb, _, _ = oracle.quantize(b, colwise=False)
+    c, d = oracle.gemm_nt(qa, qb), oracle.gemm_nt_abs(qa, qb)
+    assert np.all(d >= np.abs(c)) and np.any(d > np.abs(c) * 1.5)
+    qa2, _, _ = oracle.quantize(np.abs(a), colwise=False)
+    qb2, _, _ = oracle.quantize(np.abs(b), colwise=False)
+    c2, d2 = oracle.gemm_nt(qa2, qb2), oracle.gemm_nt_abs(qa2, qb2)
+    np.testing.assert_allclose(d2, np.abs(c2), rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("ja,jb", [(3, 0), (0, -5), (7, -11)])
+def test_gemm_nt_abs_scales_with_each_tensor_scale(ja, jb):
+    """x -> 2^j x leaves codes and block scales alone and scales s_t by 2^j,
+    so D scales by 2^(ja + jb) exactly; a normaliser without the tensor
+    scales would not move."""
+    rng = np.random.default_rng(ja * 31 + jb + 100)
+    a = rng.standard_normal((32, 64)).astype(np.float32)
+    b = rng.standard_normal((16, 64)).astype(np.float32)
+    q = lambda x: oracle.quantize(x, colwise=False)[0]
+    d0 = oracle.gemm_nt_abs(q(a), q(b))
+    d1 = oracle.gemm_nt_abs(q(a * np.float32(2.0 ** ja)), q(b * np.float32(2.0 ** jb)))
+    assert np.array_equal(d1, d0 * 2.0 ** (ja + jb))
+
+
+def test_linear_normalisers_equal_the_outputs_without_cancellation():
+    """With every input non-negative no term of Y, dX, dW, dU, dV can cancel,
+    so each normaliser equals its output's magnitude; a dropped term (the
+    rank-r part, a tensor scale) or a wrong one breaks the equality."""
+    rng = np.random.default_rng(5)
+    M, K, N, r = 48, 64, 32, 4
+    x, u, v, w, dy = _nonneg_linear_inputs(rng, M, K, N, r)
+    r_row, r_col, _ = oracle.quantize(w)
+    for beta in (1.0, 0.5):
+        f = oracle.linear_fwd(x, r_row, u, v, beta)
+        np.testing.assert_allclose(f["D"], np.abs(f["Y64"]), rtol=1e-13, atol=0)
+        b = oracle.linear_bwd(dy, x, r_col, u, v, f["T64"], beta, x_col=f["X_col"])
+        for name in ("dX", "dW", "dU", "dV"):
+            np.testing.assert_allclose(b[name + "_D"], np.abs(b[name]), rtol=1e-13, atol=0, err_msg=name)
+    # with signs the normalisers bound the outputs and exceed them somewhere
+    xs = x * rng.choice([-1.0, 1.0], x.shape).astype(np.float32)
+    f = oracle.linear_fwd(xs, r_row, u, v)
+    assert np.all(f["D"] >= np.abs(f["Y64"]) * (1 - 1e-13)) and np.any(f["D"] > 1.5 * np.abs(f["Y64"]))
+    # the rank-r part of D is |beta| sum_j |T||U|: it scales with beta
+    f1, f2 = oracle.linear_fwd(x, r_row, u, v, 1.0), oracle.linear_fwd(x, r_row, u, v, -2.0)
+    d_main = oracle.gemm_nt_abs(f1["X_row"], r_row)
+    np.testing.assert_allclose(f2["D"] - d_main, 2.0 * (f1["D"] - d_main), rtol=1e-12)

@@ -171,3 +171,22 @@ def test_clipping_at_the_maximum_is_the_plain_step():
     # the clip changes only the quantized copy: with a representable X the
     # unclipped and clipped A differ only through the clipped entries
     assert not np.array_equal(clipped["A"], plain["A"])
+
+
+def test_ns_step_normalisers_equal_the_products_without_cancellation():
+    """With a non-negative iterate and (a, b, c) > 0 no term of A, B or X'
+    cancels, so A_D, B_D and X_D equal |A|, |B| and |X'|; the normalisers
+    also scale with the iterate's tensor scale (X -> 2X: A_D x4)."""
+    rng = np.random.default_rng(9)
+    x = np.abs(rng.standard_normal((32, 96))).astype(np.float32) * np.float32(0.01)
+    st = oracle.ns_step(x, 1.0, 0.5, 0.25)
+    np.testing.assert_allclose(st["A_D"], np.abs(st["A64"]), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(st["B_D"], np.abs(st["B64"]), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(st["X_D"], np.abs(st["X64"]), rtol=1e-13, atol=0)
+    st2 = oracle.ns_step(x * np.float32(2.0), 1.0, 0.5, 0.25)
+    assert np.array_equal(st2["A_D"], 4.0 * st["A_D"])
+    # with the quintic's negative b the B normaliser strictly exceeds |B| where
+    # the two terms cancel
+    xn = oracle.ns_normalize(x)[0]          # ||X||_F = 1: A^2 is as large as A
+    stq = oracle.ns_step(xn, *MUON_ABC)
+    assert np.all(stq["B_D"] >= np.abs(stq["B64"])) and np.any(stq["B_D"] > 1.3 * np.abs(stq["B64"]))

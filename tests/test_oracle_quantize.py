@@ -194,3 +194,20 @@ def test_rejects_non_finite_and_bad_shapes():
         quantize_rows(np.zeros((2, 20), dtype=np.float32), np.float32(1))
     with pytest.raises(TypeError):
         oracle.quantize(np.zeros((16, 16)))
+
+
+def test_chunked_quantize_helper_equals_the_oracle():
+    """The tests' chunked, threaded driver of the oracle's row quantizer (used
+    at the full workload sizes) gives oracle.quantize's views bit for bit."""
+    import sys
+    import os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from gpu_util import quantize_chunked
+    rng = np.random.default_rng(17)
+    x = (rng.standard_t(3, size=(1040, 528)) * np.exp(rng.uniform(-3, 3, (1040, 1)))).astype(np.float32)
+    want = oracle.quantize(x)
+    got = quantize_chunked(x, chunk=96, threads=4)
+    assert got[2] == want[2]
+    for g, w in zip(got[:2], want[:2]):
+        assert g.rows == w.rows and g.cols == w.cols and g.tscale == w.tscale
+        assert np.array_equal(g.codes, w.codes) and np.array_equal(g.scales, w.scales)
