@@ -94,6 +94,21 @@ fs4_status fs4_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                         const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* fs4_quantize_noalloc — fs4_quantize without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight loops, harnesses that forbid allocation.  The caller passes only the
+ * input and the output views; the quantizer's scratch (its 4 KB of amax
+ * partials, the same for every input size, fs4_quantize_noalloc_scratch_bytes)
+ * lives in a device array of the library that each GPU holds from the first
+ * call on it until the process ends.  Nothing is allocated or freed.  Calls
+ * that overlap on one GPU (concurrent streams, or threads) share that array
+ * and race; serialise them.  Arguments, results and errors as fs4_quantize;
+ * also FS4_ERR_HIP when the array's device address cannot be obtained.
+ */
+size_t fs4_quantize_noalloc_scratch_bytes(void);
+fs4_status fs4_quantize_noalloc(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
+                                const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise, void *stream);
+
 /* ---------------------------------------------------------------------------
  * fs4_gemm_nt — C[M][N] = alpha * s_tA * s_tB * sum_k A_hat[m,k] B_hat[n,k]
  *                         + beta_e * E[M][N]            (E nullable)

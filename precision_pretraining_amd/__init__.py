@@ -53,6 +53,7 @@ EXPORTS = [
     "fs4_vstate_encode_workspace_bytes", "fs4_vstate_encode", "fs4_vstate_decode",
     "fs4_mstate_encode_workspace_bytes", "fs4_mstate_encode", "fs4_mstate_decode",
     "fs4_workspace_bytes", "fs4_status_str", "fs4_version", "fs4_gemm_plan", "fs4_newton_schulz_plan",
+    "fs4_quantize_noalloc", "fs4_quantize_noalloc_scratch_bytes",
 ]
 
 
@@ -84,6 +85,8 @@ _sig("fs4_version", ctypes.c_char_p, [])
 _sig("fs4_workspace_bytes", _SZ, [ctypes.c_int, _I64, _I64, _I64, ctypes.c_int])
 _sig("fs4_quantize_workspace_bytes", _SZ, [_I64, _I64])
 _sig("fs4_quantize", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _VP, _VP, _P, _SZ, _P])
+_sig("fs4_quantize_noalloc", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _VP, _VP, _P])
+_sig("fs4_quantize_noalloc_scratch_bytes", _SZ, [])
 _sig("fs4_gemm_workspace_bytes", _SZ, [_I64, _I64, _I64])
 _sig("fs4_gemm_nt", ctypes.c_int, [_VP, _VP, _F, _P, _F, _P, _P, _SZ, _P])
 _sig("fs4_linear_fwd_workspace_bytes", _SZ, [_I64, _I64, _I64, ctypes.c_int])
@@ -296,6 +299,27 @@ def quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, out_ro
                              ctypes.byref(cv) if cv is not None else None,
                              ws.data_ptr(), ws.numel(), _stream(dev)), "fs4_quantize")
     return (out_row if rowwise else None), (out_col if colwise else None)
+
+
+def quantize_noalloc(x: torch.Tensor, out_row: Optional[NVFP4], out_col: Optional[NVFP4]):
+    """quantize() into caller-given views with no workspace: the library's
+    own per-device scratch array serves (calls that overlap on one GPU
+    race).  Neither the binding nor the library allocates."""
+    rows, cols = _matrix(x, "x", _FLOAT)
+    dev = x.device
+    if out_row is None and out_col is None:
+        raise ValueError("quantize_noalloc needs at least one output view")
+    if out_row is not None:
+        _view(out_row, "out_row", rows, cols, dev)
+    if out_col is not None:
+        _view(out_col, "out_col", cols, rows, dev)
+    rv = out_row.c() if out_row is not None else None
+    cv = out_col.c() if out_col is not None else None
+    _check(_lib.fs4_quantize_noalloc(x.data_ptr(), _dtype_code(x), rows, cols,
+                                     ctypes.byref(rv) if rv is not None else None,
+                                     ctypes.byref(cv) if cv is not None else None, _stream(dev)),
+           "fs4_quantize_noalloc")
+    return out_row, out_col
 
 
 def gemm_nt(A: NVFP4, B: NVFP4, alpha: float = 1.0, E: Optional[torch.Tensor] = None, beta_e: float = 0.0,
@@ -548,7 +572,7 @@ def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> i
     return _lib.fs4_workspace_bytes(op, d0, d1, d2, r)
 
 
-__all__ = ["NVFP4", "quantize", "gemm_nt", "linear_fwd", "LinearFwd", "linear_bwd", "LinearBwd",
+__all__ = ["NVFP4", "quantize", "quantize_noalloc", "gemm_nt", "linear_fwd", "LinearFwd", "linear_bwd", "LinearBwd",
            "newton_schulz", "lora_project", "lora_realign", "abs_quantile", "quantize_clipped",
            "vstate_encode", "vstate_decode", "mstate_encode", "mstate_decode", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
            "EXPORTS", "MUON_ABC",

@@ -33,7 +33,8 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + I
                 "-Wall", "-Wno-unused-function"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-Wall"]
 
-SOURCES = ["quantize.hip", "gemm.hip", "lowrank.hip", "subspace.hip", "realign.hip", "select.hip", "adamw.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "lowrank.hip", "subspace.hip", "realign.hip", "select.hip", "adamw.hip",
+           "static_scratch.hip", "abi.cpp"]
 
 
 def _run(cmd, verbose):

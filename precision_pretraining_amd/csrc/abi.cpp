@@ -157,6 +157,16 @@ size_t fs4_quantize_workspace_bytes(int64_t, int64_t) { return quantize_ws_bytes
 fs4_status fs4_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                         const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise, void *ws,
                         size_t ws_bytes, void *stream) {
+  FS4_TRY(check_quantize_args(x, dt, rows, cols, rowwise, colwise));
+  FS4_TRY(check_ws(ws, ws_bytes, quantize_ws_bytes()));
+  return launch_quantize(x, dt, rows, cols, rowwise, colwise, ws, as_stream(stream));
+}
+
+}  // extern "C"
+
+namespace fs4 {
+fs4_status check_quantize_args(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
+                               const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise) {
   if (dt != FS4_BF16 && dt != FS4_FP32) return FS4_ERR_DTYPE;
   if (rows < 0 || cols < 0) return FS4_ERR_SHAPE;
   if (!rowwise && !colwise) return FS4_ERR_NULL;
@@ -176,9 +186,11 @@ fs4_status fs4_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
       FS4_TRY(check_view(colwise, cols, rows));
     }
   }
-  FS4_TRY(check_ws(ws, ws_bytes, quantize_ws_bytes()));
-  return launch_quantize(x, dt, rows, cols, rowwise, colwise, ws, as_stream(stream));
+  return FS4_OK;
 }
+}  // namespace fs4
+
+extern "C" {
 
 size_t fs4_abs_quantile_workspace_bytes(int64_t) { return abs_quantile_ws_bytes(); }
 

@@ -94,6 +94,9 @@ inline fs4_nvfp4 carve_view(Carver &c, int64_t rows, int64_t cols) {
 // Launchers (defined in the .hip files)
 constexpr int kAmaxPartials = 1024;      // max partial maxima written by the amax pass
 size_t quantize_ws_bytes();
+// fs4_quantize's argument checks (everything but the workspace), host only
+fs4_status check_quantize_args(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
+                               const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise);
 fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                            const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                            void *ws, hipStream_t s);

@@ -341,3 +341,18 @@ def test_binding_rejects_mismatched_factor_shapes():
         fs4.linear_fwd(X, _cpu_view(32, 64), U, V)
     with pytest.raises(ValueError):
         fs4.linear_fwd(X, _cpu_view(32, 64), U, None)
+
+
+def test_quantize_noalloc_validation():
+    """The no-workspace quantizer checks its arguments as fs4_quantize does,
+    on the host, before it touches the device."""
+    f = lambda x=A16, dt=0, rows=64, cols=64, rv="ok", cv="ok": lib.fs4_quantize_noalloc(
+        x, dt, rows, cols, ctypes.byref(view(rows, cols)) if rv == "ok" else rv,
+        ctypes.byref(view(cols, rows)) if cv == "ok" else cv, None)
+    assert f(dt=7) == DTYPE
+    assert f(rows=-16) == SHAPE
+    assert f(rv=None, cv=None) == NULL
+    assert f(x=None) == NULL
+    assert f(x=A16 + 4) == ALIGN
+    assert f(cols=40, cv=None) == SHAPE
+    assert lib.fs4_quantize_noalloc_scratch_bytes() >= lib.fs4_quantize_workspace_bytes(64, 64)
