@@ -92,3 +92,78 @@ def gemm_full_check(got, qa, qb, alpha=1.0, extra=None, extra_abs=None, rows=102
             den += extra_abs(i0, i1)
         worst = max(worst, oracle.rel_err(got[i0:i1], ref, den))
     return worst
+
+
+def _directed_f32(v64, up):
+    """float64 -> float32 rounded away from zero (up) or toward zero."""
+    v32 = v64.astype(np.float32)
+    back = v32.astype(np.float64)
+    mag, mag32 = np.abs(v64), np.abs(back)
+    fix = (mag32 < mag) if up else (mag32 > mag)
+    toward = np.where(np.signbit(v64), -np.inf, np.inf) if up else np.zeros_like(v64)
+    v32 = np.where(fix, np.nextafter(v32, toward.astype(np.float32)), v32)
+    return v32.astype(np.float32)
+
+
+def quantization_allowance(x_ref, eps):
+    """How far the dequantized NVFP4 views of any x' with |x' - x_ref| <= eps
+    (elementwise) can lie from those of x_ref.
+
+    Two correct implementations that sum in different orders give float32
+    results a few ulps apart; a quantization decision whose input lies that
+    close to a rounding boundary (tensor scale, block scale or element code)
+    may then come out either way, and both are correct.  Every decision is
+    monotone in the magnitudes it reads, so the extremes are reached by
+    shrinking or growing every magnitude by eps (this bounds each element
+    exactly while its block scale is stable; where the block scale itself is
+    ambiguous it bounds the two scale candidates at the edges of the box).
+    Returns (Q_row, Q_col, dQ_row, dQ_col): the dequantized row- and
+    column-wise views of x_ref (float64, Q_col in x^T's layout) and the
+    elementwise bounds of their change."""
+    from oracle.quantize import dequantize
+    x = np.asarray(x_ref, dtype=np.float32).astype(np.float64)
+    e = np.asarray(eps, dtype=np.float64)
+    mag = np.abs(x)
+    sgn = np.where(np.signbit(x), -1.0, 1.0)
+    lo = _directed_f32(sgn * np.maximum(mag - e, 0.0), up=False)
+    hi = _directed_f32(sgn * (mag + e), up=True)
+    ref = oracle.quantize(x.astype(np.float32))
+    outs = [dequantize(ref[0]), dequantize(ref[1])]
+    d = [np.zeros_like(outs[0]), np.zeros_like(outs[1])]
+    for alt in (lo, hi):
+        q = oracle.quantize(alt)
+        for i in range(2):
+            d[i] = np.maximum(d[i], np.abs(dequantize(q[i]) - outs[i]))
+    return outs[0], outs[1], d[0], d[1]
+
+
+def ns_step_bounds(x_k, st, a, b, c, tol, clip_p=None):
+    """Per-element bounds for one NVFP4 Newton-Schulz step computed by another
+    correct implementation from the same iterate x_k: its A within
+    tol * A_D of the oracle's; B within tol * B_D plus what any A within that
+    bound can change through the quantization of A; X' within tol * X_D plus
+    what any such B can change through the quantization of B.  (The iterate's
+    own views are bit-exact on both sides; clip_p is the clip value of its
+    quantized copy when clipping is on.)"""
+    from oracle.newton_schulz import clip_abs
+    eps_a = tol * st["A_D"]
+    qar, qac, dqar, dqac = quantization_allowance(st["A"], eps_a)
+    allow_b = abs(b) * eps_a + abs(c) * (dqar @ (np.abs(qac) + dqac).T + np.abs(qar) @ dqac.T)
+    eps_b = tol * st["B_D"] + allow_b
+    _, _, dqbr, _ = quantization_allowance(st["B"], eps_b)
+    xq = np.asarray(x_k, dtype=np.float32) if clip_p is None else clip_abs(x_k, clip_p)
+    _, x_col, _ = oracle.quantize(xq, rowwise=False, colwise=True)
+    from oracle.quantize import dequantize
+    allow_x = dqbr @ np.abs(dequantize(x_col)).T
+    return eps_a, eps_b, tol * st["X_D"] + allow_x
+
+
+def within(got, ref, bound):
+    """max |got - ref| / bound (0/0 counts as 0; a nonzero difference over a
+    zero bound as inf)."""
+    diff = np.abs(np.asarray(got, np.float64) - ref)
+    bound = np.asarray(bound, np.float64)
+    zero = bound == 0
+    if np.any(diff[zero] != 0):
+        return float("inf")
+    return float(np.max(diff[~zero] / bound[~zero])) if np.any(~zero) else 0.0

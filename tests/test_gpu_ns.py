@@ -5,7 +5,8 @@ correct implementations that differ only in fp32 summation order drift apart
 over several steps.  Parity is therefore checked one step at a time: the HIP
 path is started (normalize=0, steps=1) from the oracle's own iterate X_k and
 its A, B and X_{k+1} are compared with the oracle's step from the same X_k,
-normalised by sum |a||b| (+ |b A| and |a X| for the elementwise terms).
+normalised by sum |a||b| (+ |b A| and |a X| for the elementwise terms), with
+the allowance of tests/gpu_util.ns_step_bounds for B and X_{k+1}.
 """
 import numpy as np
 import pytest
@@ -13,12 +14,13 @@ import torch
 
 import oracle
 import synth
-from gpu_util import need_gpu, dev_bf16, dev_f32, print_case, f32
+from gpu_util import need_gpu, dev_bf16, dev_f32, print_case, f32, ns_step_bounds, within
 from oracle.newton_schulz import MUON_ABC
 
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-3
+TIGHT = 1e-5
 
 
 @pytest.mark.parametrize("m,n", [(192, 512), (80, 208)])
@@ -44,19 +46,26 @@ def test_zero_steps_without_normalization_is_a_copy():
 
 @pytest.mark.parametrize("m,n", [(192, 512), (768, 2048)])
 def test_per_step_parity(m, n):
+    """Each step from the oracle's own iterate X_k: A within 1e-5 of its
+    normaliser (both sides multiply the same bit-exact views of X_k); B and
+    X' within the bounds of tests/gpu_util.ns_step_bounds, which add to the
+    1e-5 bar what any A (then B) within that bar can change through its
+    quantization (a decision on a tie may come out either way for two
+    correct summation orders)."""
     fs4 = need_gpu()
     print_case(test="ns_step", m=m, n=n)
     g = synth.ns_input(seed=5, m=m, n=n)
     xs, steps = oracle.newton_schulz(f32(g), 5)
-    a, b, c = MUON_ABC
     for k in range(5):
         X, tX, tA, tB = fs4.newton_schulz(dev_f32(xs[k]), steps=1, normalize=False, trace=True)
         st = steps[k]
-        eA = oracle.rel_err(tA[0].cpu().numpy(), st["A64"], st["A_D"])
-        eB = oracle.rel_err(tB[0].cpu().numpy(), st["B64"], st["B_D"])
-        eX = oracle.rel_err(X.cpu().numpy(), st["X64"], st["X_D"])
-        print("step", k, "errA %.2e errB %.2e errX %.2e" % (eA, eB, eX), flush=True)
-        assert eA <= TOL and eB <= TOL and eX <= TOL, (k, eA, eB, eX)
+        Ag, Bg, Xg = tA[0].cpu().numpy(), tB[0].cpu().numpy(), X.cpu().numpy()
+        eps_a, eps_b, eps_x = ns_step_bounds(xs[k], st, *MUON_ABC, tol=TIGHT)
+        rA, rB, rX = within(Ag, st["A64"], eps_a), within(Bg, st["B64"], eps_b), within(Xg, st["X64"], eps_x)
+        eB, eX = oracle.rel_err(Bg, st["B64"], st["B_D"]), oracle.rel_err(Xg, st["X64"], st["X_D"])
+        print("step", k, "A %.2e B %.2e X %.2e of their bounds; errB %.2e errX %.2e" % (rA, rB, rX, eB, eX),
+              flush=True)
+        assert rA <= 1.0 and rB <= 1.0 and rX <= 1.0, (k, rA, rB, rX)
 
 
 def test_full_size_first_product_sampled():

@@ -1,19 +1,18 @@
 """GPU parity of the Q-Root outlier clipping: the |x| quantile (bit-exact:
 it is a selection, an element of |x|), the clipped quantizer (codes and
 scales bit-exact, as for the plain quantizer), and Newton-Schulz with the
-iterate clipped at its p99 (per step, within the GEMM tolerance of the
-plain NS tests)."""
+iterate clipped at its p99 (per step, from the oracle's iterates)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from gpu_util import assert_view_equal, dev_bf16, dev_f32, f32, need_gpu, print_case
+from gpu_util import assert_view_equal, dev_bf16, dev_f32, f32, need_gpu, ns_step_bounds, print_case, within
 from oracle.newton_schulz import MUON_ABC, abs_quantile, clip_abs
 
 pytestmark = pytest.mark.gpu
-TOL = 1e-3
+TIGHT = 1e-5
 
 
 def _inputs(kind, n, seed):
@@ -88,36 +87,30 @@ def test_quantize_clipped_is_bit_exact(rows, cols, bf16):
 
 @pytest.mark.parametrize("m,n", [(192, 512), (768, 2048)])
 def test_clipped_ns_per_step(m, n):
-    """Each product of a clipped step is checked from the GPU's own input to
-    it: A from the shared X_k, B from the GPU's A (re-quantized by the
-    oracle), X_{k+1} from the GPU's B.  A last-bit difference in fp32 A can
-    move one E4M3 block scale across a tie (the oracle alone reproduces it:
-    recomputing A in another summation order flips one block scale and moves
-    B by ~1e-2 of its normaliser at 768 x 2048), so the quantization
-    decisions must be taken on the same values on both sides."""
-    from oracle.linear import gemm_nt, gemm_nt_abs
+    """One clipped step at a time from the oracle's own iterate X_k: A (from
+    the shared, bit-exact clipped views of X_k) within 1e-5 of its
+    normaliser; B and X' against the oracle's own B and X' within the bounds
+    of tests/gpu_util.ns_step_bounds.  A last-bit difference in the fp32 A
+    (the MFMA's summation order against the oracle's rounded exact sum) can
+    move an E4M3 block scale of Q(A) across a tie, which moves B by ~1e-2 of
+    its normaliser at 768 x 2048 (a float32 summation on the CPU does the
+    same); both results are correct, and the bounds admit what any A within
+    the 1e-5 bar can change through its quantization, and no more.  Every
+    expected value and bound comes from the oracle's values alone."""
     fs4 = need_gpu()
     print_case(test="ns_clip_step", m=m, n=n)
     g = synth.ns_input(seed=7, m=m, n=n)
-    a, b, c = MUON_ABC
     xs, steps = oracle.newton_schulz(f32(g), 5, clip_q=0.99)
     for k in range(5):
         X, tX, tA, tB = fs4.newton_schulz(dev_f32(xs[k]), steps=1, normalize=False, trace=True, clip_q=0.99)
         st = steps[k]
+        eps_a, eps_b, eps_x = ns_step_bounds(xs[k], st, *MUON_ABC, tol=TIGHT, clip_p=st["P"])
         Ag, Bg, Xg = tA[0].cpu().numpy(), tB[0].cpu().numpy(), X.cpu().numpy()
-        eA = oracle.rel_err(Ag, st["A64"], st["A_D"])
-        ar, ac, _ = oracle.quantize(Ag)
-        b_ref = b * Ag.astype(np.float64) + c * gemm_nt(ar, ac)
-        b_d = abs(b) * np.abs(Ag.astype(np.float64)) + abs(c) * gemm_nt_abs(ar, ac)
-        eB = oracle.rel_err(Bg, b_ref, b_d)
-        br, _, _ = oracle.quantize(Bg, rowwise=True, colwise=False)
-        _, xcol, _ = oracle.quantize(clip_abs(xs[k], st["P"]), rowwise=False, colwise=True)
-        x64 = xs[k].astype(np.float64)
-        x_ref = a * x64 + gemm_nt(br, xcol)
-        x_d = abs(a) * np.abs(x64) + gemm_nt_abs(br, xcol)
-        eX = oracle.rel_err(Xg, x_ref, x_d)
-        print("step", k, "p %.4e errA %.2e errB %.2e errX %.2e" % (st["P"], eA, eB, eX), flush=True)
-        assert eA <= TOL and eB <= TOL and eX <= TOL, (k, eA, eB, eX)
+        rA, rB, rX = within(Ag, st["A64"], eps_a), within(Bg, st["B64"], eps_b), within(Xg, st["X64"], eps_x)
+        print("step", k, "p %.4e A %.2e B %.2e X %.2e of their bounds; errB %.2e errX %.2e" % (
+            st["P"], rA, rB, rX, oracle.rel_err(Bg, st["B64"], st["B_D"]), oracle.rel_err(Xg, st["X64"], st["X_D"])),
+            flush=True)
+        assert rA <= 1.0 and rB <= 1.0 and rX <= 1.0, (k, rA, rB, rX)
 
 
 def test_clip_at_the_maximum_equals_plain_ns():

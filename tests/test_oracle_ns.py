@@ -190,3 +190,55 @@ def test_ns_step_normalisers_equal_the_products_without_cancellation():
     xn = oracle.ns_normalize(x)[0]          # ||X||_F = 1: A^2 is as large as A
     stq = oracle.ns_step(xn, *MUON_ABC)
     assert np.all(stq["B_D"] >= np.abs(stq["B64"])) and np.any(stq["B_D"] > 1.3 * np.abs(stq["B64"]))
+
+
+def _other_order_step(x, abc, clip_q=None):
+    """One quantized step as another correct implementation computes it: the
+    same quantized operands, products summed in float32 (BLAS order) instead
+    of exactly, A stored exactly symmetric."""
+    from oracle.newton_schulz import abs_quantile, clip_abs
+    from oracle.quantize import dequantize
+    a, b, c = abc
+    xq = x if clip_q is None else clip_abs(x, abs_quantile(x, clip_q))
+    xr, xc, _ = oracle.quantize(xq)
+    d = dequantize(xr).astype(np.float32)
+    A = d @ d.T
+    A = np.triu(A) + np.triu(A, 1).T
+    ar, ac, _ = oracle.quantize(A)
+    B = (np.float32(b) * A + np.float32(c) * (dequantize(ar).astype(np.float32) @ dequantize(ac).astype(np.float32).T))
+    br, _, _ = oracle.quantize(B.astype(np.float32), colwise=False)
+    Xn = np.float32(a) * x + dequantize(br).astype(np.float32) @ dequantize(xc).astype(np.float32).T
+    return A.astype(np.float32), B.astype(np.float32), Xn.astype(np.float32)
+
+
+@pytest.mark.parametrize("clip_q", [None, 0.99])
+def test_step_bounds_cover_another_summation_order(clip_q):
+    """The per-element bounds the GPU tests use for a Newton-Schulz step
+    (tests/gpu_util.ns_step_bounds): another correct implementation (float32
+    sums in another order) lies within them at every step, also where its A
+    flips a quantization decision of the oracle's and moves B or X' by far
+    more than 1e-3 of the normaliser (this seed does so at 768 x 2048, with
+    and without clipping).  In the first two steps an error of 1e-4 of the
+    normaliser where the bound is tightest breaks them; later, as B's
+    entries cancel, the allowance B's box passes on to X' widens."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from gpu_util import ns_step_bounds, within
+    g = synth.bf16_to_f32(synth.ns_input(seed=7, m=768, n=2048))
+    xs, steps = oracle.newton_schulz(g, 4, clip_q=clip_q)
+    worst = 0.0
+    for k in range(4):
+        st = steps[k]
+        eps_a, eps_b, eps_x = ns_step_bounds(xs[k], st, *MUON_ABC, tol=1e-5, clip_p=st["P"])
+        A, B, Xn = _other_order_step(xs[k], MUON_ABC, clip_q)
+        assert within(A, st["A64"], eps_a) <= 1.0, k
+        assert within(B, st["B64"], eps_b) <= 1.0, k
+        assert within(Xn, st["X64"], eps_x) <= 1.0, k
+        worst = max(worst, oracle.rel_err(B, st["B64"], st["B_D"]), oracle.rel_err(Xn, st["X64"], st["X_D"]))
+        for got, ref, eps, den in ((B, st["B64"], eps_b, st["B_D"]), (Xn, st["X64"], eps_x, st["X_D"])) * (k < 2):
+            bad = got.astype(np.float64).copy()
+            i = np.unravel_index(np.argmin(np.where(den > 0, eps / np.where(den > 0, den, 1), np.inf)), bad.shape)
+            bad[i] += 1e-4 * den[i]
+            assert within(bad, ref, eps) > 1.0, k
+    assert worst > 1e-3          # the decision flips the bounds exist for do occur
