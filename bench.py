@@ -67,9 +67,13 @@ def step_flops(m=M, k=K, n=N, r=R_RANK):
     return main + low
 
 
-def quantizer_bytes(rows, cols, in_bytes=2):
-    # one read of the input, both layouts' codes and scales, the tensor scale
-    return rows * cols * in_bytes + 2 * (rows * cols // 2 + rows * cols // 16) + 4
+def quantizer_bytes(rows, cols, in_bytes=2, layouts=2):
+    # one read of the input, each layout's codes and scales, the tensor scale
+    return rows * cols * in_bytes + layouts * (rows * cols // 2 + rows * cols // 16) + 4
+
+
+def fwd_flops(m=M, k=K, n=N, r=R_RANK):
+    return 2.0 * m * n * k + 2.0 * (m * k * r + m * r * n)
 
 
 def ns_flops(m=3072, n=8192, steps=5):
@@ -232,10 +236,121 @@ def main():
         torch.cuda.synchronize()
         q_ms = float(np.mean([s.elapsed_time(e) for s, e in qe]))
         q_gbs = quantizer_bytes(rows_q, cols_q) / (q_ms * 1e-3) / 1e9
+        for j in range(qreps):
+            qe[j][0].record(stream)
+            fs4.quantize(copies[j % len(copies)], colwise=False, out_row=qrow)
+            qe[j][1].record(stream)
+        torch.cuda.synchronize()
+        r_ms = float(np.mean([s.elapsed_time(e) for s, e in qe]))
+        r_bytes = quantizer_bytes(rows_q, cols_q, layouts=1)
         return {"workload": "4096x4096 bf16 ~N(0,1), 0.1% x50; row+col layouts",
                 "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(q_gbs / PEAK_HBM_GBS, 4), "us_per_call": round(q_ms * 1e3, 2),
-                "bytes_per_call": quantizer_bytes(rows_q, cols_q)}
+                "bytes_per_call": quantizer_bytes(rows_q, cols_q),
+                "row_only": {"us_per_call": round(r_ms * 1e3, 2), "bytes_per_call": r_bytes,
+                             "achieved": round(r_bytes / (r_ms * 1e-3) / 1e9, 1),
+                             "frac": round(r_bytes / (r_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+
+    def fwd_leg(reps=20):
+        # the 3B forward alone (quantize X, T = X V^T, Y = Q(X) Q(R)^T + T U^T),
+        # R quantized beforehand (its quantization is timed in the step)
+        fs4.quantize(Rw, out_row=R_row, out_col=R_col)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        call = lambda: fs4.linear_fwd(X, R_row, U, V, out=Y)
+        for _ in range(5):
+            call()
+        ms = time_calls(call, reps)
+        fl = fwd_flops()
+        return {"workload": "3B-shape forward: X 8192x3072 bf16, R pre-quantized, rank 32",
+                "achieved": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "ms_per_call": round(ms, 4),
+                "gflop": round(fl / 1e9, 2)}
+
+    def ceiling_leg(reps=10):
+        # the library GEMM ceiling: torch.matmul (hipBLASLt) on plain BF16 and
+        # FP16 operands at the three step shapes (context for the block-scaled
+        # GEMM; run, never disassembled)
+        out = {}
+        for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+            tms = []
+            for (m_, n_, k_) in ((M, N, K), (M, K, N), (N, K, M)):
+                a_ = torch.randn((m_, k_), device=dev, dtype=dt)
+                b_ = torch.randn((k_, n_), device=dev, dtype=dt)
+                c_ = torch.empty((m_, n_), device=dev, dtype=dt)
+                for _ in range(3):
+                    torch.matmul(a_, b_, out=c_)
+                tms.append(time_calls(lambda: torch.matmul(a_, b_, out=c_), reps))
+                del a_, b_, c_
+            ms = float(np.mean(tms))
+            out[name] = {"avg_ms": round(ms, 4), "achieved": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                         "unit": "TFLOP/s", "frac": round(2.0 * M * N * K / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        out["what"] = "torch.matmul (hipBLASLt) at 8192x8192x3072, 8192x3072x8192 (x2), same box"
+        return out
+
+    def ns_legs():
+        out = {}
+        G = to_bf16(synth.ns_input())
+        m_, n_ = G.shape
+        Xns = torch.empty((m_, n_), dtype=torch.float32, device=dev)
+        shape_abc, shape_d = fs4.ns_shape_coefficients(m_, n_)
+        plan = fs4.newton_schulz_plan(m_, n_)
+        executed = 5 * sum(p["tiles"] * p["tile"][0] * p["tile"][1] * 2.0 * k_
+                           for p, k_ in ((plan["A"], n_), (plan["A2"], m_), (plan["update"], m_)))
+        for name, abc, cq in (("newton_schulz", fs4.MUON_ABC, 0.0), ("newton_schulz_clip_p99", fs4.MUON_ABC, 0.99),
+                              ("newton_schulz_shape", shape_abc, 0.0), ("newton_schulz_shape_p99", shape_abc, 0.99)):
+            call = lambda: fs4.newton_schulz(G, steps=5, abc=abc, out=Xns, clip_q=cq)
+            for _ in range(3):
+                call()
+            ms = time_calls(call, 5)
+            tf = ns_flops() / (ms * 1e-3) / 1e12
+            out[name] = {"ms_per_call": round(ms, 4), "achieved": round(tf, 2), "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "achieved_executed": round(executed / (ms * 1e-3) / 1e12, 2),
+                         "abc": [round(float(v), 6) for v in abc], "clip_q": cq}
+        out["newton_schulz"]["workload"] = ("G 3072x8192 bf16 ~N(0,1), 5 quintic steps, all GEMM operands NVFP4; "
+                                            "'achieved' on the dense count (%.1f GFLOP), 'achieved_executed' on the "
+                                            "products the symmetric A and A^2 actually run (%.1f GFLOP)"
+                                            % (ns_flops() / 1e9, executed / 1e9))
+        out["newton_schulz_shape"]["polar_distance"] = shape_d
+        out["ns_error_vs_fp64"] = ns_error(G, shape_abc)
+        return out
+
+    def ns_error(G, shape_abc):
+        # NVFP4 iterates against the unquantized iteration with the same
+        # coefficients, computed in float64 (torch on the device: measurement
+        # only).  'accumulated': ||X_k - X64_k||_F / ||X64_k||_F along the two
+        # trajectories; 'per_step': one NVFP4 step from the fp32-rounded fp64
+        # iterate against the fp64 step from the same input; 'vs_polar':
+        # ||X_5 - U V^T||_F / ||U V^T||_F for both.
+        g64 = G.double()
+        x0 = g64 / (torch.linalg.norm(g64) + 1e-7)
+        u_, _, vt_ = torch.linalg.svd(x0, full_matrices=False)
+        polar = u_ @ vt_
+        res = {}
+        for name, abc, cq in (("muon", fs4.MUON_ABC, 0.0), ("muon_p99", fs4.MUON_ABC, 0.99),
+                              ("shape", shape_abc, 0.0), ("shape_p99", shape_abc, 0.99)):
+            a_, b_, c_ = (float(v) for v in abc)
+
+            def step64(x):
+                A = x @ x.T
+                return a_ * x + (b_ * A + c_ * (A @ A)) @ x
+            traj = [x0]
+            for _ in range(5):
+                traj.append(step64(traj[-1]))
+            _, tX, _, _ = fs4.newton_schulz(G, steps=5, abc=abc, trace=True, clip_q=cq)
+            acc = [float(torch.linalg.norm(tX[k].double() - traj[k]) / torch.linalg.norm(traj[k])) for k in range(1, 6)]
+            per = []
+            for k in range(5):
+                xk = traj[k].float()
+                y = fs4.newton_schulz(xk, steps=1, abc=abc, normalize=False, clip_q=cq)
+                ref = step64(xk.double())
+                per.append(float(torch.linalg.norm(y.double() - ref) / torch.linalg.norm(ref)))
+            res[name] = {"accumulated": [round(v, 5) for v in acc], "per_step": [round(v, 5) for v in per],
+                         "vs_polar_nvfp4": round(float(torch.linalg.norm(tX[5].double() - polar) / torch.linalg.norm(polar)), 5),
+                         "vs_polar_fp64": round(float(torch.linalg.norm(traj[5] - polar) / torch.linalg.norm(polar)), 5)}
+            del tX
+        torch.cuda.synchronize()
+        return res
 
     if a.only == "gemm":
         print(json.dumps({"only": "gemm", "roofline": gemm_leg(max(3, a.steps))}), flush=True)
@@ -340,28 +455,14 @@ def main():
         out["roofline"] = gemm_leg(max(3, a.steps))
         out["quantizer"] = quantizer_leg()
 
-        # ---- NVFP4 Newton-Schulz, 3072 x 8192, 5 steps ------------------------
-        G = to_bf16(synth.ns_input())
-        Xns = torch.empty((3072, 8192), dtype=torch.float32, device=dev)
-        ns_call = lambda: fs4.newton_schulz(G, steps=5, out=Xns)
-        for _ in range(3):
-            ns_call()
-        ns_ms = time_calls(ns_call, 5)
-        ns_tf = ns_flops() / (ns_ms * 1e-3) / 1e12
-        out["newton_schulz"] = {"workload": "G 3072x8192 bf16 ~N(0,1), 5 quintic steps, all GEMM operands NVFP4",
-                                "achieved": round(ns_tf, 2), "unit": "TFLOP/s",
-                                "frac": round(ns_tf / PEAK_BF16_TFLOPS, 4), "ms_per_call": round(ns_ms, 4)}
-        # the Q-Root variant: the iterate's quantized copy clipped at its p99
-        nsc_call = lambda: fs4.newton_schulz(G, steps=5, out=Xns, clip_q=0.99)
-        nsc_call()
-        nsc_ms = time_calls(nsc_call, 5)
-        out["newton_schulz_clip_p99"] = {"ms_per_call": round(nsc_ms, 4),
-                                         "achieved": round(ns_flops() / (nsc_ms * 1e-3) / 1e12, 2),
-                                         "unit": "TFLOP/s"}
-
+        # the small, launch-bound calls first: run after the legs that call
+        # hipBLASLt and the eigen-solver behind the polar factor, the subspace
+        # projection measured 15x slower (its short kernels waited on the host)
         out.update(lora_legs())
-
         out.update(adamw_legs())
+        out["forward"] = fwd_leg()
+        out.update(ns_legs())
+        out["library_gemm_ceiling"] = ceiling_leg()
 
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline()

@@ -198,6 +198,20 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
                              float *X_out, float *trace_X, float *trace_A, float *trace_B,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* fs4_ns_shape_coefficients — host only, launches nothing: the quintic
+ * coefficients (a, b, c) for an m x n momentum, the shape-dependent
+ * coefficients of [FS4 §2.3] (Q-Root) in this reading: they minimise the mean
+ * squared distance of `steps` quintic steps to the polar factor (all singular
+ * values 1), averaged over the Marchenko-Pastur singular-value law of a
+ * Frobenius-normalised m x n Gaussian matrix; found by Nelder-Mead from
+ * Muon's (3.4445, -4.7750, 2.0315).  m and n may come in either order.
+ *   abc           host float[3] receives (a, b, c), for fs4_newton_schulz
+ *   distance_out  host double, nullable: the minimised mean squared distance
+ * Errors: FS4_ERR_NULL (abc), FS4_ERR_ARG (m or n < 1, steps outside 1..16).
+ * About 0.1 s of host time; callers compute it once per shape.
+ */
+fs4_status fs4_ns_shape_coefficients(int64_t m, int64_t n, int steps, float *abc, double *distance_out);
+
 /* fs4_newton_schulz_plan — introspection, launches nothing: the tile plans of
  * the three products of one fs4_newton_schulz step on an m x n iterate, in
  * the order A = Q(X) Q(X)^T (m x m x n, symmetric), A^2 (m x m x m,

@@ -115,3 +115,72 @@ def newton_schulz_fp64(g, steps: int = 5, abc=MUON_ABC, eps: float = NS_EPS):
         bm = b * am + c * (am @ am)
         x = a * x + bm @ x
     return x
+
+
+# ---- shape-dependent coefficients (Q-Root) ----------------------------------------
+# [FS4 §2.3] stabilises the NVFP4 iteration with (a, b, c) "optimised for the
+# matrix aspect ratio" but prints neither the coefficients nor the criterion.
+# Reading: for an m x n momentum (m <= n) the coefficients minimise the mean
+# squared distance of the 5-step quintic's singular values to 1 (the polar
+# factor's), averaged over the singular-value law of a Frobenius-normalised
+# m x n Gaussian matrix, which the Marchenko-Pastur law gives in closed form:
+# the eigenvalues lam of G G^T / n, y = m / n, have density
+#     f(lam) = sqrt((lam_+ - lam)(lam - lam_-)) / (2 pi y lam),
+#     lam_(+/-) = (1 +/- sqrt(y))^2,
+# and since ||G||_F^2 ~ m n, the normalised singular values are
+# sigma = sqrt(lam / m).  The minimisation starts from Muon's quintic.
+
+
+def mp_density(lam, y: float) -> np.ndarray:
+    """Marchenko-Pastur density of the eigenvalues of G G^T / n for an m x n
+    (m <= n, y = m / n) matrix of independent N(0, 1) entries."""
+    lam = np.asarray(lam, dtype=np.float64)
+    lo, hi = (1.0 - np.sqrt(y)) ** 2, (1.0 + np.sqrt(y)) ** 2
+    inside = (lam > lo) & (lam < hi)
+    out = np.zeros_like(lam)
+    out[inside] = np.sqrt((hi - lam[inside]) * (lam[inside] - lo)) / (2.0 * np.pi * y * lam[inside])
+    return out
+
+
+def mp_nodes(m: int, n: int, points: int = 400):
+    """Quadrature nodes and weights over the normalised singular values of an
+    m x n Gaussian matrix: Gauss-Chebyshev (second kind) in lam on
+    [lam_-, lam_+], which absorbs the square-root edges of the density."""
+    y = m / n
+    lo, hi = (1.0 - np.sqrt(y)) ** 2, (1.0 + np.sqrt(y)) ** 2
+    k = np.arange(1, points + 1)
+    t = np.cos(k * np.pi / (points + 1))                    # nodes of U_points in (-1, 1)
+    w_t = np.pi / (points + 1) * np.sin(k * np.pi / (points + 1)) ** 2
+    lam = 0.5 * (hi + lo) + 0.5 * (hi - lo) * t
+    # integral of g(lam) sqrt((hi-lam)(lam-lo)) dlam = ((hi-lo)/2)^2 sum w_t g(lam)
+    w = ((hi - lo) / 2.0) ** 2 * w_t / (2.0 * np.pi * y * lam)
+    return np.sqrt(lam / m), w
+
+
+def quintic_power(sigma, abc, steps: int = 5) -> np.ndarray:
+    """p applied `steps` times to singular values, p(s) = a s + b s^3 + c s^5."""
+    a, b, c = abc
+    s = np.asarray(sigma, dtype=np.float64)
+    for _ in range(steps):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
+
+
+def polar_distance(abc, m: int, n: int, steps: int = 5, points: int = 400) -> float:
+    """Mean over the m x n spectrum of (p^steps(sigma) - 1)^2: the expected
+    squared Frobenius distance per singular value between the unquantized
+    iteration and the polar factor."""
+    s, w = mp_nodes(m, n, points)
+    return float(np.sum(w * (quintic_power(s, abc, steps) - 1.0) ** 2) / np.sum(w))
+
+
+def shape_coefficients(m: int, n: int, steps: int = 5, start=MUON_ABC):
+    """(a, b, c) for an m x n momentum (m <= n): the minimiser of
+    polar_distance from Muon's quintic (Nelder-Mead, tight tolerances)."""
+    from scipy.optimize import minimize
+    if m > n:
+        m, n = n, m
+    f = lambda v: polar_distance(tuple(v), m, n, steps)
+    res = minimize(f, np.asarray(start, dtype=np.float64), method="Nelder-Mead",
+                   options={"xatol": 1e-10, "fatol": 1e-14, "maxiter": 20000, "maxfev": 40000})
+    return tuple(float(v) for v in res.x)

@@ -53,7 +53,7 @@ EXPORTS = [
     "fs4_vstate_encode_workspace_bytes", "fs4_vstate_encode", "fs4_vstate_decode",
     "fs4_mstate_encode_workspace_bytes", "fs4_mstate_encode", "fs4_mstate_decode",
     "fs4_workspace_bytes", "fs4_status_str", "fs4_version", "fs4_gemm_plan", "fs4_newton_schulz_plan",
-    "fs4_quantize_noalloc", "fs4_quantize_noalloc_scratch_bytes",
+    "fs4_quantize_noalloc", "fs4_quantize_noalloc_scratch_bytes", "fs4_ns_shape_coefficients",
 ]
 
 
@@ -112,6 +112,8 @@ _sig("fs4_newton_schulz", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_
 _sig("fs4_abs_quantile_workspace_bytes", _SZ, [_I64])
 _sig("fs4_abs_quantile", ctypes.c_int, [_P, ctypes.c_int, _I64, ctypes.c_double, _P, _P, _SZ, _P])
 _sig("fs4_gemm_plan", ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(_I64)])
+_sig("fs4_ns_shape_coefficients", ctypes.c_int, [_I64, _I64, ctypes.c_int, ctypes.POINTER(_F),
+                                                 ctypes.POINTER(ctypes.c_double)])
 _sig("fs4_newton_schulz_plan", ctypes.c_int, [_I64, _I64, ctypes.POINTER(_I64)])
 _sig("fs4_quantize_clipped_workspace_bytes", _SZ, [_I64, _I64])
 _sig("fs4_quantize_clipped", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_double, _VP, _VP, _P,
@@ -559,6 +561,17 @@ def gemm_plan(M: int, N: int, K: int) -> dict:
     return {"tile": (out[0], out[1]), "tiles": out[2], "splits": out[3]}
 
 
+def ns_shape_coefficients(m: int, n: int, steps: int = 5):
+    """Shape-dependent quintic coefficients (a, b, c) for an m x n momentum
+    (the Q-Root reading: minimum mean squared distance of `steps` steps to
+    the polar factor over the Marchenko-Pastur spectrum), as float32 values
+    for newton_schulz(abc=...).  Returns (abc, distance)."""
+    abc = (_F * 3)()
+    dist = ctypes.c_double()
+    _check(_lib.fs4_ns_shape_coefficients(m, n, steps, abc, ctypes.byref(dist)), "fs4_ns_shape_coefficients")
+    return (abc[0], abc[1], abc[2]), dist.value
+
+
 def newton_schulz_plan(m: int, n: int) -> dict:
     """The tile plans of one Newton-Schulz step's products A, A^2 and the
     (transposed) update on an m x n iterate."""
@@ -576,4 +589,4 @@ __all__ = ["NVFP4", "quantize", "quantize_noalloc", "gemm_nt", "linear_fwd", "Li
            "newton_schulz", "lora_project", "lora_realign", "abs_quantile", "quantize_clipped",
            "vstate_encode", "vstate_decode", "mstate_encode", "mstate_decode", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
            "EXPORTS", "MUON_ABC",
-           "release_workspaces", "gemm_plan", "newton_schulz_plan"]
+           "release_workspaces", "gemm_plan", "newton_schulz_plan", "ns_shape_coefficients"]

@@ -356,3 +356,20 @@ def test_quantize_noalloc_validation():
     assert f(x=A16 + 4) == ALIGN
     assert f(cols=40, cv=None) == SHAPE
     assert lib.fs4_quantize_noalloc_scratch_bytes() >= lib.fs4_quantize_workspace_bytes(64, 64)
+
+
+def test_ns_shape_coefficients_match_the_oracle():
+    """The library's shape-dependent Newton-Schulz coefficients (host code:
+    its own Marchenko-Pastur quadrature and Nelder-Mead) agree with the
+    oracle's (scipy) to 1e-5, and so do the minimised distances."""
+    import numpy as np
+    from oracle.newton_schulz import polar_distance, shape_coefficients
+    for m, n in [(3072, 8192), (768, 2048), (192, 512), (1024, 1024), (8192, 3072)]:
+        abc, d = fs4.ns_shape_coefficients(m, n)
+        want = shape_coefficients(m, n)
+        assert np.allclose(abc, want, rtol=1e-5, atol=1e-6), (m, n, abc, want)
+        assert abs(d / polar_distance(want, min(m, n), max(m, n)) - 1.0) < 1e-4
+    out = (ctypes.c_float * 3)()
+    assert lib.fs4_ns_shape_coefficients(0, 16, 5, out, None) == ARG
+    assert lib.fs4_ns_shape_coefficients(16, 16, 0, out, None) == ARG
+    assert lib.fs4_ns_shape_coefficients(16, 16, 5, None, None) == NULL

@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 from gpu_util import need_gpu, dev_bf16, dev_f32, print_case, f32, ns_step_bounds, within
-from oracle.newton_schulz import MUON_ABC
+from oracle.newton_schulz import MUON_ABC, shape_coefficients
 
 pytestmark = pytest.mark.gpu
 
@@ -44,8 +44,12 @@ def test_zero_steps_without_normalization_is_a_copy():
     assert np.array_equal(X, f32(g))
 
 
-@pytest.mark.parametrize("m,n", [(192, 512), (768, 2048)])
-def test_per_step_parity(m, n):
+def _f32_abc(abc):
+    return tuple(float(np.float32(v)) for v in abc)
+
+
+@pytest.mark.parametrize("m,n,coef", [(192, 512, "muon"), (768, 2048, "muon"), (768, 2048, "shape")])
+def test_per_step_parity(m, n, coef):
     """Each step from the oracle's own iterate X_k: A within 1e-5 of its
     normaliser (both sides multiply the same bit-exact views of X_k); B and
     X' within the bounds of tests/gpu_util.ns_step_bounds, which add to the
@@ -53,14 +57,17 @@ def test_per_step_parity(m, n):
     quantization (a decision on a tie may come out either way for two
     correct summation orders)."""
     fs4 = need_gpu()
-    print_case(test="ns_step", m=m, n=n)
+    print_case(test="ns_step", m=m, n=n, coef=coef)
+    # shape: the oracle's shape-dependent (a, b, c) (Q-Root reading), as the
+    # float32 values both sides then use
+    abc = _f32_abc(MUON_ABC if coef == "muon" else shape_coefficients(m, n))
     g = synth.ns_input(seed=5, m=m, n=n)
-    xs, steps = oracle.newton_schulz(f32(g), 5)
+    xs, steps = oracle.newton_schulz(f32(g), 5, abc=abc)
     for k in range(5):
-        X, tX, tA, tB = fs4.newton_schulz(dev_f32(xs[k]), steps=1, normalize=False, trace=True)
+        X, tX, tA, tB = fs4.newton_schulz(dev_f32(xs[k]), steps=1, abc=abc, normalize=False, trace=True)
         st = steps[k]
         Ag, Bg, Xg = tA[0].cpu().numpy(), tB[0].cpu().numpy(), X.cpu().numpy()
-        eps_a, eps_b, eps_x = ns_step_bounds(xs[k], st, *MUON_ABC, tol=TIGHT)
+        eps_a, eps_b, eps_x = ns_step_bounds(xs[k], st, *abc, tol=TIGHT)
         rA, rB, rX = within(Ag, st["A64"], eps_a), within(Bg, st["B64"], eps_b), within(Xg, st["X64"], eps_x)
         eB, eX = oracle.rel_err(Bg, st["B64"], st["B_D"]), oracle.rel_err(Xg, st["X64"], st["X_D"])
         print("step", k, "A %.2e B %.2e X %.2e of their bounds; errB %.2e errX %.2e" % (rA, rB, rX, eB, eX),
