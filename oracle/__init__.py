@@ -34,6 +34,7 @@ newton_schulz   NVFP4 Newton-Schulz iteration (and the unquantized fp64 one)
 lora            Cholesky-QR, the subspace-constrained low-rank gradients and
                 the randomized-SVD realignment
 adamw           the Q-AdamW optimizer-state codecs (second and first moment)
+attention       NVFP4 mixed-precision attention (Q-Attn), forward and backward
 """
 from .formats import (E2M1_GRID, e2m1_decode, e2m1_rne_index, e4m3_decode, e4m3_rne_satfinite,
                       tensor_scale_from_amax)
@@ -42,6 +43,7 @@ from .linear import gemm_nt, gemm_nt_abs, linear_fwd, linear_bwd, rel_err
 from .newton_schulz import ns_normalize, ns_step, newton_schulz, newton_schulz_fp64, abs_quantile, clip_abs
 from .lora import cholesky_qr, subspace_project, lora_realign, bf16_rne
 from .adamw import vstate_encode, vstate_decode, mstate_encode, mstate_decode
+from .attention import attention_fwd, attention_bwd
 
 __all__ = [
     "E2M1_GRID", "e2m1_decode", "e2m1_rne_index", "e4m3_decode", "e4m3_rne_satfinite",

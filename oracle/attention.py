@@ -1,0 +1,123 @@
+"""NVFP4 mixed-precision attention, Q-Attn (oracle; test infrastructure only).
+
+[FS4 §2.4]: attention runs the products the pages call robust, Q K^T and the
+ones taking dS, on NVFP4 operands and keeps the softmax-sensitive ones, P V,
+P^T dO and dO V^T, in BF16; the quantized views of Q, K and V made in the
+forward are reused by the backward.
+
+Readings (the pages print no formulas):
+* Q, K, V, dO are BF16 tensors [G, S, D]: G = batch x heads independent
+  sequences of length S with head dimension D.  Causal attention (decoder
+  pretraining), softmax scale 1/sqrt(D).
+* Q and K are each quantized once, as the [G*S, D] matrix, with one tensor
+  scale: the row-wise view (blocks of 16 along D) serves Q K^T, the
+  column-wise view of each sequence (blocks of 16 along S, the same tensor
+  scale) serves the dS products.  V stays BF16: both products that read V
+  are in the BF16 list; its reused "view" is the BF16 tensor itself.
+* Forward: S = s_Q s_K Q_hat K_hat^T / sqrt(D) (exact), masked above the
+  diagonal; P = softmax(S) row by row; O = P V; LSE = log sum exp(S) per row.
+  The BF16 path rounds P to BF16 before P V (its error is the tolerance of
+  the GPU test); the oracle's O is the exact product.
+* Backward: P recomputed from the same quantized Q and K; dV = P^T dO;
+  dP = dO V^T; Delta = rowsum(dO * O); dS = P * (dP - Delta) (the softmax
+  gradient); dS is quantized once as the [G*S, S] matrix with one tensor
+  scale, row-wise (blocks along keys) for dQ = Q(dS) Q_col(K)^T / sqrt(D) and
+  column-wise (blocks along queries) for dK = Q(dS^T) Q_col(Q)^T / sqrt(D).
+  dS's quantization uses the exact dS here (float32-rounded, as a kernel
+  stores it).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .quantize import NVFP4, block_values, quantize, quantize_rows
+
+
+def _views_per_sequence(x32, G, S, D):
+    """One quantization of x [G*S, D]: its row-wise view, and the column-wise
+    view of each sequence (x_g^T [D, S] blocked along S) with the same tensor
+    scale."""
+    row, _, s_t = quantize(x32.reshape(G * S, D), rowwise=True, colwise=False)
+    cols = [quantize_rows(np.ascontiguousarray(x32[g].T), s_t) for g in range(G)]
+    return row, cols, s_t
+
+
+def _head_rows(view: NVFP4, g: int, S: int) -> NVFP4:
+    return NVFP4(view.codes[g * S:(g + 1) * S], view.scales[g * S:(g + 1) * S], view.tscale, S, view.cols)
+
+
+def causal_mask(S: int) -> np.ndarray:
+    """True where key j may be attended by query i (j <= i)."""
+    return np.tril(np.ones((S, S), dtype=bool))
+
+
+def attention_fwd(q, k, v, causal: bool = True):
+    """q, k, v float32 [G, S, D] holding BF16 values.  Returns dict: O
+    (float64), LSE (float64 [G, S]), P (float64 [G, S, S]), the O error
+    normaliser O_D = P |V| (what the BF16 rounding of P can move O by, per
+    unit of relative error), and the quantized views (Q_row, K_row, Q_col,
+    K_col per sequence)."""
+    G, S, D = q.shape
+    q_row, q_cols, _ = _views_per_sequence(q, G, S, D)
+    k_row, k_cols, _ = _views_per_sequence(k, G, S, D)
+    scale = 1.0 / np.sqrt(D)
+    st = float(q_row.tscale) * float(k_row.tscale) * scale
+    mask = causal_mask(S) if causal else np.ones((S, S), dtype=bool)
+    O = np.empty((G, S, D))
+    O_D = np.empty((G, S, D))
+    P_all = np.empty((G, S, S))
+    LSE = np.empty((G, S))
+    for g in range(G):
+        s = st * (block_values(_head_rows(q_row, g, S)) @ block_values(_head_rows(k_row, g, S)).T)
+        s = np.where(mask, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        l = e.sum(axis=1, keepdims=True)
+        p = e / l
+        v64 = v[g].astype(np.float64)
+        O[g] = p @ v64
+        O_D[g] = p @ np.abs(v64)
+        P_all[g] = p
+        LSE[g] = (m + np.log(l))[:, 0]
+    return {"O": O, "O_D": O_D, "LSE": LSE, "P": P_all, "scale": scale,
+            "Q_row": q_row, "K_row": k_row, "Q_col": q_cols, "K_col": k_cols}
+
+
+def attention_bwd(q, k, v, do, fwd=None, causal: bool = True):
+    """The backward from dO float32 [G, S, D] (BF16 values), with the
+    forward's quantized views and P.  Returns dict of dQ, dK, dV (float64),
+    dS (float64 [G, S, S], before its quantization) and normalisers
+    dQ_D, dK_D (sum |a||b| of the NVFP4 products), dV_D = P^T |dO|."""
+    G, S, D = q.shape
+    if fwd is None:
+        fwd = attention_fwd(q, k, v, causal)
+    P, O, scale = fwd["P"], fwd["O"], fwd["scale"]
+    dV = np.empty((G, S, D))
+    dV_D = np.empty((G, S, D))
+    dS = np.empty((G, S, S))
+    for g in range(G):
+        do64, v64 = do[g].astype(np.float64), v[g].astype(np.float64)
+        dV[g] = P[g].T @ do64
+        dV_D[g] = P[g].T @ np.abs(do64)
+        dP = do64 @ v64.T
+        delta = np.sum(do64 * O[g], axis=1, keepdims=True)
+        dS[g] = P[g] * (dP - delta)
+    ds32 = dS.astype(np.float32)
+    ds_row, _, s_ds = quantize(ds32.reshape(G * S, S), rowwise=True, colwise=False)
+    dQ = np.empty((G, S, D))
+    dK = np.empty((G, S, D))
+    dQ_D = np.empty((G, S, D))
+    dK_D = np.empty((G, S, D))
+    for g in range(G):
+        a = block_values(_head_rows(ds_row, g, S))                         # dS_g, blocks along keys
+        at = block_values(quantize_rows(np.ascontiguousarray(ds32[g].T), s_ds))   # dS_g^T, blocks along queries
+        kc = block_values(fwd["K_col"][g])                                 # K_g^T [D, S], blocks along keys
+        qc = block_values(fwd["Q_col"][g])                                 # Q_g^T [D, S], blocks along queries
+        sq = float(s_ds) * float(fwd["K_row"].tscale) * scale
+        sk = float(s_ds) * float(fwd["Q_row"].tscale) * scale
+        dQ[g] = sq * (a @ kc.T)
+        dQ_D[g] = sq * (np.abs(a) @ np.abs(kc).T)
+        dK[g] = sk * (at @ qc.T)
+        dK_D[g] = sk * (np.abs(at) @ np.abs(qc).T)
+    return {"dQ": dQ, "dK": dK, "dV": dV, "dS": dS, "dQ_D": dQ_D, "dK_D": dK_D, "dV_D": dV_D,
+            "dS_tscale": s_ds}
