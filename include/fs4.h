@@ -363,6 +363,28 @@ const char *fs4_status_str(fs4_status s);
 /* Library version string, e.g. "fs4 0.1 gfx950" (static storage). */
 const char *fs4_version(void);
 
+/* ---------------------------------------------------------------------------
+ * fs4_attention_fwd — NVFP4 mixed-precision attention forward, [FS4 §2.4]
+ * (Q-Attn): Q K^T on NVFP4 operands, P V in BF16, per sequence g < G:
+ *     S = s_Q s_K Q_hat_g K_hat_g^T / sqrt(D), masked above the diagonal
+ *         when causal != 0;  P = softmax(S) by rows;  O_g = P V_g (P rounded
+ *         to BF16, V BF16, fp32 accumulation);  LSE_g = log sum_j exp(S_ij)
+ *   Q_row, K_row  row-wise NVFP4 views of Q and K as [G*S][D] matrices (blocks
+ *                 along D; fs4_quantize of each; the same quantization's
+ *                 column-wise views serve the backward's dS products)
+ *   V        bf16 [G][S][D]
+ *   O        fp32 [G][S][D];  LSE fp32 [G][S], nullable
+ *   Vt_save  bf16 [G][D][S], nullable: receives V^T, the layout the P V
+ *            product reads (reused by a backward); without it V^T goes to the
+ *            workspace (fs4_attention_fwd_workspace_bytes)
+ *   D = 64 or 128; S a positive multiple of 16; G >= 1, G*S < 2^31.
+ * Errors: FS4_ERR_SHAPE, FS4_ERR_NULL, FS4_ERR_ALIGN, FS4_ERR_WORKSPACE.
+ */
+size_t fs4_attention_fwd_workspace_bytes(int64_t G, int64_t S, int64_t D);
+fs4_status fs4_attention_fwd(const fs4_nvfp4 *Q_row, const fs4_nvfp4 *K_row, const void *V, int64_t G,
+                             int64_t S, int64_t D, int causal, float *O, float *LSE, void *Vt_save,
+                             void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,9 +51,11 @@ def causal_mask(S: int) -> np.ndarray:
     return np.tril(np.ones((S, S), dtype=bool))
 
 
-def attention_fwd(q, k, v, causal: bool = True):
-    """q, k, v float32 [G, S, D] holding BF16 values.  Returns dict: O
-    (float64), LSE (float64 [G, S]), P (float64 [G, S, S]), the O error
+def attention_fwd(q, k, v, causal: bool = True, seqs=None):
+    """q, k, v float32 [G, S, D] holding BF16 values (the tensor scales are
+    those of all G sequences; `seqs` limits the products to some of them,
+    leaving the others' outputs unset).  Returns dict: O (float64), LSE
+    (float64 [G, S]), P (float64 [G, S, S]; None with seqs), the O error
     normaliser O_D = P |V| (what the BF16 rounding of P can move O by, per
     unit of relative error), and the quantized views (Q_row, K_row, Q_col,
     K_col per sequence)."""
@@ -65,9 +67,9 @@ def attention_fwd(q, k, v, causal: bool = True):
     mask = causal_mask(S) if causal else np.ones((S, S), dtype=bool)
     O = np.empty((G, S, D))
     O_D = np.empty((G, S, D))
-    P_all = np.empty((G, S, S))
+    P_all = np.empty((G, S, S)) if seqs is None else None
     LSE = np.empty((G, S))
-    for g in range(G):
+    for g in (range(G) if seqs is None else seqs):
         s = st * (block_values(_head_rows(q_row, g, S)) @ block_values(_head_rows(k_row, g, S)).T)
         s = np.where(mask, s, -np.inf)
         m = s.max(axis=1, keepdims=True)
@@ -77,7 +79,8 @@ def attention_fwd(q, k, v, causal: bool = True):
         v64 = v[g].astype(np.float64)
         O[g] = p @ v64
         O_D[g] = p @ np.abs(v64)
-        P_all[g] = p
+        if P_all is not None:
+            P_all[g] = p
         LSE[g] = (m + np.log(l))[:, 0]
     return {"O": O, "O_D": O_D, "LSE": LSE, "P": P_all, "scale": scale,
             "Q_row": q_row, "K_row": k_row, "Q_col": q_cols, "K_col": k_cols}

@@ -54,6 +54,7 @@ EXPORTS = [
     "fs4_mstate_encode_workspace_bytes", "fs4_mstate_encode", "fs4_mstate_decode",
     "fs4_workspace_bytes", "fs4_status_str", "fs4_version", "fs4_gemm_plan", "fs4_newton_schulz_plan",
     "fs4_quantize_noalloc", "fs4_quantize_noalloc_scratch_bytes", "fs4_ns_shape_coefficients",
+    "fs4_attention_fwd_workspace_bytes", "fs4_attention_fwd",
 ]
 
 
@@ -115,6 +116,8 @@ _sig("fs4_gemm_plan", ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(_I64)])
 _sig("fs4_ns_shape_coefficients", ctypes.c_int, [_I64, _I64, ctypes.c_int, ctypes.POINTER(_F),
                                                  ctypes.POINTER(ctypes.c_double)])
 _sig("fs4_newton_schulz_plan", ctypes.c_int, [_I64, _I64, ctypes.POINTER(_I64)])
+_sig("fs4_attention_fwd_workspace_bytes", _SZ, [_I64, _I64, _I64])
+_sig("fs4_attention_fwd", ctypes.c_int, [_VP, _VP, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _SZ, _P])
 _sig("fs4_quantize_clipped_workspace_bytes", _SZ, [_I64, _I64])
 _sig("fs4_quantize_clipped", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_double, _VP, _VP, _P,
                                             _SZ, _P])
@@ -581,6 +584,43 @@ def newton_schulz_plan(m: int, n: int) -> dict:
             for i, name in enumerate(("A", "A2", "update"))}
 
 
+@dataclass
+class AttentionFwd:
+    O: torch.Tensor
+    LSE: torch.Tensor
+    Vt: torch.Tensor
+
+
+def attention_quantize(x: torch.Tensor):
+    """The NVFP4 views attention reuses for a BF16 [G, S, D] Q or K: one
+    quantization of the [G*S, D] matrix; row-wise (blocks along D) for
+    Q K^T, column-wise (blocks along the sequence) for the dS products."""
+    if x.dim() != 3:
+        raise ValueError("attention_quantize takes a [G, S, D] tensor")
+    G, S, D = x.shape
+    return quantize(x.reshape(G * S, D))
+
+
+def attention_fwd(Q_row: NVFP4, K_row: NVFP4, V: torch.Tensor, causal: bool = True) -> AttentionFwd:
+    """O = softmax(Q K^T / sqrt(D)) V with Q K^T on the NVFP4 views and P V
+    in BF16.  V bf16 [G, S, D]; returns O fp32 [G, S, D], LSE fp32 [G, S]
+    and V^T bf16 [G, D, S]."""
+    if not isinstance(V, torch.Tensor) or V.dim() != 3:
+        raise ValueError("V must be a [G, S, D] tensor")
+    G, S, D = (int(v) for v in V.shape)
+    dev = V.device
+    _tensor(V, "V", _BF16, (G, S, D))
+    _view(Q_row, "Q_row", G * S, D, dev)
+    _view(K_row, "K_row", G * S, D, dev)
+    O = torch.empty((G, S, D), dtype=torch.float32, device=dev)
+    LSE = torch.empty((G, S), dtype=torch.float32, device=dev)
+    Vt = torch.empty((G, D, S), dtype=torch.bfloat16, device=dev)
+    qv, kv = Q_row.c(), K_row.c()
+    _check(_lib.fs4_attention_fwd(ctypes.byref(qv), ctypes.byref(kv), V.data_ptr(), G, S, D, int(causal), O.data_ptr(),
+                                  LSE.data_ptr(), Vt.data_ptr(), None, 0, _stream(dev)), "fs4_attention_fwd")
+    return AttentionFwd(O, LSE, Vt)
+
+
 def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> int:
     return _lib.fs4_workspace_bytes(op, d0, d1, d2, r)
 
@@ -589,4 +629,5 @@ __all__ = ["NVFP4", "quantize", "quantize_noalloc", "gemm_nt", "linear_fwd", "Li
            "newton_schulz", "lora_project", "lora_realign", "abs_quantile", "quantize_clipped",
            "vstate_encode", "vstate_decode", "mstate_encode", "mstate_decode", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
            "EXPORTS", "MUON_ABC",
-           "release_workspaces", "gemm_plan", "newton_schulz_plan", "ns_shape_coefficients"]
+           "release_workspaces", "gemm_plan", "newton_schulz_plan", "ns_shape_coefficients",
+           "attention_quantize", "attention_fwd", "AttentionFwd"]

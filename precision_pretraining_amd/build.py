@@ -34,7 +34,7 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + I
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-Wall"]
 
 SOURCES = ["quantize.hip", "gemm.hip", "lowrank.hip", "subspace.hip", "realign.hip", "select.hip", "adamw.hip",
-           "static_scratch.hip", "abi.cpp", "ns_coeffs.cpp"]
+           "static_scratch.hip", "attention.hip", "abi.cpp", "ns_coeffs.cpp"]
 
 
 def _run(cmd, verbose):

@@ -597,6 +597,30 @@ fs4_status fs4_lora_realign(void *U, void *V, float *R, int64_t N, int64_t K, in
                              sigma, ws, as_stream(stream));
 }
 
+size_t fs4_attention_fwd_workspace_bytes(int64_t G, int64_t S, int64_t D) {
+  if (G < 1 || !dim_ok(S) || (D != 64 && D != 128)) return 0;
+  return attention_fwd_ws_bytes(G, S, D);
+}
+
+fs4_status fs4_attention_fwd(const fs4_nvfp4 *Q_row, const fs4_nvfp4 *K_row, const void *V, int64_t G, int64_t S,
+                             int64_t D, int causal, float *O, float *LSE, void *Vt_save, void *ws, size_t ws_bytes,
+                             void *stream) {
+  if (G < 1 || !dim_ok(S)) return FS4_ERR_SHAPE;
+  if (D != 64 && D != 128) return FS4_ERR_SHAPE;
+  if (G > ((int64_t)1 << 31) / S) return FS4_ERR_SHAPE;   // G*S rows index 32-bit grids
+  FS4_TRY(check_view(Q_row, G * S, D));
+  FS4_TRY(check_view(K_row, G * S, D));
+  FS4_TRY(check_ptr(V));
+  FS4_TRY(check_ptr(O));
+  if (LSE && ((uintptr_t)LSE & 3u)) return FS4_ERR_ALIGN;
+  if (Vt_save) FS4_TRY(check_ptr(Vt_save));
+  const size_t need = Vt_save ? 0 : attention_fwd_ws_bytes(G, S, D);
+  FS4_TRY(check_ws(ws, ws_bytes, need));
+  uint16_t *vt = Vt_save ? (uint16_t *)Vt_save : (uint16_t *)ws;
+  return launch_attention_fwd(*Q_row, *K_row, (const uint16_t *)V, G, S, D, causal != 0, O, LSE, vt,
+                              as_stream(stream));
+}
+
 size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r) {
   switch (op) {
     case FS4_OP_QUANTIZE: return fs4_quantize_workspace_bytes(d0, d1);

@@ -128,6 +128,12 @@ fs4_status launch_mstate_decode(const fs4_nvfp4 &q, int64_t R, int64_t C, float 
 fs4_status launch_abs_quantile(const void *x, fs4_dtype dt, int64_t n, double q, float *out, void *ws,
                                hipStream_t s);
 
+// NVFP4 mixed-precision attention forward: Q, K row-wise views of [G*S, D],
+// V bf16 [G][S][D]; V^T [G][D][S] is written to Vt (caller's or workspace)
+size_t attention_fwd_ws_bytes(int64_t G, int64_t S, int64_t D);
+fs4_status launch_attention_fwd(const fs4_nvfp4 &Q, const fs4_nvfp4 &K, const uint16_t *V, int64_t G, int64_t S,
+                                int64_t D, int causal, float *O, float *LSE, uint16_t *Vt, hipStream_t s);
+
 struct LowRankEpilogue {
   const float *L = nullptr;     // fp32 [M][r], scaled by l_scale before use
   const uint16_t *R = nullptr;  // bf16, element (n, j) at R[n * r_sn + j * r_sj]
