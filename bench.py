@@ -88,7 +88,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-extra", action="store_true", help="skip the quantizer/NS/roofline legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gemm", "quantizer", "copy", "lora", "adamw"],
+    ap.add_argument("--only", choices=["gemm", "quantizer", "copy", "lora", "adamw", "attention"],
                     help="run one leg alone (for counter runs under a profiler) and exit")
     return ap.parse_args()
 
@@ -352,6 +352,29 @@ def main():
         torch.cuda.synchronize()
         return res
 
+    def attention_leg(reps=10):
+        # Q-Attn forward at the 3B step's attention shape: 8192 tokens as 4
+        # sequences of 2048 x 24 heads of 128, causal.  Algorithmic work: the
+        # visible (causal) part of Q K^T and P V.
+        Gh, Sq, Dh = 96, 2048, 128
+        gen = torch.Generator(device=dev).manual_seed(13)
+        Qa, Ka, Va = (torch.randn((Gh, Sq, Dh), device=dev, generator=gen).bfloat16() for _ in range(3))
+        flop = Gh * 2.0 * 2.0 * (Sq * (Sq + 1) / 2) * Dh
+        q_row, _ = fs4.attention_quantize(Qa)
+        k_row, _ = fs4.attention_quantize(Ka)
+        kern = lambda: fs4.attention_fwd(q_row, k_row, Va)
+        full = lambda: fs4.attention_fwd(fs4.attention_quantize(Qa)[0], fs4.attention_quantize(Ka)[0], Va)
+        for _ in range(3):
+            full()
+        k_ms = time_calls(kern, reps)
+        f_ms = time_calls(full, reps)
+        return {"workload": "Q-Attn forward, 96 sequences (4 x 24 heads) x 2048 tokens, head dim 128, causal",
+                "gflop": round(flop / 1e9, 2), "unit": "TFLOP/s",
+                "attention_kernel_ms": round(k_ms, 4), "achieved": round(flop / (k_ms * 1e-3) / 1e12, 2),
+                "frac": round(flop / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "with_qk_quantization_ms": round(f_ms, 4),
+                "achieved_with_quantization": round(flop / (f_ms * 1e-3) / 1e12, 2)}
+
     if a.only == "gemm":
         print(json.dumps({"only": "gemm", "roofline": gemm_leg(max(3, a.steps))}), flush=True)
         return
@@ -429,6 +452,9 @@ def main():
                                "decode_GBps": round(N * K * (4 + 0.5 + 1 / 16) / (mdec_ms * 1e-3) / 1e9, 1)}
         return out
 
+    if a.only == "attention":
+        print(json.dumps({"only": "attention", "attention": attention_leg()}), flush=True)
+        return
     if a.only == "lora":
         print(json.dumps({"only": "lora", **lora_legs()}), flush=True)
         return
@@ -461,6 +487,7 @@ def main():
         out.update(lora_legs())
         out.update(adamw_legs())
         out["forward"] = fwd_leg()
+        out["attention"] = attention_leg()
         out.update(ns_legs())
         out["library_gemm_ceiling"] = ceiling_leg()
 
