@@ -643,12 +643,31 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
     }
     __syncthreads();
   }
+  // E for a whole 32x32 accumulator tile (16 values per lane) is loaded one
+  // tile ahead, so that its latency overlaps the previous tile's stores
+  // instead of stalling every four rows.  Tiles are disjoint, so loading E of
+  // tile q+1 before storing C of tile q is correct even when C and E are the
+  // same buffer.
+  const bool e_pipe = g.E != nullptr && interior;
+  float ebuf[2][16];
+  auto load_e = [&](int i, int j, float *dst) {
+    const int64_t base = (m0 + wm_u * TM * 32 + i * 32) * g.N + n0;
+    const int nrec = (int)((g.M * g.N - base) * 4 < 0x7FFFFFFF ? (g.M * g.N - base) * 4 : 0x7FFFFFFF);
+    const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((float *)g.E + base, 0, nrec, kBufferWord3);
+    const int loff = (4 * h * (int)g.N + wn * TN * 32 + j * 32 + l32) * 4;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      dst[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, loff, (8 * (e >> 2) + (e & 3)) * (int)g.N * 4, 0));
+  };
+  if (e_pipe) load_e(0, 0, ebuf[0]);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int arow = wm * TM * 32 + i * 32 + l32;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int brow = wn * TN * 32 + j * 32 + l32;
+      const int q = i * TN + j;
+      if (e_pipe && q + 1 < TM * TN) load_e((q + 1) / TN, (q + 1) % TN, ebuf[(q + 1) & 1]);
       floatx16_t t = acc[i][j] * scale;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -673,18 +692,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int soff = (8 * (e >> 2) + (e & 3)) * (int)g.N * 4;
-          if (g.E && (e & 3) == 0) {
-            // E for four rows at once, before their stores of C (which the
-            // loads may not pass): four loads in flight, not one
-            const __amdgpu_buffer_rsrc_t re =
-                __builtin_amdgcn_make_buffer_rsrc((float *)g.E + base, 0, nrec, kBufferWord3);
-            float ev[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              ev[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, loff, soff + c * (int)g.N * 4, 0));
-#pragma unroll
-            for (int c = 0; c < 4; ++c) t[e + c] += g.beta_e * ev[c];
-          }
+          if (e_pipe) t[e] += g.beta_e * ebuf[q & 1][e];
           const float v = t[e];
           if (g.amax_parts) amax = fmaxf(amax, fabsf(v));
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, loff, soff, 0);
