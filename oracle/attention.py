@@ -30,7 +30,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .quantize import NVFP4, block_values, quantize, quantize_rows
+from .formats import tensor_scale_from_amax
+from .quantize import NVFP4, block_values, quantize, quantize_rows, tensor_amax
 
 
 def _views_per_sequence(x32, G, S, D):
@@ -51,14 +52,25 @@ def causal_mask(S: int) -> np.ndarray:
     return np.tril(np.ones((S, S), dtype=bool))
 
 
-def attention_fwd(q, k, v, causal: bool = True, seqs=None):
+def _probs(view_q: NVFP4, view_k: NVFP4, g: int, S: int, st: float, mask: np.ndarray):
+    """P = softmax of sequence g's masked scores S = st Q_hat K_hat^T, row by
+    row, with each row's max m and sum l of exp(S - m)."""
+    s = st * (block_values(_head_rows(view_q, g, S)) @ block_values(_head_rows(view_k, g, S)).T)
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return e / l, m, l
+
+
+def attention_fwd(q, k, v, causal: bool = True, seqs=None, keep_P: bool = True):
     """q, k, v float32 [G, S, D] holding BF16 values (the tensor scales are
     those of all G sequences; `seqs` limits the products to some of them,
     leaving the others' outputs unset).  Returns dict: O (float64), LSE
-    (float64 [G, S]), P (float64 [G, S, S]; None with seqs), the O error
-    normaliser O_D = P |V| (what the BF16 rounding of P can move O by, per
-    unit of relative error), and the quantized views (Q_row, K_row, Q_col,
-    K_col per sequence)."""
+    (float64 [G, S]), P (float64 [G, S, S]; None with seqs or without
+    keep_P), the O error normaliser O_D = P |V| (what the BF16 rounding of P
+    can move O by, per unit of relative error), and the quantized views
+    (Q_row, K_row, Q_col, K_col per sequence)."""
     G, S, D = q.shape
     q_row, q_cols, _ = _views_per_sequence(q, G, S, D)
     k_row, k_cols, _ = _views_per_sequence(k, G, S, D)
@@ -67,53 +79,75 @@ def attention_fwd(q, k, v, causal: bool = True, seqs=None):
     mask = causal_mask(S) if causal else np.ones((S, S), dtype=bool)
     O = np.empty((G, S, D))
     O_D = np.empty((G, S, D))
-    P_all = np.empty((G, S, S)) if seqs is None else None
+    P_all = np.empty((G, S, S)) if seqs is None and keep_P else None
     LSE = np.empty((G, S))
     for g in (range(G) if seqs is None else seqs):
-        s = st * (block_values(_head_rows(q_row, g, S)) @ block_values(_head_rows(k_row, g, S)).T)
-        s = np.where(mask, s, -np.inf)
-        m = s.max(axis=1, keepdims=True)
-        e = np.exp(s - m)
-        l = e.sum(axis=1, keepdims=True)
-        p = e / l
+        p, m, l = _probs(q_row, k_row, g, S, st, mask)
         v64 = v[g].astype(np.float64)
         O[g] = p @ v64
         O_D[g] = p @ np.abs(v64)
         if P_all is not None:
             P_all[g] = p
         LSE[g] = (m + np.log(l))[:, 0]
-    return {"O": O, "O_D": O_D, "LSE": LSE, "P": P_all, "scale": scale,
+    return {"O": O, "O_D": O_D, "LSE": LSE, "P": P_all, "scale": scale, "st": st, "mask": mask,
+            "seqs": None if seqs is None else sorted(seqs),
             "Q_row": q_row, "K_row": k_row, "Q_col": q_cols, "K_col": k_cols}
 
 
-def attention_bwd(q, k, v, do, fwd=None, causal: bool = True):
+def softmax_grad(fwd, v, do, g: int):
+    """The softmax gradient of sequence g: P (the forward's, or recomputed
+    from the same views), dP = dO V^T, Delta = rowsum(dO * O) with the
+    forward's O, and dS = P * (dP - Delta), all float64."""
+    S = v.shape[1]
+    P = fwd["P"][g] if fwd["P"] is not None else _probs(fwd["Q_row"], fwd["K_row"], g, S, fwd["st"], fwd["mask"])[0]
+    do64, v64 = do[g].astype(np.float64), v[g].astype(np.float64)
+    dP = do64 @ v64.T
+    delta = np.sum(do64 * fwd["O"][g], axis=1, keepdims=True)
+    return {"P": P, "dP": dP, "Delta": delta[:, 0], "dS": P * (dP - delta)}
+
+
+def attention_bwd(q, k, v, do, fwd=None, causal: bool = True, seqs=None, on_seq=None):
     """The backward from dO float32 [G, S, D] (BF16 values), with the
-    forward's quantized views and P.  Returns dict of dQ, dK, dV (float64),
-    dS (float64 [G, S, S], before its quantization) and normalisers
-    dQ_D, dK_D (sum |a||b| of the NVFP4 products), dV_D = P^T |dO|."""
+    forward's quantized views (and its P when kept).  dS's tensor scale is
+    that of all G sequences; `seqs` limits the outputs to some of them (the
+    forward must then still cover all G, for every sequence's dS enters the
+    tensor scale).  `on_seq(g, parts)`, if given, sees softmax_grad's parts
+    of every sequence as they are formed.  Returns dict of dQ, dK, dV
+    (float64 [G, S, D]; rows outside `seqs` unset), dS (float64 [G, S, S]
+    before its quantization; None with seqs, else per sequence in dS_seq),
+    the normalisers dQ_D, dK_D (sum |a||b| of the NVFP4 products) and
+    dV_D = P^T |dO|, and dS's tensor scale."""
     G, S, D = q.shape
     if fwd is None:
-        fwd = attention_fwd(q, k, v, causal)
-    P, O, scale = fwd["P"], fwd["O"], fwd["scale"]
+        fwd = attention_fwd(q, k, v, causal, keep_P=seqs is None)
+    if fwd["seqs"] is not None:
+        raise ValueError("the backward needs the forward of every sequence")
+    scale = fwd["scale"]
+    sel = list(range(G)) if seqs is None else sorted(seqs)
     dV = np.empty((G, S, D))
     dV_D = np.empty((G, S, D))
-    dS = np.empty((G, S, S))
+    ds_seq = {}
+    amax = np.float32(0.0)
     for g in range(G):
-        do64, v64 = do[g].astype(np.float64), v[g].astype(np.float64)
-        dV[g] = P[g].T @ do64
-        dV_D[g] = P[g].T @ np.abs(do64)
-        dP = do64 @ v64.T
-        delta = np.sum(do64 * O[g], axis=1, keepdims=True)
-        dS[g] = P[g] * (dP - delta)
-    ds32 = dS.astype(np.float32)
-    ds_row, _, s_ds = quantize(ds32.reshape(G * S, S), rowwise=True, colwise=False)
+        parts = softmax_grad(fwd, v, do, g)
+        ds32 = parts["dS"].astype(np.float32)
+        amax = max(amax, tensor_amax(ds32))
+        if on_seq is not None:
+            on_seq(g, parts)
+        if g in sel:
+            do64 = do[g].astype(np.float64)
+            dV[g] = parts["P"].T @ do64
+            dV_D[g] = parts["P"].T @ np.abs(do64)
+            ds_seq[g] = (parts["dS"], ds32)
+    s_ds = tensor_scale_from_amax(amax)
     dQ = np.empty((G, S, D))
     dK = np.empty((G, S, D))
     dQ_D = np.empty((G, S, D))
     dK_D = np.empty((G, S, D))
-    for g in range(G):
-        a = block_values(_head_rows(ds_row, g, S))                         # dS_g, blocks along keys
-        at = block_values(quantize_rows(np.ascontiguousarray(ds32[g].T), s_ds))   # dS_g^T, blocks along queries
+    for g in sel:
+        ds32 = ds_seq[g][1]
+        a = block_values(quantize_rows(ds32, s_ds))                        # dS_g, blocks along keys
+        at = block_values(quantize_rows(np.ascontiguousarray(ds32.T), s_ds))   # dS_g^T, blocks along queries
         kc = block_values(fwd["K_col"][g])                                 # K_g^T [D, S], blocks along keys
         qc = block_values(fwd["Q_col"][g])                                 # Q_g^T [D, S], blocks along queries
         sq = float(s_ds) * float(fwd["K_row"].tscale) * scale
@@ -122,5 +156,6 @@ def attention_bwd(q, k, v, do, fwd=None, causal: bool = True):
         dQ_D[g] = sq * (np.abs(a) @ np.abs(kc).T)
         dK[g] = sk * (at @ qc.T)
         dK_D[g] = sk * (np.abs(at) @ np.abs(qc).T)
-    return {"dQ": dQ, "dK": dK, "dV": dV, "dS": dS, "dQ_D": dQ_D, "dK_D": dK_D, "dV_D": dV_D,
-            "dS_tscale": s_ds}
+    dS = np.stack([ds_seq[g][0] for g in range(G)]) if seqs is None else None
+    return {"dQ": dQ, "dK": dK, "dV": dV, "dS": dS, "dS_seq": {g: ds_seq[g][0] for g in sel},
+            "dQ_D": dQ_D, "dK_D": dK_D, "dV_D": dV_D, "dS_tscale": s_ds}

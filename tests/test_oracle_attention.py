@@ -128,3 +128,27 @@ def test_ds_products_within_the_format_bound_of_autograd():
     assert err.max() > 0 and np.mean(err) < 0.5 * np.mean(bq)
     # the normalisers bound the products themselves
     assert np.all(b["dQ_D"] >= np.abs(b["dQ"]) * (1 - 1e-12)) and np.all(b["dK_D"] >= np.abs(b["dK"]) * (1 - 1e-12))
+
+
+def test_sampled_backward_equals_the_full_one():
+    """The backward restricted to some sequences (the forward's P not kept,
+    so recomputed from the same views) gives those sequences' outputs of the
+    full backward exactly, with dS's tensor scale still over all of them;
+    the per-sequence hook sees every sequence once, in order."""
+    rng = np.random.default_rng(6)
+    G, S, D = 4, 48, 32
+    q, k, v, do = (_bf(rng, (G, S, D)) for _ in range(4))
+    do[0] *= 4.0    # sequence 0, outside the sample, sets dS's amax
+    full = attention_bwd(q, k, v, do, attention_fwd(q, k, v))
+    seen = []
+    part = attention_bwd(q, k, v, do, attention_fwd(q, k, v, keep_P=False), seqs=[1, 3],
+                         on_seq=lambda g, parts: seen.append((g, np.abs(parts["dS"]).max())))
+    assert [g for g, _ in seen] == list(range(G))
+    assert part["dS_tscale"] == full["dS_tscale"]
+    assert int(np.argmax([m for _, m in seen])) == 0
+    for name in ("dQ", "dK", "dV", "dQ_D", "dK_D", "dV_D"):
+        np.testing.assert_array_equal(part[name][[1, 3]], full[name][[1, 3]], err_msg=name)
+    for g in (1, 3):
+        np.testing.assert_array_equal(part["dS_seq"][g], full["dS"][g])
+    with pytest.raises(ValueError):
+        attention_bwd(q, k, v, do, attention_fwd(q, k, v, seqs=[1]), seqs=[1])
