@@ -375,8 +375,8 @@ const char *fs4_version(void);
  *   V        bf16 [G][S][D]
  *   O        fp32 [G][S][D];  LSE fp32 [G][S], nullable
  *   Vt_save  bf16 [G][D][S], nullable: receives V^T, the layout the P V
- *            product reads (reused by a backward); without it V^T goes to the
- *            workspace (fs4_attention_fwd_workspace_bytes)
+ *            product reads; without it V^T goes to the workspace
+ *            (fs4_attention_fwd_workspace_bytes)
  *   D = 64 or 128; S a positive multiple of 16; G >= 1, G*S < 2^31.
  * Errors: FS4_ERR_SHAPE, FS4_ERR_NULL, FS4_ERR_ALIGN, FS4_ERR_WORKSPACE.
  */
@@ -384,6 +384,41 @@ size_t fs4_attention_fwd_workspace_bytes(int64_t G, int64_t S, int64_t D);
 fs4_status fs4_attention_fwd(const fs4_nvfp4 *Q_row, const fs4_nvfp4 *K_row, const void *V, int64_t G,
                              int64_t S, int64_t D, int causal, float *O, float *LSE, void *Vt_save,
                              void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * fs4_attention_bwd — the Q-Attn backward, [FS4 §2.4]: the products that
+ * take dS on NVFP4 operands, P^T dO and dO V^T in BF16, the forward's
+ * quantized Q and K reused.  Per sequence g < G:
+ *     P = exp(S - LSE), S recomputed from Q_row, K_row as in the forward
+ *     dP = dO V^T,  Delta = rowsum(dO * O),  dS = P * (dP - Delta)   (fp32)
+ *     dV = P^T dO                     (P rounded to BF16, dO BF16, fp32 sums)
+ *     dQ = s_dS s_K Q(dS) Q_col(K)^T / sqrt(D)
+ *     dK = s_dS s_Q Q(dS^T) Q_col(Q)^T / sqrt(D)
+ *   where dS is quantized once as the [G*S][S] matrix, one tensor scale over
+ *   all sequences: row-wise (blocks along keys) for dQ, column-wise (blocks
+ *   along queries) for dK.  Under a causal mask the all-zero blocks of dS
+ *   above the diagonal are skipped in dQ and dK (their products are zero).
+ *   Q_row, K_row  the forward's row-wise views ([G*S][D], blocks along D)
+ *   Q_col, K_col  the column-wise views of the same quantizations ([D][G*S],
+ *                 blocks of 16 along the sequence, never across sequences)
+ *   V, dO    bf16 [G][S][D];  O fp32 [G][S][D] and LSE fp32 [G][S] from the
+ *            forward
+ *   dQ, dK, dV  fp32 [G][S][D] outputs
+ *   dS       fp32 [G*S][S], nullable: receives the softmax gradient before
+ *            its quantization (zeros where masked); otherwise it stays in
+ *            the workspace
+ *   workspace: fs4_attention_bwd_workspace_bytes(G, S, D) (includes dS's
+ *   4 G S^2 bytes whether or not dS is given), 256-byte aligned.
+ *   D = 64 or 128; S a positive multiple of 16; G >= 1, G*S < 2^31 and
+ *   G*S*S < 2^31.  All buffers 16-byte aligned (LSE 4).
+ * Errors: FS4_ERR_SHAPE, FS4_ERR_NULL, FS4_ERR_ALIGN, FS4_ERR_WORKSPACE (the
+ * size call returns 0 for a shape the call rejects).
+ */
+size_t fs4_attention_bwd_workspace_bytes(int64_t G, int64_t S, int64_t D);
+fs4_status fs4_attention_bwd(const fs4_nvfp4 *Q_row, const fs4_nvfp4 *K_row, const fs4_nvfp4 *Q_col,
+                             const fs4_nvfp4 *K_col, const void *V, const void *dO, const float *O,
+                             const float *LSE, int64_t G, int64_t S, int64_t D, int causal, float *dQ,
+                             float *dK, float *dV, float *dS, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -63,7 +63,18 @@ def _probs(view_q: NVFP4, view_k: NVFP4, g: int, S: int, st: float, mask: np.nda
     return e / l, m, l
 
 
-def attention_fwd(q, k, v, causal: bool = True, seqs=None, keep_P: bool = True):
+def _each(fn, seqs, threads: int):
+    """fn(g) for every g in seqs, in order, on `threads` threads (the
+    sequences are independent; each one's arithmetic is the same either
+    way)."""
+    if threads <= 1:
+        return [fn(g) for g in seqs]
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(fn, seqs))
+
+
+def attention_fwd(q, k, v, causal: bool = True, seqs=None, keep_P: bool = True, threads: int = 1):
     """q, k, v float32 [G, S, D] holding BF16 values (the tensor scales are
     those of all G sequences; `seqs` limits the products to some of them,
     leaving the others' outputs unset).  Returns dict: O (float64), LSE
@@ -81,7 +92,8 @@ def attention_fwd(q, k, v, causal: bool = True, seqs=None, keep_P: bool = True):
     O_D = np.empty((G, S, D))
     P_all = np.empty((G, S, S)) if seqs is None and keep_P else None
     LSE = np.empty((G, S))
-    for g in (range(G) if seqs is None else seqs):
+
+    def one(g):
         p, m, l = _probs(q_row, k_row, g, S, st, mask)
         v64 = v[g].astype(np.float64)
         O[g] = p @ v64
@@ -89,6 +101,8 @@ def attention_fwd(q, k, v, causal: bool = True, seqs=None, keep_P: bool = True):
         if P_all is not None:
             P_all[g] = p
         LSE[g] = (m + np.log(l))[:, 0]
+
+    _each(one, range(G) if seqs is None else seqs, threads)
     return {"O": O, "O_D": O_D, "LSE": LSE, "P": P_all, "scale": scale, "st": st, "mask": mask,
             "seqs": None if seqs is None else sorted(seqs),
             "Q_row": q_row, "K_row": k_row, "Q_col": q_cols, "K_col": k_cols}
@@ -106,13 +120,14 @@ def softmax_grad(fwd, v, do, g: int):
     return {"P": P, "dP": dP, "Delta": delta[:, 0], "dS": P * (dP - delta)}
 
 
-def attention_bwd(q, k, v, do, fwd=None, causal: bool = True, seqs=None, on_seq=None):
+def attention_bwd(q, k, v, do, fwd=None, causal: bool = True, seqs=None, on_seq=None, threads: int = 1):
     """The backward from dO float32 [G, S, D] (BF16 values), with the
     forward's quantized views (and its P when kept).  dS's tensor scale is
     that of all G sequences; `seqs` limits the outputs to some of them (the
     forward must then still cover all G, for every sequence's dS enters the
     tensor scale).  `on_seq(g, parts)`, if given, sees softmax_grad's parts
-    of every sequence as they are formed.  Returns dict of dQ, dK, dV
+    of every sequence as they are formed (from several threads at once
+    when threads > 1).  Returns dict of dQ, dK, dV
     (float64 [G, S, D]; rows outside `seqs` unset), dS (float64 [G, S, S]
     before its quantization; None with seqs, else per sequence in dS_seq),
     the normalisers dQ_D, dK_D (sum |a||b| of the NVFP4 products) and
@@ -127,11 +142,10 @@ def attention_bwd(q, k, v, do, fwd=None, causal: bool = True, seqs=None, on_seq=
     dV = np.empty((G, S, D))
     dV_D = np.empty((G, S, D))
     ds_seq = {}
-    amax = np.float32(0.0)
-    for g in range(G):
+
+    def one(g):
         parts = softmax_grad(fwd, v, do, g)
         ds32 = parts["dS"].astype(np.float32)
-        amax = max(amax, tensor_amax(ds32))
         if on_seq is not None:
             on_seq(g, parts)
         if g in sel:
@@ -139,7 +153,9 @@ def attention_bwd(q, k, v, do, fwd=None, causal: bool = True, seqs=None, on_seq=
             dV[g] = parts["P"].T @ do64
             dV_D[g] = parts["P"].T @ np.abs(do64)
             ds_seq[g] = (parts["dS"], ds32)
-    s_ds = tensor_scale_from_amax(amax)
+        return tensor_amax(ds32)
+
+    s_ds = tensor_scale_from_amax(max(_each(one, range(G), threads)))
     dQ = np.empty((G, S, D))
     dK = np.empty((G, S, D))
     dQ_D = np.empty((G, S, D))

@@ -55,6 +55,7 @@ EXPORTS = [
     "fs4_workspace_bytes", "fs4_status_str", "fs4_version", "fs4_gemm_plan", "fs4_newton_schulz_plan",
     "fs4_quantize_noalloc", "fs4_quantize_noalloc_scratch_bytes", "fs4_ns_shape_coefficients",
     "fs4_attention_fwd_workspace_bytes", "fs4_attention_fwd",
+    "fs4_attention_bwd_workspace_bytes", "fs4_attention_bwd",
 ]
 
 
@@ -118,6 +119,9 @@ _sig("fs4_ns_shape_coefficients", ctypes.c_int, [_I64, _I64, ctypes.c_int, ctype
 _sig("fs4_newton_schulz_plan", ctypes.c_int, [_I64, _I64, ctypes.POINTER(_I64)])
 _sig("fs4_attention_fwd_workspace_bytes", _SZ, [_I64, _I64, _I64])
 _sig("fs4_attention_fwd", ctypes.c_int, [_VP, _VP, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _SZ, _P])
+_sig("fs4_attention_bwd_workspace_bytes", _SZ, [_I64, _I64, _I64])
+_sig("fs4_attention_bwd", ctypes.c_int, [_VP, _VP, _VP, _VP, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int,
+                                         _P, _P, _P, _P, _P, _SZ, _P])
 _sig("fs4_quantize_clipped_workspace_bytes", _SZ, [_I64, _I64])
 _sig("fs4_quantize_clipped", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, ctypes.c_double, _VP, _VP, _P,
                                             _SZ, _P])
@@ -621,6 +625,49 @@ def attention_fwd(Q_row: NVFP4, K_row: NVFP4, V: torch.Tensor, causal: bool = Tr
     return AttentionFwd(O, LSE, Vt)
 
 
+@dataclass
+class AttentionBwd:
+    dQ: torch.Tensor
+    dK: torch.Tensor
+    dV: torch.Tensor
+    dS: Optional[torch.Tensor]
+
+
+def attention_bwd(dO: torch.Tensor, V: torch.Tensor, fwd: AttentionFwd, Q_views, K_views, causal: bool = True,
+                  keep_dS: bool = False) -> AttentionBwd:
+    """The backward of attention_fwd: dV = P^T dO and dP = dO V^T in BF16,
+    dQ and dK on NVFP4 views of dS (one tensor scale over all sequences) and
+    the forward's column-wise Q and K views.  dO, V bf16 [G, S, D];
+    Q_views, K_views the (row, col) pairs attention_quantize returned; fwd
+    the forward's outputs (O and LSE are read).  Returns dQ, dK, dV fp32
+    [G, S, D] and, with keep_dS, dS fp32 [G*S, S] before its quantization."""
+    if not isinstance(dO, torch.Tensor) or dO.dim() != 3:
+        raise ValueError("dO must be a [G, S, D] tensor")
+    G, S, D = (int(v) for v in dO.shape)
+    dev = dO.device
+    _tensor(dO, "dO", _BF16, (G, S, D))
+    _tensor(V, "V", _BF16, (G, S, D), dev)
+    _tensor(fwd.O, "O", _F32, (G, S, D), dev)
+    _tensor(fwd.LSE, "LSE", _F32, (G, S), dev)
+    (q_row, q_col), (k_row, k_col) = Q_views, K_views
+    _view(q_row, "Q_row", G * S, D, dev)
+    _view(k_row, "K_row", G * S, D, dev)
+    _view(q_col, "Q_col", D, G * S, dev)
+    _view(k_col, "K_col", D, G * S, dev)
+    dQ, dK, dV = (torch.empty((G, S, D), dtype=torch.float32, device=dev) for _ in range(3))
+    dS = torch.empty((G * S, S), dtype=torch.float32, device=dev) if keep_dS else None
+    nbytes = _lib.fs4_attention_bwd_workspace_bytes(G, S, D)
+    if nbytes == 0:
+        raise ValueError("attention_bwd: unsupported shape G=%d S=%d D=%d" % (G, S, D))
+    ws = _workspace(nbytes, dev)
+    qr, kr, qc, kc = q_row.c(), k_row.c(), q_col.c(), k_col.c()
+    _check(_lib.fs4_attention_bwd(ctypes.byref(qr), ctypes.byref(kr), ctypes.byref(qc), ctypes.byref(kc),
+                                  V.data_ptr(), dO.data_ptr(), fwd.O.data_ptr(), fwd.LSE.data_ptr(), G, S, D,
+                                  int(causal), dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), _ptr(dS),
+                                  ws.data_ptr(), ws.numel(), _stream(dev)), "fs4_attention_bwd")
+    return AttentionBwd(dQ, dK, dV, dS)
+
+
 def workspace_bytes(op: int, d0: int, d1: int = 0, d2: int = 0, r: int = 0) -> int:
     return _lib.fs4_workspace_bytes(op, d0, d1, d2, r)
 
@@ -630,4 +677,4 @@ __all__ = ["NVFP4", "quantize", "quantize_noalloc", "gemm_nt", "linear_fwd", "Li
            "vstate_encode", "vstate_decode", "mstate_encode", "mstate_decode", "workspace_bytes", "version", "status_str", "FS4Error", "LIB_PATH",
            "EXPORTS", "MUON_ABC",
            "release_workspaces", "gemm_plan", "newton_schulz_plan", "ns_shape_coefficients",
-           "attention_quantize", "attention_fwd", "AttentionFwd"]
+           "attention_quantize", "attention_fwd", "AttentionFwd", "attention_bwd", "AttentionBwd"]

@@ -621,6 +621,40 @@ fs4_status fs4_attention_fwd(const fs4_nvfp4 *Q_row, const fs4_nvfp4 *K_row, con
                               as_stream(stream));
 }
 
+size_t fs4_attention_bwd_workspace_bytes(int64_t G, int64_t S, int64_t D) {
+  if (G < 1 || !dim_ok(S) || (D != 64 && D != 128)) return 0;
+  if (G > ((int64_t)1 << 31) / S || G * S > (((int64_t)1 << 31) - 1) / S) return 0;
+  return attention_bwd_ws_bytes(G, S, D);
+}
+
+fs4_status fs4_attention_bwd(const fs4_nvfp4 *Q_row, const fs4_nvfp4 *K_row, const fs4_nvfp4 *Q_col,
+                             const fs4_nvfp4 *K_col, const void *V, const void *dO, const float *O,
+                             const float *LSE, int64_t G, int64_t S, int64_t D, int causal, float *dQ, float *dK,
+                             float *dV, float *dS, void *ws, size_t ws_bytes, void *stream) {
+  if (G < 1 || !dim_ok(S)) return FS4_ERR_SHAPE;
+  if (D != 64 && D != 128) return FS4_ERR_SHAPE;
+  if (G > ((int64_t)1 << 31) / S) return FS4_ERR_SHAPE;                  // G*S rows index 32-bit grids
+  if (G * S > (((int64_t)1 << 31) - 1) / S) return FS4_ERR_SHAPE;        // dS's G*S*S elements
+  FS4_TRY(check_view(Q_row, G * S, D));
+  FS4_TRY(check_view(K_row, G * S, D));
+  FS4_TRY(check_view(Q_col, D, G * S));
+  FS4_TRY(check_view(K_col, D, G * S));
+  FS4_TRY(check_ptr(V));
+  FS4_TRY(check_ptr(dO));
+  FS4_TRY(check_ptr(O));
+  FS4_TRY(check_ptr(dQ));
+  FS4_TRY(check_ptr(dK));
+  FS4_TRY(check_ptr(dV));
+  if (!LSE) return FS4_ERR_NULL;
+  if ((uintptr_t)LSE & 3u) return FS4_ERR_ALIGN;
+  if (dS) FS4_TRY(check_ptr(dS));
+  FS4_TRY(check_ws(ws, ws_bytes, attention_bwd_ws_bytes(G, S, D)));
+  Carver c(ws);
+  const AttnBwdWs w = attention_bwd_carve(c, G, S, D);
+  return launch_attention_bwd(*Q_row, *K_row, *Q_col, *K_col, (const uint16_t *)V, (const uint16_t *)dO, O, LSE,
+                              G, S, D, causal != 0, dQ, dK, dV, dS, w, as_stream(stream));
+}
+
 size_t fs4_workspace_bytes(fs4_op op, int64_t d0, int64_t d1, int64_t d2, int r) {
   switch (op) {
     case FS4_OP_QUANTIZE: return fs4_quantize_workspace_bytes(d0, d1);

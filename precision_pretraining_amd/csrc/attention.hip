@@ -308,6 +308,455 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__r
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward.  Per sequence, from the forward's quantized Q and K, its O and
+// LSE, and dO:
+//   P = exp(S - LSE)                  (S recomputed from the same NVFP4 views)
+//   dP = dO V^T, Delta = rowsum(dO * O), dS = P * (dP - Delta)
+//   dV = P^T dO                        (P rounded to BF16, dO BF16)
+//   dQ = Q(dS) Q_col(K)^T / sqrt(D),  dK = Q(dS^T) Q_col(Q)^T / sqrt(D)
+// dS is quantized once, with one tensor scale over all sequences, so it is
+// materialised in fp32: the softmax-gradient kernel writes it together with
+// one partial amax per workgroup, the quantizer's encode pass turns it into
+// both NVFP4 views, and a batched NVFP4 product kernel forms dQ and dK.
+//
+// The softmax-gradient kernel gives each workgroup 128 keys of one sequence,
+// 32 per wave, and walks the queries in blocks of 64.  A wave keeps its keys'
+// K (expanded to FP16) and V (BF16) in registers as the B operands of
+// S = Q K^T and dP = dO V^T, so both accumulators hold one key per lane and
+// 16 queries per lane in registers; P and dS are formed in place.  Those P
+// registers, rounded to BF16, are the B operand of dV^T = dO^T P, the
+// queries contracted in the order the registers hold them (dO^T is staged
+// transposed so the A fragments follow that order).  Each query block's Q
+// is expanded to FP16 once per workgroup, into LDS.
+
+constexpr int kBwdKeys = 128;   // keys per workgroup, 32 per wave
+constexpr int kBwdQ = 64;       // queries per step: two 32-query tiles
+
+struct AttnBwdArgs {
+  const uint8_t *q_codes, *q_scales, *k_codes, *k_scales;
+  const float *q_ts, *k_ts;
+  const uint16_t *v;      // bf16 [G][S][D]
+  const uint16_t *dout;   // bf16 [G][S][D]
+  const uint16_t *doutt;  // bf16 [G][D][S]
+  const float *lse;       // [G][S], natural log
+  const float *delta;     // [G][S]
+  float *ds;              // fp32 [G*S][S]
+  float *dv;              // fp32 [G][S][D]
+  uint32_t *amax;         // one max |dS| per workgroup (fp32 bits)
+  int64_t G, S;
+  float scale;
+  int causal;
+};
+
+template <int D>
+struct BwdLds {
+  static constexpr int kQh = D + 8;       // FP16 per row of the expanded Q block
+  static constexpr int kDo = D + 8;       // BF16 per row of the dO block
+  static constexpr int kDt = kBwdQ + 8;   // BF16 per row of dO^T
+  static constexpr int kQhOff = 0;
+  static constexpr int kDoOff = kQhOff + kBwdQ * kQh * 2;
+  static constexpr int kDtOff = kDoOff + kBwdQ * kDo * 2;
+  static constexpr int kLseOff = kDtOff + D * kDt * 2;
+  static constexpr int kDeltaOff = kLseOff + kBwdQ * 4;
+  static constexpr int kStage = kDeltaOff + kBwdQ * 4;
+  static constexpr int kEpt = kBwdQ * D / kAttnThreads;                // Q elements a thread expands
+  static constexpr int kDoPer = kBwdQ * D * 2 / 16 / kAttnThreads;     // 16-byte words of dO per thread
+  static constexpr int kDtPer = D * kBwdQ * 2 / 16 / kAttnThreads;     // and of dO^T
+  static_assert(D / kEpt == 4 && kEpt % 16 == 0, "Q staging: four threads per row, whole scale blocks");
+  static_assert(kStage % 16 == 0, "stage alignment");
+};
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs a) {
+  using L = BwdLds<D>;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DT = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::kStage];
+  __shared__ uint32_t red[kAttnThreads / 64];
+
+  const int64_t G = a.G, S = a.S;
+  const int64_t g = blockIdx.x % G;
+  const int64_t kb = (int64_t)blockIdx.x / G;   // under a causal mask the first keys see the most queries
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int64_t k0 = kb * kBwdKeys;
+  const int64_t kend = k0 + kBwdKeys < S ? k0 + kBwdKeys : S;
+  const int64_t kw0 = k0 + w * 32;
+  const int64_t key = kw0 + l32;
+  const bool key_ok = key < S;
+  const int64_t keyc = key_ok ? key : S - 1;
+
+  // ---- this wave's keys: K expanded to FP16 and V, both B operands --------
+  f16x8_t kf[KSTEPS];
+  bf16x8_t vf[KSTEPS];
+  {
+    const uint8_t *krow = a.k_codes + (g * S + keyc) * (D / 2);
+    const uint8_t *ksc = a.k_scales + (g * S + keyc) * (D / 16);
+    const uint16_t *vrow = a.v + (g * S + keyc) * D;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      kf[t] = expand8(*(const uint32_t *)(krow + 8 * t + 4 * h), split_scale(ksc[t]));   // d = 16t + 8h .. +8
+      vf[t] = *(const bf16x8_t *)(vrow + 16 * t + 8 * h);
+    }
+  }
+
+  // ---- under a causal mask, dS is zero for the queries before this block ---
+  if (a.causal && k0 > 0) {
+    const int64_t n4 = (kend - k0) / 4;
+    for (int64_t i = tid; i < k0 * n4; i += kAttnThreads) {
+      const int64_t row = i / n4, c = i % n4;
+      *(float4 *)(a.ds + (g * S + row) * S + k0 + 4 * c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+
+  // ---- query-block staging: global -> registers -> LDS ---------------------
+  uint4 rq = make_uint4(0, 0, 0, 0);
+  uint32_t rqs = 0;
+  uint4 rdo[L::kDoPer], rdt[L::kDtPer];
+  float rls = 0.0f;
+  const int qrow = tid / 4, qc0 = (tid % 4) * L::kEpt;   // the Q elements this thread expands
+  auto load_block = [&](int64_t q0) {
+    {
+      int64_t qq = q0 + qrow;
+      qq = qq < S ? qq : S - 1;
+      const uint8_t *cp = a.q_codes + (g * S + qq) * (D / 2) + qc0 / 2;
+      const uint8_t *sp = a.q_scales + (g * S + qq) * (D / 16) + qc0 / 16;
+      if constexpr (L::kEpt == 32) {
+        rq = *(const uint4 *)cp;
+        rqs = *(const uint16_t *)sp;
+      } else {
+        const uint2 t = *(const uint2 *)cp;
+        rq = make_uint4(t.x, t.y, 0u, 0u);
+        rqs = *sp;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < L::kDoPer; ++i) {
+      const int idx = tid + i * kAttnThreads;
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      const int64_t qq = q0 + row;
+      rdo[i] = qq < S ? *(const uint4 *)(a.dout + (g * S + qq) * D + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < L::kDtPer; ++i) {
+      const int idx = tid + i * kAttnThreads;
+      const int d = idx / (kBwdQ / 8), ch = idx % (kBwdQ / 8);   // 8 queries per word
+      const int64_t qq = q0 + ch * 8;
+      rdt[i] = qq < S ? *(const uint4 *)(a.doutt + (g * D + d) * S + qq) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 2 * kBwdQ) {
+      const int64_t qq = q0 + (tid & (kBwdQ - 1));
+      rls = qq < S ? (tid < kBwdQ ? a.lse[g * S + qq] * kLog2e : a.delta[g * S + qq]) : 0.0f;
+    }
+  };
+  auto store_block = [&](int st) {
+    uint8_t *base = lds + st * L::kStage;
+    _Float16 *qh = (_Float16 *)(base + L::kQhOff) + qrow * L::kQh + qc0;
+    const uint32_t cw[4] = {rq.x, rq.y, rq.z, rq.w};
+#pragma unroll
+    for (int j = 0; j < L::kEpt / 8; ++j)
+      *(f16x8_t *)(qh + 8 * j) = expand8(cw[j], split_scale((rqs >> (8 * (j / 2))) & 0xFFu));
+#pragma unroll
+    for (int i = 0; i < L::kDoPer; ++i) {
+      const int idx = tid + i * kAttnThreads;
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      *(uint4 *)(base + L::kDoOff + (row * L::kDo + ch * 8) * 2) = rdo[i];
+    }
+#pragma unroll
+    for (int i = 0; i < L::kDtPer; ++i) {
+      const int idx = tid + i * kAttnThreads;
+      const int d = idx / (kBwdQ / 8), ch = idx % (kBwdQ / 8);
+      *(uint4 *)(base + L::kDtOff + (d * L::kDt + ch * 8) * 2) = rdt[i];
+    }
+    if (tid < 2 * kBwdQ) ((float *)(base + L::kLseOff))[tid] = rls;   // lse2 then delta, adjacent
+  };
+
+  const float c_log2 = (*a.q_ts) * (*a.k_ts) * a.scale * kLog2e;   // S in log2 units
+  floatx16_t dvt[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dvt[i][e] = 0.0f;
+  float amax = 0.0f;
+
+  const int64_t nqb = (S + kBwdQ - 1) / kBwdQ;
+  const int64_t qb0 = a.causal ? k0 / kBwdQ : 0;
+  load_block(qb0 * kBwdQ);
+  store_block(0);
+  __syncthreads();
+
+  for (int64_t qb = qb0; qb < nqb; ++qb) {
+    if (qb + 1 < nqb) load_block((qb + 1) * kBwdQ);
+    const int st = (int)((qb - qb0) & 1);
+    const uint8_t *base = lds + st * L::kStage;
+    const _Float16 *qh = (const _Float16 *)(base + L::kQhOff);
+    const uint16_t *dor = (const uint16_t *)(base + L::kDoOff);
+    const uint8_t *dtr = base + L::kDtOff;
+    const float *lse2 = (const float *)(base + L::kLseOff);
+    const float *dlt = (const float *)(base + L::kDeltaOff);
+    const int64_t q0 = qb * kBwdQ;
+    bf16x8_t pb[2][2];
+    bool live[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int64_t qt0 = q0 + 32 * qt;
+      // some query of this tile sees some key of this wave (wave-uniform)
+      live[qt] = qt0 < S && (!a.causal || qt0 + 31 >= kw0);
+      floatx16_t sacc, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sacc[e] = 0.0f;
+        dp[e] = 0.0f;
+      }
+      if (live[qt]) {
+        const int r = 32 * qt + l32;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8_t *)(qh + r * L::kQh + 16 * t + 8 * h), kf[t],
+                                                         sacc, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(dor + r * L::kDo + 16 * t + 8 * h), vf[t],
+                                                        dp, 0, 0, 0);
+      }
+      // register e holds query q0 + 32 qt + 8 (e/4) + 4 h + e%4 of key `key`
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int qi = 32 * qt + 8 * c + 4 * h;
+        const float4 l4 = *(const float4 *)(lse2 + qi);
+        const float4 d4 = *(const float4 *)(dlt + qi);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * c + r;
+          const int64_t query = q0 + qi + r;
+          const bool valid = key_ok && query < S && (!a.causal || key <= query);
+          const float p = valid ? __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[r]) : 0.0f;
+          const float dsv = valid ? p * (dp[e] - dv[r]) : 0.0f;
+          pb[qt][e >> 3][e & 7] = (__bf16)p;
+          amax = fmaxf(amax, fabsf(dsv));
+          if (key_ok && query < S) a.ds[(g * S + query) * S + key] = dsv;
+        }
+      }
+    }
+    // ---- dV^T += dO^T P, queries in the registers' order ---------------------
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint8_t *drow = dtr + (dt * 32 + l32) * L::kDt * 2;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int qt = u >> 1, s = u & 1;
+        if (!live[qt]) continue;
+        const int kk = 32 * qt + 16 * s + 4 * h;   // queries kk..kk+3 and kk+8..kk+11
+        const uint2 v0 = *(const uint2 *)(drow + kk * 2);
+        const uint2 v1 = *(const uint2 *)(drow + (kk + 8) * 2);
+        const uint32_t vw[4] = {v0.x, v0.y, v1.x, v1.y};
+        bf16x8_t af;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          af[2 * i] = __builtin_bit_cast(__bf16, (uint16_t)(vw[i] & 0xFFFFu));
+          af[2 * i + 1] = __builtin_bit_cast(__bf16, (uint16_t)(vw[i] >> 16));
+        }
+        dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[qt][s], dvt[dt], 0, 0, 0);
+      }
+    }
+    if (qb + 1 < nqb) store_block(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- dV, and this workgroup's max |dS| -----------------------------------
+  if (key_ok) {
+    float *vrow = a.dv + (g * S + key) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *(float4 *)(vrow + dt * 32 + 8 * c + 4 * h) =
+            make_float4(dvt[dt][4 * c], dvt[dt][4 * c + 1], dvt[dt][4 * c + 2], dvt[dt][4 * c + 3]);
+  }
+  uint32_t m = __builtin_bit_cast(uint32_t, amax);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(m, off, 64);
+    m = m > o ? m : o;
+  }
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t r = red[0];
+#pragma unroll
+    for (int i = 1; i < kAttnThreads / 64; ++i) r = r > red[i] ? r : red[i];
+    a.amax[blockIdx.x] = r;
+  }
+}
+
+// Delta[row] = sum_d dO[row][d] O[row][d] (fp32), D / 8 lanes per row
+template <int D>
+__global__ __launch_bounds__(256) void attention_delta_kernel(const uint16_t *__restrict__ dout,
+                                                              const float *__restrict__ o, int64_t rows,
+                                                              float *__restrict__ delta) {
+  constexpr int TPR = D / 8;
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c = (threadIdx.x % TPR) * 8;
+  float acc = 0.0f;
+  if (row < rows) {
+    const uint4 dw = *(const uint4 *)(dout + row * D + c);
+    const float4 o0 = *(const float4 *)(o + row * D + c), o1 = *(const float4 *)(o + row * D + c + 4);
+    const uint32_t wv[4] = {dw.x, dw.y, dw.z, dw.w};
+    const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc += __builtin_bit_cast(float, wv[i] << 16) * ov[2 * i];
+      acc += __builtin_bit_cast(float, wv[i] & 0xFFFF0000u) * ov[2 * i + 1];
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && threadIdx.x % TPR == 0) delta[row] = acc;
+}
+
+// ---- dQ and dK: batched NT products of NVFP4 views --------------------------
+// C_g = s_a s_b scale A_g B_g^T for every sequence g, A_g [S][S] and B_g [D][S]
+// NVFP4 views (blocks along the contraction) at a per-sequence offset within
+// larger views.  Under a causal mask dS is lower triangular, so dQ's rows
+// (queries) contract over the keys up to their block's end, and dK's rows
+// (keys) over the queries from their block's start; the skipped products are
+// exact zeros.  Each workgroup forms 256 rows x D, 64 rows per wave, with
+// both operands expanded to FP16 into LDS 64 columns at a time.
+constexpr int kDsBM = 256;
+constexpr int kDsKC = 64;
+
+struct DsOperand {
+  const uint8_t *codes, *scales;
+  int64_t ld, gs;   // bytes of codes: row stride and per-sequence offset (scales: both / 8)
+};
+struct DsGemmArgs {
+  DsOperand a[2], b[2];
+  const float *ts_a[2], *ts_b[2];
+  float *c[2];      // fp32 [G][S][D]
+  int mode[2];      // 0 every column, 1 columns before the row block's end, 2 from its start
+  int64_t G, S;
+  float scale;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attention_ds_gemm_kernel(DsGemmArgs p) {
+  constexpr int TN = D / 32;
+  constexpr int TM = 2;
+  constexpr int kH = kDsKC + 8;                 // FP16 per LDS row
+  constexpr int A_BYTES = kDsBM * kH * 2, B_BYTES = D * kH * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int APER = kDsBM * (kDsKC / 16) / 256;   // 16-element units per thread
+  constexpr int BPER = D * (kDsKC / 16) / 256;
+  static_assert(APER == 4 && BPER >= 1, "staging");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+
+  const int z = blockIdx.y;
+  const DsOperand A = p.a[z], B = p.b[z];
+  const int mode = p.mode[z];
+  const int64_t G = p.G, S = p.S;
+  const int64_t nrb = (S + kDsBM - 1) / kDsBM;
+  const int64_t g = blockIdx.x % G;
+  const int64_t rbx = (int64_t)blockIdx.x / G;
+  const int64_t rb = mode == 1 ? nrb - 1 - rbx : rbx;   // the longest row blocks first
+  const int64_t r0 = rb * kDsBM;
+  const int64_t k_lo = mode == 2 ? r0 : 0;
+  const int64_t k_hi = mode == 1 ? (r0 + kDsBM < S ? r0 + kDsBM : S) : S;
+  const int nkc = (int)((k_hi - k_lo + kDsKC - 1) / kDsKC);
+  const uint8_t *ac = A.codes + g * A.gs, *as = A.scales + g * (A.gs / 8);
+  const uint8_t *bc = B.codes + g * B.gs, *bs = B.scales + g * (B.gs / 8);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+
+  uint2 ra[APER], rbv[BPER];
+  uint32_t ras = 0, rbs = 0;   // one scale byte per unit
+  auto load = [&](int kc) {
+    const int64_t kk0 = k_lo + (int64_t)kc * kDsKC;
+    ras = 0;
+    rbs = 0;
+#pragma unroll
+    for (int i = 0; i < APER; ++i) {
+      const int u = tid + i * 256, row = u >> 2, blk = u & 3;
+      const int64_t rg = r0 + row, kg = kk0 + 16 * blk;
+      const bool ok = rg < S && kg < k_hi;
+      ra[i] = ok ? *(const uint2 *)(ac + rg * A.ld + kg / 2) : make_uint2(0, 0);
+      ras |= (ok ? (uint32_t)as[rg * (A.ld / 8) + kg / 16] : 0u) << (8 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < BPER; ++i) {
+      const int u = tid + i * 256, row = u >> 2, blk = u & 3;
+      const int64_t kg = kk0 + 16 * blk;
+      const bool ok = kg < k_hi;
+      rbv[i] = ok ? *(const uint2 *)(bc + row * B.ld + kg / 2) : make_uint2(0, 0);
+      rbs |= (ok ? (uint32_t)bs[row * (B.ld / 8) + kg / 16] : 0u) << (8 * i);
+    }
+  };
+  auto store = [&](int st) {
+    _Float16 *ah = (_Float16 *)(lds + st * STAGE);
+    _Float16 *bh = (_Float16 *)(lds + st * STAGE + A_BYTES);
+#pragma unroll
+    for (int i = 0; i < APER; ++i) {
+      const int u = tid + i * 256, row = u >> 2, blk = u & 3;
+      const ScalePair sp = split_scale((ras >> (8 * i)) & 0xFFu);
+      *(f16x8_t *)(ah + row * kH + 16 * blk) = expand8(ra[i].x, sp);
+      *(f16x8_t *)(ah + row * kH + 16 * blk + 8) = expand8(ra[i].y, sp);
+    }
+#pragma unroll
+    for (int i = 0; i < BPER; ++i) {
+      const int u = tid + i * 256, row = u >> 2, blk = u & 3;
+      const ScalePair sp = split_scale((rbs >> (8 * i)) & 0xFFu);
+      *(f16x8_t *)(bh + row * kH + 16 * blk) = expand8(rbv[i].x, sp);
+      *(f16x8_t *)(bh + row * kH + 16 * blk + 8) = expand8(rbv[i].y, sp);
+    }
+  };
+
+  floatx16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  if (nkc > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int kc = 0; kc < nkc; ++kc) {
+    if (kc + 1 < nkc) load(kc + 1);
+    const _Float16 *ah = (const _Float16 *)(lds + (kc & 1) * STAGE);
+    const _Float16 *bh = (const _Float16 *)(lds + (kc & 1) * STAGE + A_BYTES);
+#pragma unroll
+    for (int ks = 0; ks < kDsKC / 16; ++ks) {
+      f16x8_t af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *(const f16x8_t *)(ah + (64 * w + 32 * i + l32) * kH + 16 * ks + 8 * h);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[j] = *(const f16x8_t *)(bh + (32 * j + l32) * kH + 16 * ks + 8 * h);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (kc + 1 < nkc) store((kc + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- C = alpha acc: lane holds column 32 j + l32, rows 8 (e/4) + 4 h + e%4
+  const float alpha = (*p.ts_a[z]) * (*p.ts_b[z]) * p.scale;
+  float *c = p.c[z] + g * S * D;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t row = r0 + 64 * w + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (row < S) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) c[row * D + 32 * j + l32] = alpha * acc[i][j][e];
+      }
+    }
+}
+
 }  // namespace
 
 size_t attention_fwd_ws_bytes(int64_t G, int64_t S, int64_t D) {
@@ -330,6 +779,70 @@ fs4_status launch_attention_fwd(const fs4_nvfp4 &Q, const fs4_nvfp4 &K, const ui
   const unsigned grid = (unsigned)(G * nqb);
   if (D == 128) attention_fwd_kernel<128><<<grid, kAttnThreads, 0, s>>>(a);
   else attention_fwd_kernel<64><<<grid, kAttnThreads, 0, s>>>(a);
+  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+}
+
+size_t attention_bwd_ws_bytes(int64_t G, int64_t S, int64_t D) {
+  Carver c(nullptr);
+  attention_bwd_carve(c, G, S, D);
+  return c.off;
+}
+
+AttnBwdWs attention_bwd_carve(Carver &c, int64_t G, int64_t S, int64_t D) {
+  AttnBwdWs w;
+  w.doutt = (uint16_t *)c.take((size_t)(G * S * D) * 2);
+  w.delta = (float *)c.take((size_t)(G * S) * 4);
+  w.nwg = G * ((S + kBwdKeys - 1) / kBwdKeys);
+  w.amax = (uint32_t *)c.take((size_t)w.nwg * 4);
+  w.ds = (float *)c.take((size_t)(G * S) * (size_t)S * 4);
+  w.ds_row = carve_view(c, G * S, S);
+  w.ds_col = carve_view(c, S, G * S);
+  return w;
+}
+
+fs4_status launch_attention_bwd(const fs4_nvfp4 &Qr, const fs4_nvfp4 &Kr, const fs4_nvfp4 &Qc,
+                                const fs4_nvfp4 &Kc, const uint16_t *V, const uint16_t *dO, const float *O,
+                                const float *LSE, int64_t G, int64_t S, int64_t D, int causal, float *dQ,
+                                float *dK, float *dV, float *dS, const AttnBwdWs &w, hipStream_t s) {
+  const dim3 tg((unsigned)((S + 63) / 64), (unsigned)((D + 63) / 64), (unsigned)G);
+  transpose_bf16_kernel<<<tg, 256, 0, s>>>(dO, S, D, w.doutt);
+  const int64_t rows = G * S;
+  const unsigned dgrid = (unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)));
+  if (D == 128) attention_delta_kernel<128><<<dgrid, 256, 0, s>>>(dO, O, rows, w.delta);
+  else attention_delta_kernel<64><<<dgrid, 256, 0, s>>>(dO, O, rows, w.delta);
+  if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
+
+  float *ds = dS ? dS : w.ds;
+  AttnBwdArgs a;
+  a.q_codes = Qr.codes; a.q_scales = Qr.scales; a.k_codes = Kr.codes; a.k_scales = Kr.scales;
+  a.q_ts = Qr.tscale; a.k_ts = Kr.tscale;
+  a.v = V; a.dout = dO; a.doutt = w.doutt; a.lse = LSE; a.delta = w.delta;
+  a.ds = ds; a.dv = dV; a.amax = w.amax;
+  a.G = G; a.S = S;
+  a.scale = (float)(1.0 / __builtin_sqrt((double)D));
+  a.causal = causal;
+  if (D == 128) attention_bwd_kernel<128><<<(unsigned)w.nwg, kAttnThreads, 0, s>>>(a);
+  else attention_bwd_kernel<64><<<(unsigned)w.nwg, kAttnThreads, 0, s>>>(a);
+  if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
+
+  // dS -> its row-wise (blocks along keys) and column-wise (along queries) views
+  const fs4_status qs = launch_quantize_encode(ds, FS4_FP32, G * S, S, &w.ds_row, &w.ds_col, w.amax, (int)w.nwg, s);
+  if (qs != FS4_OK) return qs;
+
+  DsGemmArgs p;
+  // dQ_g = Q(dS_g) Q_col(K_g)^T: dS rows g*S.., K^T columns g*S..
+  p.a[0] = {w.ds_row.codes, w.ds_row.scales, S / 2, S * S / 2};
+  p.b[0] = {Kc.codes, Kc.scales, G * S / 2, S / 2};
+  p.ts_a[0] = w.ds_row.tscale; p.ts_b[0] = Kc.tscale; p.c[0] = dQ; p.mode[0] = causal ? 1 : 0;
+  // dK_g = Q(dS_g^T) Q_col(Q_g)^T: dS^T columns g*S.., Q^T columns g*S..
+  p.a[1] = {w.ds_col.codes, w.ds_col.scales, G * S / 2, S / 2};
+  p.b[1] = {Qc.codes, Qc.scales, G * S / 2, S / 2};
+  p.ts_a[1] = w.ds_col.tscale; p.ts_b[1] = Qc.tscale; p.c[1] = dK; p.mode[1] = causal ? 2 : 0;
+  p.G = G; p.S = S;
+  p.scale = a.scale;
+  const dim3 grid((unsigned)(G * ((S + kDsBM - 1) / kDsBM)), 2);
+  if (D == 128) attention_ds_gemm_kernel<128><<<grid, 256, 0, s>>>(p);
+  else attention_ds_gemm_kernel<64><<<grid, 256, 0, s>>>(p);
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 

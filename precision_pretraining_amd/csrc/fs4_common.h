@@ -134,6 +134,24 @@ size_t attention_fwd_ws_bytes(int64_t G, int64_t S, int64_t D);
 fs4_status launch_attention_fwd(const fs4_nvfp4 &Q, const fs4_nvfp4 &K, const uint16_t *V, int64_t G, int64_t S,
                                 int64_t D, int causal, float *O, float *LSE, uint16_t *Vt, hipStream_t s);
 
+// Its backward.  Workspace: dO^T, Delta, one amax partial per softmax-gradient
+// workgroup, dS in fp32 [G*S][S] (unused when the caller takes dS) and dS's
+// two NVFP4 views (row-wise [G*S][S], column-wise [S][G*S]).
+struct AttnBwdWs {
+  uint16_t *doutt;
+  float *delta;
+  uint32_t *amax;
+  int64_t nwg;
+  float *ds;
+  fs4_nvfp4 ds_row, ds_col;
+};
+AttnBwdWs attention_bwd_carve(Carver &c, int64_t G, int64_t S, int64_t D);
+size_t attention_bwd_ws_bytes(int64_t G, int64_t S, int64_t D);
+fs4_status launch_attention_bwd(const fs4_nvfp4 &Qr, const fs4_nvfp4 &Kr, const fs4_nvfp4 &Qc,
+                                const fs4_nvfp4 &Kc, const uint16_t *V, const uint16_t *dO, const float *O,
+                                const float *LSE, int64_t G, int64_t S, int64_t D, int causal, float *dQ,
+                                float *dK, float *dV, float *dS, const AttnBwdWs &w, hipStream_t s);
+
 struct LowRankEpilogue {
   const float *L = nullptr;     // fp32 [M][r], scaled by l_scale before use
   const uint16_t *R = nullptr;  // bf16, element (n, j) at R[n * r_sn + j * r_sj]

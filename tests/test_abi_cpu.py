@@ -373,3 +373,54 @@ def test_ns_shape_coefficients_match_the_oracle():
     assert lib.fs4_ns_shape_coefficients(0, 16, 5, out, None) == ARG
     assert lib.fs4_ns_shape_coefficients(16, 16, 0, out, None) == ARG
     assert lib.fs4_ns_shape_coefficients(16, 16, 5, None, None) == NULL
+
+
+def afwd(G=2, S=64, D=128, qr="ok", kr="ok", V=A16, O=A16 * 2, LSE=A16 * 3, Vt=A16 * 4, wsb=0):
+    qv = view(G * S, D) if qr == "ok" else qr
+    kv = view(G * S, D) if kr == "ok" else kr
+    return lib.fs4_attention_fwd(ctypes.byref(qv) if qv is not None else None,
+                                 ctypes.byref(kv) if kv is not None else None, V, G, S, D, 1, O, LSE, Vt,
+                                 A16 * 16 if wsb else None, wsb, None)
+
+
+def test_attention_fwd_validation():
+    assert afwd(D=96) == SHAPE
+    assert afwd(S=40) == SHAPE
+    assert afwd(G=0) == SHAPE
+    assert afwd(qr=view(2 * 64, 64)) == SHAPE
+    assert afwd(kr=None) == NULL
+    assert afwd(V=None) == NULL
+    assert afwd(O=A16 + 8) == ALIGN
+    assert afwd(LSE=A16 + 2) == ALIGN
+    assert afwd(Vt=None, wsb=0) == WORKSPACE
+    assert lib.fs4_attention_fwd_workspace_bytes(2, 64, 128) >= 2 * 64 * 128 * 2
+    assert lib.fs4_attention_fwd_workspace_bytes(2, 64, 96) == 0
+
+
+def abwd(G=2, S=64, D=128, qr="ok", kr="ok", qc="ok", kc="ok", V=A16, dO=A16 * 2, O=A16 * 3, LSE=A16 * 4,
+         dQ=A16 * 5, dK=A16 * 6, dV=A16 * 7, dS=None, wsb=1 << 30):
+    views = []
+    for v, shape in ((qr, (G * S, D)), (kr, (G * S, D)), (qc, (D, G * S)), (kc, (D, G * S))):
+        views.append(view(*shape) if v == "ok" else v)
+    refs = [ctypes.byref(v) if v is not None else None for v in views]
+    return lib.fs4_attention_bwd(*refs, V, dO, O, LSE, G, S, D, 1, dQ, dK, dV, dS, A16 * 256, wsb, None)
+
+
+def test_attention_bwd_validation():
+    assert abwd(D=32) == SHAPE
+    assert abwd(S=24) == SHAPE
+    assert abwd(G=0) == SHAPE
+    assert abwd(G=1 << 12, S=1 << 10) == SHAPE              # G S^2 = 2^32 elements of dS
+    assert abwd(qc=view(128, 2 * 64 + 16)) == SHAPE
+    assert abwd(S=96, kc=view(2 * 96, 128)) == SHAPE         # K's row view where its column view goes
+    assert abwd(qr=None) == NULL
+    assert abwd(dO=None) == NULL
+    assert abwd(LSE=None) == NULL
+    assert abwd(dV=A16 + 4) == ALIGN
+    assert abwd(dS=A16 + 8) == ALIGN
+    assert abwd(wsb=1024) == WORKSPACE
+    need = lib.fs4_attention_bwd_workspace_bytes(2, 64, 128)
+    assert need >= 2 * 64 * 64 * 4 + 2 * 64 * 128 * 2        # dS in fp32 and dO^T
+    assert abwd(wsb=need - 1) == WORKSPACE
+    assert lib.fs4_attention_bwd_workspace_bytes(2, 64, 96) == 0
+    assert lib.fs4_attention_bwd_workspace_bytes(1 << 12, 1 << 10, 128) == 0
