@@ -368,12 +368,28 @@ def main():
             full()
         k_ms = time_calls(kern, reps)
         f_ms = time_calls(full, reps)
-        return {"workload": "Q-Attn forward, 96 sequences (4 x 24 heads) x 2048 tokens, head dim 128, causal",
-                "gflop": round(flop / 1e9, 2), "unit": "TFLOP/s",
-                "attention_kernel_ms": round(k_ms, 4), "achieved": round(flop / (k_ms * 1e-3) / 1e12, 2),
-                "frac": round(flop / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "with_qk_quantization_ms": round(f_ms, 4),
-                "achieved_with_quantization": round(flop / (f_ms * 1e-3) / 1e12, 2)}
+        out = {"workload": "Q-Attn forward, 96 sequences (4 x 24 heads) x 2048 tokens, head dim 128, causal",
+               "gflop": round(flop / 1e9, 2), "unit": "TFLOP/s",
+               "attention_kernel_ms": round(k_ms, 4), "achieved": round(flop / (k_ms * 1e-3) / 1e12, 2),
+               "frac": round(flop / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "with_qk_quantization_ms": round(f_ms, 4),
+               "achieved_with_quantization": round(flop / (f_ms * 1e-3) / 1e12, 2)}
+        # the backward: S recomputed, dP = dO V^T, dV = P^T dO, dQ, dK (five
+        # products over the visible triangle), dS through fp32 and the encode
+        # pass
+        dOa = torch.randn((Gh, Sq, Dh), device=dev, generator=gen).bfloat16()
+        qv, kv = fs4.attention_quantize(Qa), fs4.attention_quantize(Ka)
+        fw = fs4.attention_fwd(qv[0], kv[0], Va)
+        bwd = lambda: fs4.attention_bwd(dOa, Va, fw, qv, kv)
+        for _ in range(3):
+            bwd()
+        b_ms = time_calls(bwd, reps)
+        bflop = flop * 5 / 2
+        out["backward"] = {"gflop": round(bflop / 1e9, 2), "ms": round(b_ms, 4),
+                           "achieved": round(bflop / (b_ms * 1e-3) / 1e12, 2),
+                           "frac": round(bflop / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "ds_fp32_bytes": Gh * Sq * Sq * 4}
+        return out
 
     if a.only == "gemm":
         print(json.dumps({"only": "gemm", "roofline": gemm_leg(max(3, a.steps))}), flush=True)

@@ -347,6 +347,7 @@ struct AttnBwdArgs {
   int64_t G, S;
   float scale;
   int causal;
+  int zero_fill;          // write the zeros above the diagonal that no query block covers
 };
 
 template <int D>
@@ -401,7 +402,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
   }
 
   // ---- under a causal mask, dS is zero for the queries before this block ---
-  if (a.causal && k0 > 0) {
+  // (not written when nothing reads it: the quantizer skips those tiles)
+  if (a.causal && a.zero_fill && k0 > 0) {
     const int64_t n4 = (kend - k0) / 4;
     for (int64_t i = tid; i < k0 * n4; i += kAttnThreads) {
       const int64_t row = i / n4, c = i % n4;
@@ -821,12 +823,17 @@ fs4_status launch_attention_bwd(const fs4_nvfp4 &Qr, const fs4_nvfp4 &Kr, const 
   a.G = G; a.S = S;
   a.scale = (float)(1.0 / __builtin_sqrt((double)D));
   a.causal = causal;
+  // With S % 64 == 0 the quantizer's 64 x 64 tiles line up with the sequences,
+  // and every tile of the region above the diagonal that no query block
+  // covers lies wholly above it, so the quantizer never reads that region.
+  a.zero_fill = dS != nullptr || S % 64 != 0;
   if (D == 128) attention_bwd_kernel<128><<<(unsigned)w.nwg, kAttnThreads, 0, s>>>(a);
   else attention_bwd_kernel<64><<<(unsigned)w.nwg, kAttnThreads, 0, s>>>(a);
   if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
 
   // dS -> its row-wise (blocks along keys) and column-wise (along queries) views
-  const fs4_status qs = launch_quantize_encode(ds, FS4_FP32, G * S, S, &w.ds_row, &w.ds_col, w.amax, (int)w.nwg, s);
+  const fs4_status qs = launch_quantize_encode(ds, FS4_FP32, G * S, S, &w.ds_row, &w.ds_col, w.amax, (int)w.nwg, s,
+                                               nullptr, causal ? S : 0);
   if (qs != FS4_OK) return qs;
 
   DsGemmArgs p;

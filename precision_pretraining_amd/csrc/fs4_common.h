@@ -103,11 +103,13 @@ fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t co
 // The encode pass alone, for a caller whose earlier kernel already wrote npart
 // (npart >= 1) partial maxima of |x| (fp32 bits) that cover all of x.  With
 // clip (a device scalar p >= 0), x is clipped to magnitude p first and p is
-// its amax (the partials are not read).
+// its amax (the partials are not read).  With tri_s > 0 the caller promises
+// that x is a stack of tri_s-row blocks, each zero above its diagonal
+// (column > row within the block): 64 x 64 tiles lying there are not read.
 fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                                   const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                                   const uint32_t *partials, int npart, hipStream_t s,
-                                  const float *clip = nullptr);
+                                  const float *clip = nullptr, int64_t tri_s = 0);
 // *out = the k-th smallest |x| of x[0..n) (bf16 or fp32), k = ceil(q n) in
 // fp64 clamped to [1, n], by exact radix selection; ws needs
 // abs_quantile_ws_bytes().  n >= 1.

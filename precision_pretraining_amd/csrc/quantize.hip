@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
                                                             int64_t cols,
                                                             const uint32_t *__restrict__ partials,
                                                             int npart, fs4_nvfp4 rv, fs4_nvfp4 cv,
-                                                            const float *clip = nullptr) {
+                                                            const float *clip = nullptr, int64_t tri_s = 0) {
   __shared__ float tile[kTile][kTile + 1];
   __shared__ Tables tab;
   __shared__ uint32_t red[kThreads / 64];
@@ -426,9 +426,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
   int sr1 = sr, sc1 = sc;
   if (have) order.advance(sr1, sc1);
   int have1 = (have && order.seek(sr1, sc1)) ? 1 : 0;
+  // With tri_s > 0, x is a stack of tri_s-row blocks each zero above its
+  // diagonal (column > row within the block).  A tile that lies in one block
+  // and entirely above the diagonal is neither read nor encoded: its codes
+  // and scales are zero, as encoding its zeros would give.
+  auto zero_tile = [&](int r, int c) -> bool {
+    if (tri_s <= 0) return false;
+    const int64_t a = order.r0(r), b = order.c0(c);
+    const int64_t lr = a % tri_s;
+    return lr + kTile <= tri_s && b > lr + kTile - 1;
+  };
   TileRegs<BF16> g0, g1;
-  tile_gload<BF16>(x, rows, cols, order.r0(sr), order.c0(sc), have != 0, g0);
-  tile_gload<BF16>(x, rows, cols, order.r0(sr1), order.c0(sc1), have1 != 0, g1);
+  tile_gload<BF16>(x, rows, cols, order.r0(sr), order.c0(sc), have != 0 && !zero_tile(sr, sc), g0);
+  tile_gload<BF16>(x, rows, cols, order.r0(sr1), order.c0(sc1), have1 != 0 && !zero_tile(sr1, sc1), g1);
   build_tables_n<kThreads>(tab, s_t);
   // 1/(6 s_t) only seeds the scale-code estimate; the tables make it exact
   const float inv6st = s_t > 0.0f ? (float)(1.0 / (6.0 * (double)s_t)) : 0.0f;   // may be inf
@@ -448,17 +458,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
     int sr2 = sr1, sc2 = sc1;
     if (have1) order.advance(sr2, sc2);
     const int have2 = (have1 && order.seek(sr2, sc2)) ? 1 : 0;
-    tile_gload<BF16>(x, rows, cols, order.r0(sr2), order.c0(sc2), have2 != 0, ahead);
+    tile_gload<BF16>(x, rows, cols, order.r0(sr2), order.c0(sc2), have2 != 0 && !zero_tile(sr2, sc2), ahead);
     // zero padding outside the tensor encodes harmlessly; only stores are masked
     uint2 pr = make_uint2(0, 0), pc = make_uint2(0, 0);
     uint32_t sbr = 0, sbc = 0;
-    if (ROW) {
-      const float *src = &tile[line][blk * kBlock];
-      sbr = encode16([&](int i) { return src[i]; }, inv6st, inv_finite, tab, pr);
-    }
-    if (COL) {
-      const float *src = &tile[blk * kBlock][line];
-      sbc = encode16([&](int i) { return src[i * (kTile + 1)]; }, inv6st, inv_finite, tab, pc);
+    if (!zero_tile(sr, sc)) {
+      if (ROW) {
+        const float *src = &tile[line][blk * kBlock];
+        sbr = encode16([&](int i) { return src[i]; }, inv6st, inv_finite, tab, pr);
+      }
+      if (COL) {
+        const float *src = &tile[blk * kBlock][line];
+        sbc = encode16([&](int i) { return src[i * (kTile + 1)]; }, inv6st, inv_finite, tab, pc);
+      }
     }
     __syncthreads();
     tile_store<BF16, CLIP>(nxt, rows, cols, order.r0(sr1), order.c0(sc1), tile, clipv);   // unread past the last tile
@@ -499,7 +511,7 @@ size_t quantize_ws_bytes() { return kAmaxPartials * sizeof(uint32_t); }
 fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                                   const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                                   const uint32_t *partials, int npart, hipStream_t s,
-                                  const float *clip) {
+                                  const float *clip, int64_t tri_s) {
   const fs4_nvfp4 none = {nullptr, nullptr, nullptr, 0, 0};
   const fs4_nvfp4 rv = rowwise ? *rowwise : none;
   const fs4_nvfp4 cv = colwise ? *colwise : none;
@@ -514,9 +526,9 @@ fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int
 #define FS4_QK(B, R, C)                                                                            \
   do {                                                                                             \
     if (clip)                                                                                      \
-      quantize_kernel<B, R, C, true><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv, clip); \
+      quantize_kernel<B, R, C, true><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv, clip, tri_s); \
     else                                                                                           \
-      quantize_kernel<B, R, C><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv);  \
+      quantize_kernel<B, R, C><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv, nullptr, tri_s); \
   } while (0)
   if (bf16) {
     if (row && col) FS4_QK(true, true, true);

@@ -11,7 +11,9 @@ emulated second implementation and planted mistakes).  Two ways in:
   test's bars, which then widen the bounds of Delta and P.
 Every output is compared element by element: dS (fp32, before its
 quantization), dV, dQ, dK; the column-wise NVFP4 views of Q and K that the
-dS products read are compared bit for bit.
+dS products read are compared bit for bit, and a second call that does not
+keep dS (so the zeros above a causal diagonal are never written, nor read
+by the quantizer) must return the same dQ, dK and dV bit for bit.
 """
 import os
 
@@ -64,7 +66,12 @@ def _run(G, S, D, causal, seed, seqs=None, std_qk=1.0, chain=False):
                              torch.from_numpy(fwd["LSE"].astype(np.float32)).to(V.device), None)
         o_err, lse_err = 2.0 ** -24 * np.abs(fwd["O"]), 2.0 ** -24 * np.abs(fwd["LSE"])
     b = fs4.attention_bwd(dO, V, f, qv, kv, causal, keep_dS=True)
+    # without dS kept, the zeros above the diagonal are not written (the
+    # quantizer skips those tiles): the results must not change by a bit
+    b2 = fs4.attention_bwd(dO, V, f, qv, kv, causal, keep_dS=False)
     torch.cuda.synchronize()
+    for name in ("dQ", "dK", "dV"):
+        assert torch.equal(getattr(b, name), getattr(b2, name)), name
     for g in sel:
         _col_slice_equal(qv[1], fwd["Q_col"][g], g, S, "Q_col")
         _col_slice_equal(kv[1], fwd["K_col"][g], g, S, "K_col")
