@@ -21,7 +21,7 @@
 // the keys are contracted in the order the registers hold them, and the V^T
 // fragments are read from LDS in that same order (V is staged transposed,
 // [D][keys]).
-#include "fs4_common.h"
+#include "nvfp4_encode.h"
 
 namespace fs4 {
 namespace {
@@ -315,10 +315,12 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__r
 //   dP = dO V^T, Delta = rowsum(dO * O), dS = P * (dP - Delta)
 //   dV = P^T dO                        (P rounded to BF16, dO BF16)
 //   dQ = Q(dS) Q_col(K)^T / sqrt(D),  dK = Q(dS^T) Q_col(Q)^T / sqrt(D)
-// dS is quantized once, with one tensor scale over all sequences, so it is
-// materialised in fp32: the softmax-gradient kernel writes it together with
-// one partial amax per workgroup, the quantizer's encode pass turns it into
-// both NVFP4 views, and a batched NVFP4 product kernel forms dQ and dK.
+// dS is quantized once, with one tensor scale over all sequences, so the
+// keys are walked twice: the softmax-gradient kernel forms dS and dV and
+// keeps one partial amax of |dS| per workgroup; a second kernel forms dS
+// again, identically, and encodes it into both NVFP4 views with the tensor
+// scale those partials give; a batched NVFP4 product kernel forms dQ and dK.
+// dS never goes through memory in fp32 (unless the caller asks for it).
 //
 // The softmax-gradient kernel gives each workgroup 128 keys of one sequence,
 // 32 per wave, and walks the queries in blocks of 64.  A wave keeps its keys'
@@ -341,13 +343,12 @@ struct AttnBwdArgs {
   const uint16_t *doutt;  // bf16 [G][D][S]
   const float *lse;       // [G][S], natural log
   const float *delta;     // [G][S]
-  float *ds;              // fp32 [G*S][S]
+  float *ds;              // fp32 [G*S][S], nullable: dS for the caller
   float *dv;              // fp32 [G][S][D]
   uint32_t *amax;         // one max |dS| per workgroup (fp32 bits)
   int64_t G, S;
   float scale;
   int causal;
-  int zero_fill;          // write the zeros above the diagonal that no query block covers
 };
 
 template <int D>
@@ -402,8 +403,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
   }
 
   // ---- under a causal mask, dS is zero for the queries before this block ---
-  // (not written when nothing reads it: the quantizer skips those tiles)
-  if (a.causal && a.zero_fill && k0 > 0) {
+  if (a.ds && a.causal && k0 > 0) {
     const int64_t n4 = (kend - k0) / 4;
     for (int64_t i = tid; i < k0 * n4; i += kAttnThreads) {
       const int64_t row = i / n4, c = i % n4;
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
           const float dsv = valid ? p * (dp[e] - dv[r]) : 0.0f;
           pb[qt][e >> 3][e & 7] = (__bf16)p;
           amax = fmaxf(amax, fabsf(dsv));
-          if (key_ok && query < S) a.ds[(g * S + query) * S + key] = dsv;
+          if (a.ds && key_ok && query < S) a.ds[(g * S + query) * S + key] = dsv;
         }
       }
     }
@@ -589,6 +589,239 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
 #pragma unroll
     for (int i = 1; i < kAttnThreads / 64; ++i) r = r > red[i] ? r : red[i];
     a.amax[blockIdx.x] = r;
+  }
+}
+
+// ---- dS quantized where it is formed ----------------------------------------
+// The second pass over the keys: with the amax of dS known from the first
+// pass (its per-workgroup partials), each workgroup recomputes S, P, dP and
+// dS for its 128 keys exactly as the first pass does (same operands, same
+// instruction sequence) and encodes them into dS's two NVFP4 views, so dS
+// never goes through memory in fp32.  A wave's 32 x 32 tile of dS is staged
+// in its own LDS scratch; each lane then encodes one 16-key block of a query
+// (the row-wise view, blocks along keys) and one 16-query block of a key (the
+// column-wise view, blocks along queries).  Tiles wholly above a causal
+// diagonal are not encoded: the dQ and dK products skip those blocks.
+struct AttnDsqArgs {
+  const uint8_t *q_codes, *q_scales, *k_codes, *k_scales;
+  const float *q_ts, *k_ts;
+  const uint16_t *v;      // bf16 [G][S][D]
+  const uint16_t *dout;   // bf16 [G][S][D]
+  const float *lse;       // [G][S], natural log
+  const float *delta;     // [G][S]
+  const uint32_t *amax;   // the first pass's partial maxima of |dS| (fp32 bits)
+  int npart;
+  fs4_nvfp4 row, col;     // dS views: row-wise [G*S][S], column-wise [S][G*S]
+  int64_t G, S;
+  float scale;
+  int causal;
+};
+
+template <int D>
+struct DsqLds {
+  static constexpr int kQh = D + 8;
+  static constexpr int kDo = D + 8;
+  static constexpr int kQhOff = 0;
+  static constexpr int kDoOff = kQhOff + kBwdQ * kQh * 2;
+  static constexpr int kLseOff = kDoOff + kBwdQ * kDo * 2;
+  static constexpr int kDeltaOff = kLseOff + kBwdQ * 4;
+  static constexpr int kStage = kDeltaOff + kBwdQ * 4;
+  static constexpr int kEpt = kBwdQ * D / kAttnThreads;
+  static constexpr int kDoPer = kBwdQ * D * 2 / 16 / kAttnThreads;
+  static constexpr int kT = 33;                       // scratch row stride (floats)
+  static_assert(kStage % 16 == 0, "stage alignment");
+};
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void attention_dsq_kernel(AttnDsqArgs a) {
+  using L = DsqLds<D>;
+  constexpr int KSTEPS = D / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::kStage];   // one stage: two workgroups fit a CU
+  __shared__ float scratch[kAttnThreads / 64][32 * L::kT];
+  __shared__ Tables tab;
+  __shared__ uint32_t red[kAttnThreads / 64];
+
+  const int64_t G = a.G, S = a.S;
+  const int64_t g = blockIdx.x % G;
+  const int64_t kb = (int64_t)blockIdx.x / G;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int64_t k0 = kb * kBwdKeys;
+  const int64_t kw0 = k0 + w * 32;
+  const int64_t key = kw0 + l32;
+  const bool key_ok = key < S;
+  const int64_t keyc = key_ok ? key : S - 1;
+
+  // ---- dS's tensor scale from the first pass's partials; the tables --------
+  uint32_t m = 0;
+  for (int i = tid; i < a.npart; i += kAttnThreads) m = m > a.amax[i] ? m : a.amax[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(m, off, 64);
+    m = m > o ? m : o;
+  }
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int i = 1; i < kAttnThreads / 64; ++i) m = m > red[i] ? m : red[i];
+  const float s_t = (float)((double)__builtin_bit_cast(float, m) / kTensorDiv);
+  if (blockIdx.x == 0 && tid == 0) {
+    *a.row.tscale = s_t;
+    *a.col.tscale = s_t;
+  }
+  build_tables_n<kAttnThreads>(tab, s_t);
+  const float inv6st = s_t > 0.0f ? (float)(1.0 / (6.0 * (double)s_t)) : 0.0f;   // may be inf
+  const bool inv_finite = inv6st < __builtin_huge_valf();
+
+  // ---- this wave's keys: K expanded to FP16 and V, as in the first pass ---
+  f16x8_t kf[KSTEPS];
+  bf16x8_t vf[KSTEPS];
+  {
+    const uint8_t *krow = a.k_codes + (g * S + keyc) * (D / 2);
+    const uint8_t *ksc = a.k_scales + (g * S + keyc) * (D / 16);
+    const uint16_t *vrow = a.v + (g * S + keyc) * D;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      kf[t] = expand8(*(const uint32_t *)(krow + 8 * t + 4 * h), split_scale(ksc[t]));
+      vf[t] = *(const bf16x8_t *)(vrow + 16 * t + 8 * h);
+    }
+  }
+
+  uint4 rq = make_uint4(0, 0, 0, 0);
+  uint32_t rqs = 0;
+  uint4 rdo[L::kDoPer];
+  float rls = 0.0f;
+  const int qrow = tid / 4, qc0 = (tid % 4) * L::kEpt;
+  auto load_block = [&](int64_t q0) {
+    {
+      int64_t qq = q0 + qrow;
+      qq = qq < S ? qq : S - 1;
+      const uint8_t *cp = a.q_codes + (g * S + qq) * (D / 2) + qc0 / 2;
+      const uint8_t *sp = a.q_scales + (g * S + qq) * (D / 16) + qc0 / 16;
+      if constexpr (L::kEpt == 32) {
+        rq = *(const uint4 *)cp;
+        rqs = *(const uint16_t *)sp;
+      } else {
+        const uint2 t = *(const uint2 *)cp;
+        rq = make_uint4(t.x, t.y, 0u, 0u);
+        rqs = *sp;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < L::kDoPer; ++i) {
+      const int idx = tid + i * kAttnThreads;
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      const int64_t qq = q0 + row;
+      rdo[i] = qq < S ? *(const uint4 *)(a.dout + (g * S + qq) * D + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 2 * kBwdQ) {
+      const int64_t qq = q0 + (tid & (kBwdQ - 1));
+      rls = qq < S ? (tid < kBwdQ ? a.lse[g * S + qq] * kLog2e : a.delta[g * S + qq]) : 0.0f;
+    }
+  };
+  auto store_block = [&](int st) {
+    uint8_t *base = lds + st * L::kStage;
+    _Float16 *qh = (_Float16 *)(base + L::kQhOff) + qrow * L::kQh + qc0;
+    const uint32_t cw[4] = {rq.x, rq.y, rq.z, rq.w};
+#pragma unroll
+    for (int j = 0; j < L::kEpt / 8; ++j)
+      *(f16x8_t *)(qh + 8 * j) = expand8(cw[j], split_scale((rqs >> (8 * (j / 2))) & 0xFFu));
+#pragma unroll
+    for (int i = 0; i < L::kDoPer; ++i) {
+      const int idx = tid + i * kAttnThreads;
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      *(uint4 *)(base + L::kDoOff + (row * L::kDo + ch * 8) * 2) = rdo[i];
+    }
+    if (tid < 2 * kBwdQ) ((float *)(base + L::kLseOff))[tid] = rls;
+  };
+
+  const float c_log2 = (*a.q_ts) * (*a.k_ts) * a.scale * kLog2e;
+  float *sc = scratch[w];
+  const int bi = lane >> 1, bh = lane & 1;   // this lane's blocks: (query bi, keys 16 bh..) and (key bi, queries 16 bh..)
+  const int64_t GS = G * S;
+
+  const int64_t nqb = (S + kBwdQ - 1) / kBwdQ;
+  const int64_t qb0 = a.causal ? k0 / kBwdQ : 0;
+  load_block(qb0 * kBwdQ);
+  store_block(0);
+  __syncthreads();
+
+  for (int64_t qb = qb0; qb < nqb; ++qb) {
+    if (qb + 1 < nqb) load_block((qb + 1) * kBwdQ);
+    const uint8_t *base = lds;
+    const _Float16 *qh = (const _Float16 *)(base + L::kQhOff);
+    const uint16_t *dor = (const uint16_t *)(base + L::kDoOff);
+    const float *lse2 = (const float *)(base + L::kLseOff);
+    const float *dlt = (const float *)(base + L::kDeltaOff);
+    const int64_t q0 = qb * kBwdQ;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int64_t qt0 = q0 + 32 * qt;
+      // a tile wholly above the diagonal holds only zeros, which the dS
+      // products never read (wave-uniform)
+      if (qt0 >= S || (a.causal && qt0 + 31 < kw0)) continue;
+      floatx16_t sacc, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sacc[e] = 0.0f;
+        dp[e] = 0.0f;
+      }
+      const int r = 32 * qt + l32;
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8_t *)(qh + r * L::kQh + 16 * t + 8 * h), kf[t],
+                                                       sacc, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(dor + r * L::kDo + 16 * t + 8 * h), vf[t],
+                                                      dp, 0, 0, 0);
+      // dS exactly as the first pass forms it; the tile goes to the scratch
+      // as [key][query]
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int qi = 32 * qt + 8 * c + 4 * h;
+        const float4 l4 = *(const float4 *)(lse2 + qi);
+        const float4 d4 = *(const float4 *)(dlt + qi);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int e = 4 * c + rr;
+          const int64_t query = q0 + qi + rr;
+          const bool valid = key_ok && query < S && (!a.causal || key <= query);
+          const float p = valid ? __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[rr]) : 0.0f;
+          sc[l32 * L::kT + 8 * c + 4 * h + rr] = valid ? p * (dp[e] - dv[rr]) : 0.0f;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // row-wise view: query bi of the tile, keys 16 bh .. 16 bh + 15
+      {
+        uint2 pk;
+        const float *src = sc + 16 * bh * L::kT + bi;
+        const uint32_t sb = encode16([&](int i) { return src[i * L::kT]; }, inv6st, inv_finite, tab, pk);
+        const int64_t query = qt0 + bi, k16 = kw0 + 16 * bh;
+        if (query < S && k16 < S) {
+          *(uint2 *)(a.row.codes + (g * S + query) * (S / 2) + k16 / 2) = pk;
+          a.row.scales[(g * S + query) * (S / 16) + k16 / 16] = (uint8_t)sb;
+        }
+      }
+      // column-wise view: key bi of the tile, queries 16 bh .. 16 bh + 15
+      {
+        uint2 pk;
+        const float *src = sc + bi * L::kT + 16 * bh;
+        const uint32_t sb = encode16([&](int i) { return src[i]; }, inv6st, inv_finite, tab, pk);
+        const int64_t kk = kw0 + bi, q16 = qt0 + 16 * bh;
+        if (kk < S && q16 < S) {
+          *(uint2 *)(a.col.codes + kk * (GS / 2) + (g * S + q16) / 2) = pk;
+          a.col.scales[kk * (GS / 16) + (g * S + q16) / 16] = (uint8_t)sb;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (qb + 1 < nqb) {
+      __syncthreads();
+      store_block(0);
+    }
+    __syncthreads();
   }
 }
 
@@ -679,7 +912,10 @@ __global__ __launch_bounds__(256) void attention_ds_gemm_kernel(DsGemmArgs p) {
     for (int i = 0; i < APER; ++i) {
       const int u = tid + i * 256, row = u >> 2, blk = u & 3;
       const int64_t rg = r0 + row, kg = kk0 + 16 * blk;
-      const bool ok = rg < S && kg < k_hi;
+      // blocks wholly above a causal diagonal are zero and are not read:
+      // dQ (rows are queries) past the row, dK (rows are keys) before it
+      const bool above = (mode == 1 && kg > rg) || (mode == 2 && kg + 15 < rg);
+      const bool ok = rg < S && kg < k_hi && !above;
       ra[i] = ok ? *(const uint2 *)(ac + rg * A.ld + kg / 2) : make_uint2(0, 0);
       ras |= (ok ? (uint32_t)as[rg * (A.ld / 8) + kg / 16] : 0u) << (8 * i);
     }
@@ -796,7 +1032,6 @@ AttnBwdWs attention_bwd_carve(Carver &c, int64_t G, int64_t S, int64_t D) {
   w.delta = (float *)c.take((size_t)(G * S) * 4);
   w.nwg = G * ((S + kBwdKeys - 1) / kBwdKeys);
   w.amax = (uint32_t *)c.take((size_t)w.nwg * 4);
-  w.ds = (float *)c.take((size_t)(G * S) * (size_t)S * 4);
   w.ds_row = carve_view(c, G * S, S);
   w.ds_col = carve_view(c, S, G * S);
   return w;
@@ -814,27 +1049,34 @@ fs4_status launch_attention_bwd(const fs4_nvfp4 &Qr, const fs4_nvfp4 &Kr, const 
   else attention_delta_kernel<64><<<dgrid, 256, 0, s>>>(dO, O, rows, w.delta);
   if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
 
-  float *ds = dS ? dS : w.ds;
+  const float scale = (float)(1.0 / __builtin_sqrt((double)D));
+  // first pass over the keys: dV, the amax of dS (and dS when asked for)
   AttnBwdArgs a;
   a.q_codes = Qr.codes; a.q_scales = Qr.scales; a.k_codes = Kr.codes; a.k_scales = Kr.scales;
   a.q_ts = Qr.tscale; a.k_ts = Kr.tscale;
   a.v = V; a.dout = dO; a.doutt = w.doutt; a.lse = LSE; a.delta = w.delta;
-  a.ds = ds; a.dv = dV; a.amax = w.amax;
+  a.ds = dS; a.dv = dV; a.amax = w.amax;
   a.G = G; a.S = S;
-  a.scale = (float)(1.0 / __builtin_sqrt((double)D));
+  a.scale = scale;
   a.causal = causal;
-  // With S % 64 == 0 the quantizer's 64 x 64 tiles line up with the sequences,
-  // and every tile of the region above the diagonal that no query block
-  // covers lies wholly above it, so the quantizer never reads that region.
-  a.zero_fill = dS != nullptr || S % 64 != 0;
   if (D == 128) attention_bwd_kernel<128><<<(unsigned)w.nwg, kAttnThreads, 0, s>>>(a);
   else attention_bwd_kernel<64><<<(unsigned)w.nwg, kAttnThreads, 0, s>>>(a);
   if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
 
-  // dS -> its row-wise (blocks along keys) and column-wise (along queries) views
-  const fs4_status qs = launch_quantize_encode(ds, FS4_FP32, G * S, S, &w.ds_row, &w.ds_col, w.amax, (int)w.nwg, s,
-                                               nullptr, causal ? S : 0);
-  if (qs != FS4_OK) return qs;
+  // second pass: dS again, encoded into its row-wise (blocks along keys) and
+  // column-wise (blocks along queries) views
+  AttnDsqArgs q;
+  q.q_codes = Qr.codes; q.q_scales = Qr.scales; q.k_codes = Kr.codes; q.k_scales = Kr.scales;
+  q.q_ts = Qr.tscale; q.k_ts = Kr.tscale;
+  q.v = V; q.dout = dO; q.lse = LSE; q.delta = w.delta;
+  q.amax = w.amax; q.npart = (int)w.nwg;
+  q.row = w.ds_row; q.col = w.ds_col;
+  q.G = G; q.S = S;
+  q.scale = scale;
+  q.causal = causal;
+  if (D == 128) attention_dsq_kernel<128><<<(unsigned)w.nwg, kAttnThreads, 0, s>>>(q);
+  else attention_dsq_kernel<64><<<(unsigned)w.nwg, kAttnThreads, 0, s>>>(q);
+  if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
 
   DsGemmArgs p;
   // dQ_g = Q(dS_g) Q_col(K_g)^T: dS rows g*S.., K^T columns g*S..
@@ -846,7 +1088,7 @@ fs4_status launch_attention_bwd(const fs4_nvfp4 &Qr, const fs4_nvfp4 &Kr, const 
   p.b[1] = {Qc.codes, Qc.scales, G * S / 2, S / 2};
   p.ts_a[1] = w.ds_col.tscale; p.ts_b[1] = Qc.tscale; p.c[1] = dK; p.mode[1] = causal ? 2 : 0;
   p.G = G; p.S = S;
-  p.scale = a.scale;
+  p.scale = scale;
   const dim3 grid((unsigned)(G * ((S + kDsBM - 1) / kDsBM)), 2);
   if (D == 128) attention_ds_gemm_kernel<128><<<grid, 256, 0, s>>>(p);
   else attention_ds_gemm_kernel<64><<<grid, 256, 0, s>>>(p);

@@ -103,13 +103,11 @@ fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t co
 // The encode pass alone, for a caller whose earlier kernel already wrote npart
 // (npart >= 1) partial maxima of |x| (fp32 bits) that cover all of x.  With
 // clip (a device scalar p >= 0), x is clipped to magnitude p first and p is
-// its amax (the partials are not read).  With tri_s > 0 the caller promises
-// that x is a stack of tri_s-row blocks, each zero above its diagonal
-// (column > row within the block): 64 x 64 tiles lying there are not read.
+// its amax (the partials are not read).
 fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                                   const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                                   const uint32_t *partials, int npart, hipStream_t s,
-                                  const float *clip = nullptr, int64_t tri_s = 0);
+                                  const float *clip = nullptr);
 // *out = the k-th smallest |x| of x[0..n) (bf16 or fp32), k = ceil(q n) in
 // fp64 clamped to [1, n], by exact radix selection; ws needs
 // abs_quantile_ws_bytes().  n >= 1.
@@ -137,14 +135,13 @@ fs4_status launch_attention_fwd(const fs4_nvfp4 &Q, const fs4_nvfp4 &K, const ui
                                 int64_t D, int causal, float *O, float *LSE, uint16_t *Vt, hipStream_t s);
 
 // Its backward.  Workspace: dO^T, Delta, one amax partial per softmax-gradient
-// workgroup, dS in fp32 [G*S][S] (unused when the caller takes dS) and dS's
-// two NVFP4 views (row-wise [G*S][S], column-wise [S][G*S]).
+// workgroup and dS's two NVFP4 views (row-wise [G*S][S], column-wise
+// [S][G*S]).
 struct AttnBwdWs {
   uint16_t *doutt;
   float *delta;
   uint32_t *amax;
   int64_t nwg;
-  float *ds;
   fs4_nvfp4 ds_row, ds_col;
 };
 AttnBwdWs attention_bwd_carve(Carver &c, int64_t G, int64_t S, int64_t D);
