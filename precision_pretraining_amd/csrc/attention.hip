@@ -93,7 +93,7 @@ struct AttnLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs a) {
   using L = AttnLds<D>;
   constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int DT = D / 32;       // 32-row tiles of O^T
