@@ -875,7 +875,7 @@ struct DsGemmArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void attention_ds_gemm_kernel(DsGemmArgs p) {
+__global__ __launch_bounds__(256, 2) void attention_ds_gemm_kernel(DsGemmArgs p) {
   constexpr int TN = D / 32;
   constexpr int TM = 2;
   constexpr int kH = kDsKC + 8;                 // FP16 per LDS row
@@ -884,7 +884,7 @@ __global__ __launch_bounds__(256) void attention_ds_gemm_kernel(DsGemmArgs p) {
   constexpr int APER = kDsBM * (kDsKC / 16) / 256;   // 16-element units per thread
   constexpr int BPER = D * (kDsKC / 16) / 256;
   static_assert(APER == 4 && BPER >= 1, "staging");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[STAGE];   // one stage: two workgroups fit a CU
 
   const int z = blockIdx.y;
   const DsOperand A = p.a[z], B = p.b[z];
@@ -962,8 +962,8 @@ __global__ __launch_bounds__(256) void attention_ds_gemm_kernel(DsGemmArgs p) {
   }
   for (int kc = 0; kc < nkc; ++kc) {
     if (kc + 1 < nkc) load(kc + 1);
-    const _Float16 *ah = (const _Float16 *)(lds + (kc & 1) * STAGE);
-    const _Float16 *bh = (const _Float16 *)(lds + (kc & 1) * STAGE + A_BYTES);
+    const _Float16 *ah = (const _Float16 *)lds;
+    const _Float16 *bh = (const _Float16 *)(lds + A_BYTES);
 #pragma unroll
     for (int ks = 0; ks < kDsKC / 16; ++ks) {
       f16x8_t af[TM], bf[TN];
@@ -976,7 +976,10 @@ __global__ __launch_bounds__(256) void attention_ds_gemm_kernel(DsGemmArgs p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (kc + 1 < nkc) store((kc + 1) & 1);
+    if (kc + 1 < nkc) {
+      __syncthreads();
+      store(0);
+    }
     __syncthreads();
   }
 
