@@ -13,8 +13,8 @@
 // query, the output rescaled as the max grows).  The wave computes S^T =
 // K Q^T with FP16 MFMA 32x32x16: its Q block is expanded to FP16 once
 // (E2M1 code x E4M3 block scale is exact in FP16: <= 6 significant bits)
-// and stays in registers; each key block's codes sit in LDS and every wave
-// expands the K fragments it multiplies.  In the S^T accumulator layout a
+// and stays in registers; each key block is expanded to FP16 once per
+// workgroup as it is staged in LDS, and the waves read its fragments.  In the S^T accumulator layout a
 // lane holds 16 keys of one query, so the softmax reductions are in-lane
 // plus one exchange with the lane 32 apart.  Those registers, rounded to
 // BF16, are directly the B operand of O^T = V^T P^T (BF16 MFMA 32x32x16):
@@ -79,17 +79,17 @@ __device__ inline f16x8_t expand8(uint32_t codes8, const ScalePair &s) {
 
 template <int D>
 struct AttnLds {
-  static constexpr int kKc = D / 2 + 8;           // K code row stride (bytes): 8-byte aligned, spreads banks
-  static constexpr int kKs = D / 16;              // K scale row stride
+  static constexpr int kKh = D + 8;               // FP16 per row of the expanded K block
   static constexpr int kVt = kBK * 2 + 8;         // V^T row stride (bytes), 64 keys of BF16 + pad
-  static constexpr int kKcBytes = kBK * kKc, kKsBytes = kBK * kKs, kVtBytes = D * kVt;
-  static constexpr int kStage = kKcBytes + kKsBytes + kVtBytes;
-  // per-lane staging registers: K codes, K scales, V^T (16-byte words)
-  static constexpr int kKcWords = kBK * (D / 2) / 16;    // 256 for D = 128
+  static constexpr int kKhBytes = kBK * kKh * 2, kVtBytes = D * kVt;
+  static constexpr int kStage = kKhBytes + kVtBytes;
+  // staging: each thread expands kEpt K elements (a quarter row) and moves
+  // kVtPer 16-byte words of V^T
+  static constexpr int kEpt = kBK * D / kAttnThreads;    // 32 for D = 128, 16 for D = 64
   static constexpr int kVtWords = D * kBK * 2 / 16;      // 1024 for D = 128
-  static constexpr int kKcPer = (kKcWords + kAttnThreads - 1) / kAttnThreads;
   static constexpr int kVtPer = kVtWords / kAttnThreads;
   static_assert(kVtWords % kAttnThreads == 0, "V^T staging");
+  static_assert(D / kEpt == 4 && kEpt % 16 == 0, "K staging: four threads per key, whole scale blocks");
 };
 
 template <int D>
@@ -134,24 +134,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
   const int64_t nkb = a.causal ? ((q0 + kBQ < S ? q0 + kBQ : S) + kBK - 1) / kBK : nkb_all;
 
   // ---- key-block staging: global -> registers -> LDS ------------------------
-  uint4 rk[L::kKcPer], rv[L::kVtPer];
-  uint2 rs = make_uint2(0, 0);
+  // K is expanded to FP16 once per workgroup as it is stored, and every wave
+  // reads its fragments from LDS
+  uint4 rk = make_uint4(0, 0, 0, 0), rv[L::kVtPer];
+  uint32_t rks = 0;
+  const int krow_s = tid / 4, kc0 = (tid % 4) * L::kEpt;   // the K elements this thread expands
   auto load_block = [&](int64_t kb) {
     const int64_t k0 = kb * kBK;
-#pragma unroll
-    for (int i = 0; i < L::kKcPer; ++i) {
-      const int idx = tid + i * kAttnThreads;
-      const int row = idx / (D / 32), ch = idx % (D / 32);
-      int64_t key = k0 + row;
+    {
+      int64_t key = k0 + krow_s;
       key = key < S ? key : S - 1;
-      rk[i] = idx < L::kKcWords ? *(const uint4 *)(a.k_codes + (g * S + key) * (D / 2) + ch * 16)
-                                : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < kBK) {
-      int64_t key = k0 + tid;
-      key = key < S ? key : S - 1;
-      if constexpr (D == 128) rs = *(const uint2 *)(a.k_scales + (g * S + key) * 8);
-      else rs = make_uint2(*(const uint32_t *)(a.k_scales + (g * S + key) * 4), 0u);
+      const uint8_t *cp = a.k_codes + (g * S + key) * (D / 2) + kc0 / 2;
+      const uint8_t *sp = a.k_scales + (g * S + key) * (D / 16) + kc0 / 16;
+      if constexpr (L::kEpt == 32) {
+        rk = *(const uint4 *)cp;
+        rks = *(const uint16_t *)sp;
+      } else {
+        const uint2 t = *(const uint2 *)cp;
+        rk = make_uint4(t.x, t.y, 0u, 0u);
+        rks = *sp;
+      }
     }
 #pragma unroll
     for (int i = 0; i < L::kVtPer; ++i) {
@@ -163,21 +165,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
   };
   auto store_block = [&](int st) {
     uint8_t *base = lds + st * L::kStage;
-    uint8_t *kc = base, *ks = base + L::kKcBytes, *vt = ks + L::kKsBytes;
+    _Float16 *kh = (_Float16 *)base + krow_s * L::kKh + kc0;
+    uint8_t *vt = base + L::kKhBytes;
+    const uint32_t cw[4] = {rk.x, rk.y, rk.z, rk.w};
 #pragma unroll
-    for (int i = 0; i < L::kKcPer; ++i) {
-      const int idx = tid + i * kAttnThreads;
-      if (idx < L::kKcWords) {
-        const int row = idx / (D / 32), ch = idx % (D / 32);
-        uint2 *p = (uint2 *)(kc + row * L::kKc + ch * 16);
-        p[0] = make_uint2(rk[i].x, rk[i].y);
-        p[1] = make_uint2(rk[i].z, rk[i].w);
-      }
-    }
-    if (tid < kBK) {
-      if constexpr (D == 128) *(uint2 *)(ks + tid * 8) = rs;
-      else *(uint32_t *)(ks + tid * 4) = rs.x;
-    }
+    for (int j = 0; j < L::kEpt / 8; ++j)
+      *(f16x8_t *)(kh + 8 * j) = expand8(cw[j], split_scale((rks >> (8 * (j / 2))) & 0xFFu));
 #pragma unroll
     for (int i = 0; i < L::kVtPer; ++i) {
       const int idx = tid + i * kAttnThreads;
@@ -199,7 +192,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
     const bool live = !a.causal || k0 <= qw0 + 31;
     if (live) {
       const uint8_t *base = lds + (int)(kb & 1) * L::kStage;
-      const uint8_t *kc = base, *ks = base + L::kKcBytes, *vt = ks + L::kKsBytes;
+      const _Float16 *kh = (const _Float16 *)base;
+      const uint8_t *vt = base + L::kKhBytes;
       // ---- S^T = K Q^T: two 32-key tiles ------------------------------------
       floatx16_t st[2];
 #pragma unroll
@@ -208,11 +202,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
         for (int e = 0; e < 16; ++e) st[kt][e] = 0.0f;
         const int krow = kt * 32 + l32;
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-          const uint32_t c8 = *(const uint32_t *)(kc + krow * L::kKc + 8 * t + 4 * h);
-          const f16x8_t kf = expand8(c8, split_scale(ks[krow * L::kKs + t]));
-          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[t], st[kt], 0, 0, 0);
-        }
+        for (int t = 0; t < KSTEPS; ++t)
+          st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8_t *)(kh + krow * L::kKh + 16 * t + 8 * h),
+                                                           qf[t], st[kt], 0, 0, 0);
       }
       // ---- online softmax in log2 units ------------------------------------
       // register e of tile kt holds key k0 + 32 kt + 8 (e/4) + 4 h + e%4
