@@ -82,7 +82,8 @@ BwdWs carve_bwd(void *ws, int64_t M, int64_t N, int64_t K, int r, size_t *total)
   size_t pb = 0;
   for (size_t b : {small_gemm_partials_bytes(M, rr, N), small_gemm_partials_bytes(N, rr, M),
                    small_gemm_partials_bytes(rr, K, M), rowred_partials_bytes(M, rr, N),
-                   colred_partials_bytes(M, N, rr), colred_partials_bytes(M, K, rr)})
+                   colred_partials_bytes(M, N, rr), colred_partials_bytes(M, K, rr),
+                   dualred_partials_bytes(M, N, rr)})
     pb = b > pb ? b : pb;
   w.partials = (float *)c.take(pb);
   if (total) *total = c.off;
@@ -403,15 +404,22 @@ fs4_status fs4_linear_bwd(const void *dY, int64_t M, int64_t N, int64_t K, const
   hipStream_t s = as_stream(stream);
   BwdWs w = carve_bwd(ws, M, N, K, r, nullptr);
   LowRankEpilogue lr;
+  // dU comes out of the same read of dY as P when r <= 32
+  const bool dual = r > 0 && r <= 32 && dU && M * N < ((int64_t)1 << 30) && M * r < ((int64_t)1 << 30);
   if (r > 0) {
     // P[m][j] = sum_n dY[m][n] U[n][j] (U transposed once so both operands
     // run along n); this pass reads all of dY, so it also yields dY's amax
-    // partials for the quantizer when they fit
+    // partials for the quantizer when they fit.  With dual, the same pass
+    // forms dU[n][j] = beta sum_m dY[m][n] T[m][j].
     FS4_TRY(launch_transpose_rank((const uint16_t *)U, N, r, w.Ut, s));
-    const int64_t nwg = rowred_workgroups(M, N);
+    const int64_t nwg = dual ? dualred_workgroups(M, N) : rowred_workgroups(M, N);
     const bool fuse = nwg <= kAmaxPartials;
-    FS4_TRY(launch_rowred((const uint16_t *)dY, w.Ut, M, r, N, 1.0f, w.P, w.partials,
-                          fuse ? w.qws : nullptr, s));
+    if (dual)
+      FS4_TRY(launch_dualred((const uint16_t *)dY, w.Ut, T, M, N, r, 1.0f, w.P, beta, dU,
+                             w.partials, w.bt, fuse ? w.qws : nullptr, s));
+    else
+      FS4_TRY(launch_rowred((const uint16_t *)dY, w.Ut, M, r, N, 1.0f, w.P, w.partials,
+                            fuse ? w.qws : nullptr, s));
     if (fuse)
       FS4_TRY(launch_quantize_encode(dY, FS4_BF16, M, N, &w.dy_row, &w.dy_col, w.qws, (int)nwg, s));
     else
@@ -428,7 +436,7 @@ fs4_status fs4_linear_bwd(const void *dY, int64_t M, int64_t N, int64_t K, const
   FS4_TRY(launch_gemm_nt(w.dy_row, *R_col, 1.0f, nullptr, 0.0f, dX, lr, s));
   FS4_TRY(launch_gemm_nt(w.dy_col, *X_col, 1.0f, nullptr, 0.0f, dW, LowRankEpilogue(), s));
   // column contractions over the M tokens
-  if (r > 0 && dU) {
+  if (r > 0 && dU && !dual) {
     // dU[n][j] = beta sum_m dY[m][n] T[m][j]
     FS4_TRY(launch_colred((const uint16_t *)dY, T, M, N, r, beta, dU, false, w.partials, w.bt, s));
   }

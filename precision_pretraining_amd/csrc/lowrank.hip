@@ -14,6 +14,8 @@
 // keep ~16 significant bits.  The k range is split over the 4 waves of a
 // workgroup and over gridDim.y; partial sums go to a workspace and a second
 // pass adds them in a fixed order (deterministic).
+#include <type_traits>
+
 #include "fs4_common.h"
 
 namespace fs4 {
@@ -21,6 +23,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 struct SmallGemm {
   const void *P;
@@ -476,6 +479,174 @@ __global__ void transpose_rank_kernel(const uint16_t *__restrict__ U, int64_t N,
   Ut[i] = U[n * r + j];
 }
 
+// dualred: both rank-r contractions of one bf16 matrix A [M][N] in a single
+// read of it (r <= 32):
+//   P[m][j]  = sum_n A[m][n] B[j][n]          (along the rows of A)
+//   Q[n][j]  = sum_m A[m][n] Bm[m][j]         (down its columns)
+// with B bf16 [r][N] and Bm fp32 [M][r], given as its transposed BF16 hi/lo
+// split (bt_hi, bt_lo [r][M]).  In the LoRA-SVD backward A = dY, B = U^T and
+// Bm = T: P = dY U feeds the dX epilogue and Q = dY^T T is dU.
+// A workgroup owns a 512 x 512 block of A, walked in 64-row slabs staged in
+// LDS (the next slab's loads in flight), with its 512 columns of B staged
+// once.  Per slab, waves 0 and 1 form the slab's two 32-row tiles of P over
+// the block's columns and store them to partial slot "column block"; every
+// wave adds the slab into the Q rows of its 64 columns, kept in registers
+// over the block's 512 rows and stored to partial slot "row block" at the
+// end.  Two reductions then add the slots in order (deterministic).  With
+// amax_parts, each workgroup also writes the largest |A| of its block (fp32
+// bits).
+constexpr int kDrCols = 512, kDrRows = 512, kDrSlab = 64;
+constexpr int kDrStride = kDrCols + 8;     // 1040-byte LDS rows
+constexpr int kDrThreads = 512;
+constexpr int kRawBufferWord3 = 0x00020000;   // buffer resource word 3: 32-bit untyped access
+
+__global__ __launch_bounds__(kDrThreads) void dualred_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    const uint16_t *__restrict__ bt_hi, const uint16_t *__restrict__ bt_lo, int64_t M, int64_t N,
+    int r, float *__restrict__ ppart, float *__restrict__ qpart, uint32_t *__restrict__ amax_parts) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kDrSlab][kDrStride];      // A slab [m][n]
+  __shared__ __attribute__((aligned(16))) uint16_t sb[32][kDrStride];           // B [j][n]
+  __shared__ __attribute__((aligned(16))) uint16_t sh[32][kDrSlab + 8];         // Bm^T hi [j][m]
+  __shared__ __attribute__((aligned(16))) uint16_t sl[32][kDrSlab + 8];         // Bm^T lo [j][m]
+  __shared__ uint32_t smax;
+  if (threadIdx.x == 0) smax = 0;   // (published by the first slab's barrier)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t n0 = (int64_t)blockIdx.x * kDrCols, mb0 = (int64_t)blockIdx.y * kDrRows;
+  const int64_t mlim = mb0 + kDrRows < M ? mb0 + kDrRows : M;
+
+  // B's 32 x 512 block, once (64 threads per row)
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int idx = tid + p * kDrThreads, j = idx >> 6, seg = idx & 63;
+    const int64_t n = n0 + seg * 8;
+    const uint4 v = (j < r && n < N) ? *(const uint4 *)(B + (int64_t)j * N + n) : make_uint4(0, 0, 0, 0);
+    *(uint4 *)&sb[j][seg * 8] = v;
+  }
+  // Slab loads: A 64 x 512 (8 words per thread; word p of a thread is slab
+  // row wave + 8p at column n0 + 8 lane, so a wave reads 1 KB of one row);
+  // Bm^T hi (waves 0-3) or lo (waves 4-7) 32 x 64.  The next slab's loads are
+  // in flight while a slab is multiplied (a second slab in flight measured no
+  // faster).  Raw buffer loads take the row's byte offset in a scalar
+  // register and the column's in a vector one (the launcher keeps M N and M r
+  // below 2^30).  Columns past N load the last 8 columns and Bm^T rows past r
+  // or M its last row or columns; these are zeroed by a mask where they are
+  // stored to LDS (a select right behind the load, or one in a branch, makes
+  // the compiler wait for the load there).
+  uint4 ga[8], gt;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool col_ok = n0 + lane * 8 < N;
+  const int col_off = (int)((col_ok ? n0 + lane * 8 : N - 8) * 2);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, (int)(M * N * 2), kRawBufferWord3);
+  const int tj = (tid & 255) >> 3, tseg = tid & 7;
+  const __amdgpu_buffer_rsrc_t rt_ = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(wave_u < 4 ? bt_hi : bt_lo), 0, (int)(M * r * 2), kRawBufferWord3);
+  const int t_row = (tj < r ? tj : r - 1) * (int)M;
+  auto gload = [&](int64_t m0) {
+    const int64_t tm = m0 + tseg * 8;
+    const int t_off = (t_row + (int)(tm < M ? tm : M - 8)) * 2;
+    gt = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rt_, t_off, 0, 0));
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int64_t m = m0 + wave_u + 8 * p;
+      const int roff = (int)((m < mlim ? m : mlim - 1) * N * 2);
+      ga[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, col_off, roff, 0));
+    }
+  };
+
+  floatx16_t accq[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) accq[c][e] = 0.0f;
+  gload(mb0);
+  for (int64_t m0 = mb0; m0 < mlim; m0 += kDrSlab) {
+    __syncthreads();          // the previous slab is fully read
+    u16x2_t am2 = {0, 0};     // max bf16 magnitude bits, two lanes of 16
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t keep = (col_ok && m0 + wave_u + 8 * p < mlim) ? 0xFFFFFFFFu : 0u;
+      const uint4 v = make_uint4(ga[p].x & keep, ga[p].y & keep, ga[p].z & keep, ga[p].w & keep);
+      *(uint4 *)&sa[wave + 8 * p][lane * 8] = v;
+      am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu));
+      am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu));
+      am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu));
+      am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu));
+    }
+    if (amax_parts) {
+      // the slab's max |A| per wave, folded into the block's in LDS (a value
+      // carried in registers across the slabs costs the loop its registers)
+      uint32_t mv = am2[0] > am2[1] ? am2[0] : am2[1];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = __shfl_xor(mv, off, 64);
+        mv = mv > o ? mv : o;
+      }
+      if (lane == 0) atomicMax(&smax, mv);
+    }
+    {
+      const uint32_t keep = (tj < r && m0 + tseg * 8 < mlim) ? 0xFFFFFFFFu : 0u;
+      *(uint4 *)&(wave_u < 4 ? sh : sl)[tj][tseg * 8] =
+          make_uint4(gt.x & keep, gt.y & keep, gt.z & keep, gt.w & keep);
+    }
+    __syncthreads();
+    if (m0 + kDrSlab < mlim) gload(m0 + kDrSlab);
+    if (wave < 2) {
+      // P: waves 0 and 1 take one 32-row tile each, over all 512 columns (no
+      // sum across waves), and store it to the partial slot
+      floatx16_t accp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) accp[e] = 0.0f;
+#pragma unroll
+      for (int st = 0; st < kDrCols / 16; ++st) {
+        const int kk = st * 16 + 8 * h;
+        accp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)&sa[wave * 32 + l32][kk],
+                                                       *(const bf16x8_t *)&sb[l32][kk], accp, 0, 0, 0);
+      }
+      float *out = ppart + (int64_t)blockIdx.x * M * r;
+      const int j = l32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t rw = m0 + wave * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (rw < mlim && j < r) out[rw * r + j] = accp[e];
+      }
+    }
+    // Q: the slab's rows into this wave's 64 columns (A fragments read down
+    // the LDS columns)
+#pragma unroll
+    for (int st = 0; st < kDrSlab / 16; ++st) {
+      const int mm = st * 16 + 8 * h;
+      const bf16x8_t fh = *(const bf16x8_t *)&sh[l32][mm], fl = *(const bf16x8_t *)&sl[l32][mm];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int col = wave * 64 + c * 32 + l32;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = (uint32_t)sa[mm + 2 * q][col] | ((uint32_t)sa[mm + 2 * q + 1][col] << 16);
+        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        accq[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fh, accq[c], 0, 0, 0);
+        accq[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fl, accq[c], 0, 0, 0);
+      }
+    }
+  }
+  {
+    float *out = qpart + (int64_t)blockIdx.y * N * r;
+    const int j = l32;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t col = n0 + wave * 64 + c * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (col < N && j < r) out[col * r + j] = accq[c][e];
+      }
+  }
+  if (amax_parts) {
+    __syncthreads();
+    if (tid == 0) amax_parts[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = smax << 16;   // -> fp32 bits
+  }
+}
+
 int64_t rowred_splits(int64_t Na, int64_t K, int64_t *kchunk) {
   const int64_t blocks = (Na + kRrRows - 1) / kRrRows;
   // >= 1024 workgroups when K allows, chunks of whole 128-k slabs
@@ -572,6 +743,32 @@ fs4_status launch_colred(const uint16_t *A, const float *Bm, int64_t M, int64_t 
   const int64_t n = C * r;
   reduce_partials_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(partials, (int)S, C, r, scale,
                                                                       out, transpose_out);
+  return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
+}
+size_t dualred_partials_bytes(int64_t M, int64_t N, int r) {
+  const int64_t cb = (N + kDrCols - 1) / kDrCols, rb = (M + kDrRows - 1) / kDrRows;
+  return (size_t)((cb * M + rb * N) * r) * sizeof(float);
+}
+int64_t dualred_workgroups(int64_t M, int64_t N) {
+  return ((N + kDrCols - 1) / kDrCols) * ((M + kDrRows - 1) / kDrRows);
+}
+fs4_status launch_dualred(const uint16_t *A, const uint16_t *B, const float *Bm, int64_t M,
+                          int64_t N, int r, float p_scale, float *P, float q_scale, float *Q,
+                          float *partials, uint16_t *bt, uint32_t *amax_parts, hipStream_t s) {
+  if (M == 0 || N == 0 || r == 0) return FS4_OK;
+  if (r > 32) return FS4_ERR_RANK;
+  if (M * N >= ((int64_t)1 << 30) || M * r >= ((int64_t)1 << 30)) return FS4_ERR_SHAPE;   // 32-bit buffer offsets
+  uint16_t *bt_hi = bt, *bt_lo = bt + M * r;
+  const int64_t nb = M * r;
+  split_transpose_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, s>>>(Bm, M, r, bt_hi, bt_lo);
+  const int64_t cb = (N + kDrCols - 1) / kDrCols, rb = (M + kDrRows - 1) / kDrRows;
+  float *ppart = partials, *qpart = partials + cb * M * r;
+  dualred_kernel<<<dim3((unsigned)cb, (unsigned)rb), kDrThreads, 0, s>>>(A, B, bt_hi, bt_lo, M, N, r,
+                                                                       ppart, qpart, amax_parts);
+  reduce_partials_kernel<<<(unsigned)((M * r + 255) / 256), 256, 0, s>>>(ppart, (int)cb, M, r,
+                                                                          p_scale, P, false);
+  reduce_partials_kernel<<<(unsigned)((N * r + 255) / 256), 256, 0, s>>>(qpart, (int)rb, N, r,
+                                                                          q_scale, Q, false);
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 fs4_status launch_transpose_rank(const uint16_t *U, int64_t N, int r, uint16_t *Ut, hipStream_t s) {

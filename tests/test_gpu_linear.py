@@ -113,7 +113,11 @@ def test_tiny_linear_fwd_bwd():
 
 @pytest.mark.parametrize("M,K,N,r,beta", [(80, 272, 208, 5, 1.0), (64, 128, 96, 0, 1.0),
                                           (48, 64, 64, 64, 0.5), (272, 512, 400, 32, 1.0),
-                                          (16, 16, 16, 1, 2.0)])
+                                          (16, 16, 16, 1, 2.0),
+                                          # several 512 x 512 blocks of dY with ragged edges
+                                          # (P and dU from one read of dY), and r = 33 past it
+                                          (1040, 128, 1552, 32, 0.75), (1552, 64, 528, 7, 1.0),
+                                          (528, 96, 1040, 33, 1.0)])
 def test_linear_ragged_shapes_and_ranks(M, K, N, r, beta):
     print_case(test="linear_ragged", M=M, K=K, N=N, r=r, beta=beta)
     rng = np.random.default_rng(M * 31 + K + N + r)
