@@ -329,7 +329,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   struct Stage { const uint8_t *a, *b, *sa, *sb; };
   uint32_t sa4[TM], sb4[TN];      // the four scale bytes of each row's blocks in this lane half
   uint2 clo_a[TM], clo_b[TN], chi_a[TM], chi_b[TN];
-  ScalePair sa[TM], sb[TN];
+  ScalePair sa[2][TM], sb[2][TN];   // the scales of the blocks in use, by block parity
   f16x8_t av[TM], bv[TN];         // operands of the current k-step
   // half q (0: words 0-1, 1: words 2-3) of code pair p of row r
   auto codes_at = [&](const uint8_t *base, int r, int p, int q) -> uint2 {
@@ -345,17 +345,17 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
   };
   auto read_scales = [&](int blk) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = lut_scale(scale_lut, (sa4[i] >> (8 * blk)) & 0xFFu);
+    for (int i = 0; i < TM; ++i) sa[blk & 1][i] = lut_scale(scale_lut, (sa4[i] >> (8 * blk)) & 0xFFu);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sb[j] = lut_scale(scale_lut, (sb4[j] >> (8 * blk)) & 0xFFu);
+    for (int j = 0; j < TN; ++j) sb[blk & 1][j] = lut_scale(scale_lut, (sb4[j] >> (8 * blk)) & 0xFFu);
   };
   auto expand_step = [&](int s, f16x8_t *ao, f16x8_t *bo) {
     const int w = s & 3;
     const uint2 *wa = w < 2 ? clo_a : chi_a, *wb = w < 2 ? clo_b : chi_b;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ao[i] = expand8((w & 1) ? wa[i].y : wa[i].x, sa[i]);
+    for (int i = 0; i < TM; ++i) ao[i] = expand8((w & 1) ? wa[i].y : wa[i].x, sa[(s >> 1) & 1][i]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bo[j] = expand8((w & 1) ? wb[j].y : wb[j].x, sb[j]);
+    for (int j = 0; j < TN; ++j) bo[j] = expand8((w & 1) ? wb[j].y : wb[j].x, sb[(s >> 1) & 1][j]);
   };
   auto read_scale_bytes = [&](const Stage &t) {
 #pragma unroll
@@ -373,13 +373,16 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
     read_scales(0);
     expand_step(0, av, bv);
   };
-  // The 8 k-steps of stage t (whose step 0 is already in av/bv and whose
-  // pair-0 codes are in clo/chi).  Reads: pair 1 lo in step 1, pair 1 hi in
-  // step 3.  With CROSS, stage nt's scale bytes (step 6) and pair 0 (lo in
-  // step 5, hi in step 7) are read too, and the last step expands nt's
-  // step 0, so no k-step runs without expansion work beside its MFMAs.
-  // mid() runs after step 3, once this wave has issued its last read of t;
-  // the reads of nt come after it.
+  // The 8 k-steps of stage t (whose step 0 is already in av/bv, whose
+  // pair-0 codes are in clo/chi and whose block-0 scales are in set 0).
+  // Reads: pair 1 lo in step 1, pair 1 hi in step 3; the scales of block b
+  // (b = 1, 2, 3) in step 2b - 2, one step before the step that expands with
+  // them first, so that their LDS latency passes under that step's MFMAs.
+  // With CROSS, stage nt's scale bytes (step 5), its block-0 scales (step 6)
+  // and its pair 0 (lo in step 5, hi in step 7) are read too, and the last
+  // step expands nt's step 0, so no k-step runs without expansion work beside
+  // its MFMAs.  mid() runs after step 3, once this wave has issued its last
+  // read of t; the reads of nt come after it.
   auto run_tile = [&](const Stage &t, const Stage &nt, auto cross, auto mid) {
     constexpr bool CROSS = decltype(cross)::value;
     static_for<0, 8>([&](auto step) {
@@ -388,17 +391,15 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
       f16x8_t an[TM], bn[TN];
       if constexpr (s == 1) read_codes(t, 1, 0);
       if constexpr (s == 3) read_codes(t, 1, 1);
-      if constexpr (CROSS && s == 5) read_codes(nt, 0, 0);
-      if constexpr (CROSS && s == 6) read_scale_bytes(nt);   // this stage's were last decoded in step 5
-      if constexpr (CROSS && s == 7) read_codes(nt, 0, 1);
-      if constexpr (s + 1 < 8) {
-        constexpr int u = s + 1;
-        if constexpr ((u & 1) == 0) read_scales(u >> 1);
-        expand_step(u, an, bn);
-      } else if constexpr (CROSS) {
-        read_scales(0);
-        expand_step(0, an, bn);
+      if constexpr (s == 0 || s == 2 || s == 4) read_scales(s / 2 + 1);
+      if constexpr (CROSS && s == 5) {
+        read_codes(nt, 0, 0);
+        read_scale_bytes(nt);   // this stage's were last decoded in step 4
       }
+      if constexpr (CROSS && s == 6) read_scales(0);
+      if constexpr (CROSS && s == 7) read_codes(nt, 0, 1);
+      if constexpr (s + 1 < 8) expand_step(s + 1, an, bn);
+      else if constexpr (CROSS) expand_step(0, an, bn);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
