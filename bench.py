@@ -167,6 +167,12 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
+    def hold_queue():
+        # a ~10 ms spin on the stream ahead of a timed run of short calls, so
+        # that the host enqueues them while the device is busy and the events
+        # time device work, not the binding's per-call host time
+        torch.cuda._sleep(20_000_000)
+
     def to_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
@@ -229,6 +235,7 @@ def main():
             fs4.quantize(c, out_row=qrow, out_col=qcol)
         torch.cuda.synchronize()
         qe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(qreps)]
+        hold_queue()
         for j in range(qreps):
             qe[j][0].record(stream)
             fs4.quantize(copies[j % len(copies)], out_row=qrow, out_col=qcol)
@@ -236,6 +243,7 @@ def main():
         torch.cuda.synchronize()
         q_ms = float(np.mean([s.elapsed_time(e) for s, e in qe]))
         q_gbs = quantizer_bytes(rows_q, cols_q) / (q_ms * 1e-3) / 1e9
+        hold_queue()
         for j in range(qreps):
             qe[j][0].record(stream)
             fs4.quantize(copies[j % len(copies)], colwise=False, out_row=qrow)
@@ -406,6 +414,7 @@ def main():
     def time_calls(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        hold_queue()
         e0.record(stream)
         for _ in range(n):
             fn()
