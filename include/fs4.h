@@ -374,9 +374,10 @@ const char *fs4_version(void);
  *                 column-wise views serve the backward's dS products)
  *   V        bf16 [G][S][D]
  *   O        fp32 [G][S][D];  LSE fp32 [G][S], nullable
- *   Vt_save  bf16 [G][D][S], nullable: receives V^T, the layout the P V
- *            product reads; without it V^T goes to the workspace
- *            (fs4_attention_fwd_workspace_bytes)
+ *   Vt_save  bf16 [G][D][S], nullable: receives V^T as a side output (the
+ *            kernel transposes each V block itself as it stages it)
+ *   ws       no workspace is needed (fs4_attention_fwd_workspace_bytes is 0;
+ *            ws may be null)
  *   D = 64 or 128; S a positive multiple of 16; G >= 1, G*S < 2^31.
  * Errors: FS4_ERR_SHAPE, FS4_ERR_NULL, FS4_ERR_ALIGN, FS4_ERR_WORKSPACE.
  */

@@ -592,7 +592,7 @@ def newton_schulz_plan(m: int, n: int) -> dict:
 class AttentionFwd:
     O: torch.Tensor
     LSE: torch.Tensor
-    Vt: torch.Tensor
+    Vt: Optional[torch.Tensor]
 
 
 def attention_quantize(x: torch.Tensor):
@@ -605,10 +605,11 @@ def attention_quantize(x: torch.Tensor):
     return quantize(x.reshape(G * S, D))
 
 
-def attention_fwd(Q_row: NVFP4, K_row: NVFP4, V: torch.Tensor, causal: bool = True) -> AttentionFwd:
+def attention_fwd(Q_row: NVFP4, K_row: NVFP4, V: torch.Tensor, causal: bool = True,
+                  keep_vt: bool = False) -> AttentionFwd:
     """O = softmax(Q K^T / sqrt(D)) V with Q K^T on the NVFP4 views and P V
     in BF16.  V bf16 [G, S, D]; returns O fp32 [G, S, D], LSE fp32 [G, S]
-    and V^T bf16 [G, D, S]."""
+    and, with keep_vt, V^T bf16 [G, D, S] as a side output."""
     if not isinstance(V, torch.Tensor) or V.dim() != 3:
         raise ValueError("V must be a [G, S, D] tensor")
     G, S, D = (int(v) for v in V.shape)
@@ -618,10 +619,10 @@ def attention_fwd(Q_row: NVFP4, K_row: NVFP4, V: torch.Tensor, causal: bool = Tr
     _view(K_row, "K_row", G * S, D, dev)
     O = torch.empty((G, S, D), dtype=torch.float32, device=dev)
     LSE = torch.empty((G, S), dtype=torch.float32, device=dev)
-    Vt = torch.empty((G, D, S), dtype=torch.bfloat16, device=dev)
+    Vt = torch.empty((G, D, S), dtype=torch.bfloat16, device=dev) if keep_vt else None
     qv, kv = Q_row.c(), K_row.c()
     _check(_lib.fs4_attention_fwd(ctypes.byref(qv), ctypes.byref(kv), V.data_ptr(), G, S, D, int(causal), O.data_ptr(),
-                                  LSE.data_ptr(), Vt.data_ptr(), None, 0, _stream(dev)), "fs4_attention_fwd")
+                                  LSE.data_ptr(), _ptr(Vt), None, 0, _stream(dev)), "fs4_attention_fwd")
     return AttentionFwd(O, LSE, Vt)
 
 

@@ -622,11 +622,9 @@ fs4_status fs4_attention_fwd(const fs4_nvfp4 *Q_row, const fs4_nvfp4 *K_row, con
   FS4_TRY(check_ptr(O));
   if (LSE && ((uintptr_t)LSE & 3u)) return FS4_ERR_ALIGN;
   if (Vt_save) FS4_TRY(check_ptr(Vt_save));
-  const size_t need = Vt_save ? 0 : attention_fwd_ws_bytes(G, S, D);
-  FS4_TRY(check_ws(ws, ws_bytes, need));
-  uint16_t *vt = Vt_save ? (uint16_t *)Vt_save : (uint16_t *)ws;
-  return launch_attention_fwd(*Q_row, *K_row, (const uint16_t *)V, G, S, D, causal != 0, O, LSE, vt,
-                              as_stream(stream));
+  FS4_TRY(check_ws(ws, ws_bytes, attention_fwd_ws_bytes(G, S, D)));
+  return launch_attention_fwd(*Q_row, *K_row, (const uint16_t *)V, G, S, D, causal != 0, O, LSE,
+                              (uint16_t *)Vt_save, as_stream(stream));
 }
 
 size_t fs4_attention_bwd_workspace_bytes(int64_t G, int64_t S, int64_t D) {

@@ -40,7 +40,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct AttnArgs {
   const uint8_t *q_codes, *q_scales, *k_codes, *k_scales;
   const float *q_ts, *k_ts;
-  const uint16_t *vt;   // bf16 [G][D][S]
+  const uint16_t *v;    // bf16 [G][S][D]
   float *o;             // fp32 [G][S][D]
   float *lse;           // fp32 [G][S], nullable
   int64_t G, S;
@@ -83,12 +83,11 @@ struct AttnLds {
   static constexpr int kVt = kBK * 2 + 8;         // V^T row stride (bytes), 64 keys of BF16 + pad
   static constexpr int kKhBytes = kBK * kKh * 2, kVtBytes = D * kVt;
   static constexpr int kStage = kKhBytes + kVtBytes;
-  // staging: each thread expands kEpt K elements (a quarter row) and moves
-  // kVtPer 16-byte words of V^T
+  // staging: each thread expands kEpt K elements (a quarter row) and
+  // transposes kVPairs pairs of V words (8 dims of two consecutive keys)
   static constexpr int kEpt = kBK * D / kAttnThreads;    // 32 for D = 128, 16 for D = 64
-  static constexpr int kVtWords = D * kBK * 2 / 16;      // 1024 for D = 128
-  static constexpr int kVtPer = kVtWords / kAttnThreads;
-  static_assert(kVtWords % kAttnThreads == 0, "V^T staging");
+  static constexpr int kVPairs = (kBK / 2) * (D / 8) / kAttnThreads;   // 2 for D = 128, 1 for D = 64
+  static_assert((kBK / 2) * (D / 8) % kAttnThreads == 0, "V staging");
   static_assert(D / kEpt == 4 && kEpt % 16 == 0, "K staging: four threads per key, whole scale blocks");
 };
 
@@ -136,7 +135,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
   // ---- key-block staging: global -> registers -> LDS ------------------------
   // K is expanded to FP16 once per workgroup as it is stored, and every wave
   // reads its fragments from LDS
-  uint4 rk = make_uint4(0, 0, 0, 0), rv[L::kVtPer];
+  uint4 rk = make_uint4(0, 0, 0, 0), rv[2 * L::kVPairs];
   uint32_t rks = 0;
   const int krow_s = tid / 4, kc0 = (tid % 4) * L::kEpt;   // the K elements this thread expands
   auto load_block = [&](int64_t kb) {
@@ -155,15 +154,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
         rks = *sp;
       }
     }
+    // V as it sits in memory: word (key, dims 8 dg .. 8 dg + 7); a thread
+    // takes keys 2 kp and 2 kp + 1 of one dim group, so that it can write
+    // both keys of a dim as one 32-bit word of the transposed LDS rows
 #pragma unroll
-    for (int i = 0; i < L::kVtPer; ++i) {
-      const int idx = tid + i * kAttnThreads;
-      const int d = idx / (kBK / 8), ch = idx % (kBK / 8);     // 8 keys per 16-byte word
-      const int64_t key = k0 + ch * 8;
-      rv[i] = key < S ? *(const uint4 *)(a.vt + (g * D + d) * S + key) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < L::kVPairs; ++j) {
+      const int idx = tid + j * kAttnThreads;
+      const int kp = idx % (kBK / 2), dg = idx / (kBK / 2);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        // (keys past S load the last key and are zeroed where they are
+        // stored, not behind the load)
+        int64_t key = k0 + 2 * kp + b;
+        key = key < S ? key : S - 1;
+        rv[2 * j + b] = *(const uint4 *)(a.v + (g * S + key) * D + dg * 8);
+      }
     }
   };
-  auto store_block = [&](int st) {
+  auto store_block = [&](int st, int64_t k0) {
     uint8_t *base = lds + st * L::kStage;
     _Float16 *kh = (_Float16 *)base + krow_s * L::kKh + kc0;
     uint8_t *vt = base + L::kKhBytes;
@@ -171,18 +179,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
 #pragma unroll
     for (int j = 0; j < L::kEpt / 8; ++j)
       *(f16x8_t *)(kh + 8 * j) = expand8(cw[j], split_scale((rks >> (8 * (j / 2))) & 0xFFu));
+    // V^T rows [d][keys]: dims 2q, 2q + 1 of each word pair become two 32-bit
+    // words (key 2 kp in the low half, 2 kp + 1 in the high half)
 #pragma unroll
-    for (int i = 0; i < L::kVtPer; ++i) {
-      const int idx = tid + i * kAttnThreads;
-      const int d = idx / (kBK / 8), ch = idx % (kBK / 8);
-      uint2 *p = (uint2 *)(vt + d * L::kVt + ch * 16);
-      p[0] = make_uint2(rv[i].x, rv[i].y);
-      p[1] = make_uint2(rv[i].z, rv[i].w);
+    for (int j = 0; j < L::kVPairs; ++j) {
+      const int idx = tid + j * kAttnThreads;
+      const int kp = idx % (kBK / 2), dg = idx / (kBK / 2);
+      const uint32_t m0 = k0 + 2 * kp < S ? 0xFFFFFFFFu : 0u, m1 = k0 + 2 * kp + 1 < S ? 0xFFFFFFFFu : 0u;
+      const uint32_t w0[4] = {rv[2 * j].x & m0, rv[2 * j].y & m0, rv[2 * j].z & m0, rv[2 * j].w & m0};
+      const uint32_t w1[4] = {rv[2 * j + 1].x & m1, rv[2 * j + 1].y & m1, rv[2 * j + 1].z & m1, rv[2 * j + 1].w & m1};
+      uint8_t *col = vt + (dg * 8) * L::kVt + 4 * kp;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        *(uint32_t *)(col + (2 * qd) * L::kVt) = __builtin_amdgcn_perm(w1[qd], w0[qd], 0x05040100u);
+        *(uint32_t *)(col + (2 * qd + 1) * L::kVt) = __builtin_amdgcn_perm(w1[qd], w0[qd], 0x07060302u);
+      }
     }
   };
 
   load_block(0);
-  store_block(0);
+  store_block(0, 0);
   __syncthreads();
 
   for (int64_t kb = 0; kb < nkb; ++kb) {
@@ -262,7 +278,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
         }
       }
     }
-    if (kb + 1 < nkb) store_block((int)((kb + 1) & 1));
+    if (kb + 1 < nkb) store_block((int)((kb + 1) & 1), (kb + 1) * kBK);
     __syncthreads();
   }
 
@@ -992,19 +1008,20 @@ __global__ __launch_bounds__(256, 2) void attention_ds_gemm_kernel(DsGemmArgs p)
 
 }  // namespace
 
-size_t attention_fwd_ws_bytes(int64_t G, int64_t S, int64_t D) {
-  return round_up((size_t)(G * S * D) * 2, 256);
-}
+size_t attention_fwd_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
 
 fs4_status launch_attention_fwd(const fs4_nvfp4 &Q, const fs4_nvfp4 &K, const uint16_t *V, int64_t G, int64_t S,
                                 int64_t D, int causal, float *O, float *LSE, uint16_t *Vt, hipStream_t s) {
-  const dim3 tg((unsigned)((S + 63) / 64), (unsigned)((D + 63) / 64), (unsigned)G);
-  transpose_bf16_kernel<<<tg, 256, 0, s>>>(V, S, D, Vt);
-  if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
+  if (Vt) {
+    // V^T as a side output, for callers that keep it
+    const dim3 tg((unsigned)((S + 63) / 64), (unsigned)((D + 63) / 64), (unsigned)G);
+    transpose_bf16_kernel<<<tg, 256, 0, s>>>(V, S, D, Vt);
+    if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
+  }
   AttnArgs a;
   a.q_codes = Q.codes; a.q_scales = Q.scales; a.k_codes = K.codes; a.k_scales = K.scales;
   a.q_ts = Q.tscale; a.k_ts = K.tscale;
-  a.vt = Vt; a.o = O; a.lse = LSE;
+  a.v = V; a.o = O; a.lse = LSE;
   a.G = G; a.S = S;
   a.scale = (float)(1.0 / __builtin_sqrt((double)D));
   a.causal = causal;

@@ -35,7 +35,7 @@ def _run(G, S, D, causal, seed, seqs=None, std_qk=1.0):
     Q, K, V = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     q_row, q_col = fs4.attention_quantize(Q)
     k_row, k_col = fs4.attention_quantize(K)
-    out = fs4.attention_fwd(q_row, k_row, V, causal)
+    out = fs4.attention_fwd(q_row, k_row, V, causal, keep_vt=True)
     torch.cuda.synchronize()
     q32, k32, v32 = (synth.bf16_to_f32(x) for x in (qb, kb, vb))
     ref = attention_fwd(q32, k32, v32, causal, seqs=seqs)
@@ -47,8 +47,11 @@ def _run(G, S, D, causal, seed, seqs=None, std_qk=1.0):
     err_l = np.max(np.abs(LSE[sel] - ref["LSE"][sel]) / np.maximum(1.0, np.abs(ref["LSE"][sel])))
     print("O err %.3e (bar %.3e)  LSE err %.3e" % (err_o, O_TOL, err_l), flush=True)
     assert err_o <= O_TOL and err_l <= LSE_TOL, (err_o, err_l)
-    # V^T as the backward reuses it
+    # V^T as a side output; and the same forward without it is bit-identical
     assert torch.equal(out.Vt, V.transpose(1, 2).contiguous())
+    out2 = fs4.attention_fwd(q_row, k_row, V, causal)
+    assert out2.Vt is None
+    assert torch.equal(out2.O, out.O) and torch.equal(out2.LSE, out.LSE)
     return err_o
 
 
