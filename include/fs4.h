@@ -409,9 +409,8 @@ fs4_status fs4_attention_fwd(const fs4_nvfp4 *Q_row, const fs4_nvfp4 *K_row, con
  *            its quantization (zeros where masked); without it dS is never
  *            stored in fp32 (the keys are walked twice: dV and the amax of
  *            dS, then dS again, encoded straight into its NVFP4 views)
- *   workspace: fs4_attention_bwd_workspace_bytes(G, S, D) (dO^T, Delta and
- *   dS's two NVFP4 views, about 1.1 G S^2 + 2 G S D bytes), 256-byte
- *   aligned.
+ *   workspace: fs4_attention_bwd_workspace_bytes(G, S, D) (Delta and dS's
+ *   two NVFP4 views, about 1.1 G S^2 bytes), 256-byte aligned.
  *   D = 64 or 128; S a positive multiple of 16; G >= 1, G*S < 2^31 and
  *   G*S*S < 2^31.  All buffers 16-byte aligned (LSE 4).
  * Errors: FS4_ERR_SHAPE, FS4_ERR_NULL, FS4_ERR_ALIGN, FS4_ERR_WORKSPACE (the

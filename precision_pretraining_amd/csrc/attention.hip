@@ -348,7 +348,6 @@ struct AttnBwdArgs {
   const float *q_ts, *k_ts;
   const uint16_t *v;      // bf16 [G][S][D]
   const uint16_t *dout;   // bf16 [G][S][D]
-  const uint16_t *doutt;  // bf16 [G][D][S]
   const float *lse;       // [G][S], natural log
   const float *delta;     // [G][S]
   float *ds;              // fp32 [G*S][S], nullable: dS for the caller
@@ -371,8 +370,10 @@ struct BwdLds {
   static constexpr int kDeltaOff = kLseOff + kBwdQ * 4;
   static constexpr int kStage = kDeltaOff + kBwdQ * 4;
   static constexpr int kEpt = kBwdQ * D / kAttnThreads;                // Q elements a thread expands
-  static constexpr int kDoPer = kBwdQ * D * 2 / 16 / kAttnThreads;     // 16-byte words of dO per thread
-  static constexpr int kDtPer = D * kBwdQ * 2 / 16 / kAttnThreads;     // and of dO^T
+  // dO words (8 dims of a query) in pairs of consecutive queries: each pair
+  // is stored as two rows of dO and, transposed, as 32-bit words of dO^T
+  static constexpr int kDoPairs = (kBwdQ / 2) * (D / 8) / kAttnThreads;   // 2 for D = 128, 1 for D = 64
+  static_assert((kBwdQ / 2) * (D / 8) % kAttnThreads == 0, "dO staging");
   static_assert(D / kEpt == 4 && kEpt % 16 == 0, "Q staging: four threads per row, whole scale blocks");
   static_assert(kStage % 16 == 0, "stage alignment");
 };
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
   // ---- query-block staging: global -> registers -> LDS ---------------------
   uint4 rq = make_uint4(0, 0, 0, 0);
   uint32_t rqs = 0;
-  uint4 rdo[L::kDoPer], rdt[L::kDtPer];
+  uint4 rdo[2 * L::kDoPairs];
   float rls = 0.0f;
   const int qrow = tid / 4, qc0 = (tid % 4) * L::kEpt;   // the Q elements this thread expands
   auto load_block = [&](int64_t q0) {
@@ -440,26 +441,25 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
         rqs = *sp;
       }
     }
+    // (queries past S load the last query and are zeroed where they are
+    // stored, not behind the load)
 #pragma unroll
-    for (int i = 0; i < L::kDoPer; ++i) {
-      const int idx = tid + i * kAttnThreads;
-      const int row = idx / (D / 8), ch = idx % (D / 8);
-      const int64_t qq = q0 + row;
-      rdo[i] = qq < S ? *(const uint4 *)(a.dout + (g * S + qq) * D + ch * 8) : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < L::kDoPairs; ++j) {
+      const int idx = tid + j * kAttnThreads;
+      const int qp = idx % (kBwdQ / 2), dg = idx / (kBwdQ / 2);
 #pragma unroll
-    for (int i = 0; i < L::kDtPer; ++i) {
-      const int idx = tid + i * kAttnThreads;
-      const int d = idx / (kBwdQ / 8), ch = idx % (kBwdQ / 8);   // 8 queries per word
-      const int64_t qq = q0 + ch * 8;
-      rdt[i] = qq < S ? *(const uint4 *)(a.doutt + (g * D + d) * S + qq) : make_uint4(0, 0, 0, 0);
+      for (int b = 0; b < 2; ++b) {
+        int64_t qq = q0 + 2 * qp + b;
+        qq = qq < S ? qq : S - 1;
+        rdo[2 * j + b] = *(const uint4 *)(a.dout + (g * S + qq) * D + dg * 8);
+      }
     }
     if (tid < 2 * kBwdQ) {
       const int64_t qq = q0 + (tid & (kBwdQ - 1));
       rls = qq < S ? (tid < kBwdQ ? a.lse[g * S + qq] * kLog2e : a.delta[g * S + qq]) : 0.0f;
     }
   };
-  auto store_block = [&](int st) {
+  auto store_block = [&](int st, int64_t q0) {
     uint8_t *base = lds + st * L::kStage;
     _Float16 *qh = (_Float16 *)(base + L::kQhOff) + qrow * L::kQh + qc0;
     const uint32_t cw[4] = {rq.x, rq.y, rq.z, rq.w};
@@ -467,16 +467,24 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
     for (int j = 0; j < L::kEpt / 8; ++j)
       *(f16x8_t *)(qh + 8 * j) = expand8(cw[j], split_scale((rqs >> (8 * (j / 2))) & 0xFFu));
 #pragma unroll
-    for (int i = 0; i < L::kDoPer; ++i) {
-      const int idx = tid + i * kAttnThreads;
-      const int row = idx / (D / 8), ch = idx % (D / 8);
-      *(uint4 *)(base + L::kDoOff + (row * L::kDo + ch * 8) * 2) = rdo[i];
-    }
+    for (int j = 0; j < L::kDoPairs; ++j) {
+      const int idx = tid + j * kAttnThreads;
+      const int qp = idx % (kBwdQ / 2), dg = idx / (kBwdQ / 2);
+      const uint32_t m0 = q0 + 2 * qp < S ? 0xFFFFFFFFu : 0u, m1 = q0 + 2 * qp + 1 < S ? 0xFFFFFFFFu : 0u;
+      const uint4 w0 = make_uint4(rdo[2 * j].x & m0, rdo[2 * j].y & m0, rdo[2 * j].z & m0, rdo[2 * j].w & m0);
+      const uint4 w1 = make_uint4(rdo[2 * j + 1].x & m1, rdo[2 * j + 1].y & m1, rdo[2 * j + 1].z & m1,
+                                  rdo[2 * j + 1].w & m1);
+      *(uint4 *)(base + L::kDoOff + ((2 * qp) * L::kDo + dg * 8) * 2) = w0;
+      *(uint4 *)(base + L::kDoOff + ((2 * qp + 1) * L::kDo + dg * 8) * 2) = w1;
+      // dO^T rows [d][queries]: dims 2c, 2c + 1 of the pair become two 32-bit
+      // words (query 2 qp in the low half, 2 qp + 1 in the high half)
+      const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w}, a1[4] = {w1.x, w1.y, w1.z, w1.w};
+      uint8_t *col = base + L::kDtOff + (dg * 8) * L::kDt * 2 + 4 * qp;
 #pragma unroll
-    for (int i = 0; i < L::kDtPer; ++i) {
-      const int idx = tid + i * kAttnThreads;
-      const int d = idx / (kBwdQ / 8), ch = idx % (kBwdQ / 8);
-      *(uint4 *)(base + L::kDtOff + (d * L::kDt + ch * 8) * 2) = rdt[i];
+      for (int c = 0; c < 4; ++c) {
+        *(uint32_t *)(col + (2 * c) * L::kDt * 2) = __builtin_amdgcn_perm(a1[c], a0[c], 0x05040100u);
+        *(uint32_t *)(col + (2 * c + 1) * L::kDt * 2) = __builtin_amdgcn_perm(a1[c], a0[c], 0x07060302u);
+      }
     }
     if (tid < 2 * kBwdQ) ((float *)(base + L::kLseOff))[tid] = rls;   // lse2 then delta, adjacent
   };
@@ -492,7 +500,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
   const int64_t nqb = (S + kBwdQ - 1) / kBwdQ;
   const int64_t qb0 = a.causal ? k0 / kBwdQ : 0;
   load_block(qb0 * kBwdQ);
-  store_block(0);
+  store_block(0, qb0 * kBwdQ);
   __syncthreads();
 
   for (int64_t qb = qb0; qb < nqb; ++qb) {
@@ -570,7 +578,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
         dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[qt][s], dvt[dt], 0, 0, 0);
       }
     }
-    if (qb + 1 < nqb) store_block(st ^ 1);
+    if (qb + 1 < nqb) store_block(st ^ 1, (qb + 1) * kBwdQ);
     __syncthreads();
   }
 
@@ -1040,7 +1048,6 @@ size_t attention_bwd_ws_bytes(int64_t G, int64_t S, int64_t D) {
 
 AttnBwdWs attention_bwd_carve(Carver &c, int64_t G, int64_t S, int64_t D) {
   AttnBwdWs w;
-  w.doutt = (uint16_t *)c.take((size_t)(G * S * D) * 2);
   w.delta = (float *)c.take((size_t)(G * S) * 4);
   w.nwg = G * ((S + kBwdKeys - 1) / kBwdKeys);
   w.amax = (uint32_t *)c.take((size_t)w.nwg * 4);
@@ -1053,8 +1060,6 @@ fs4_status launch_attention_bwd(const fs4_nvfp4 &Qr, const fs4_nvfp4 &Kr, const 
                                 const fs4_nvfp4 &Kc, const uint16_t *V, const uint16_t *dO, const float *O,
                                 const float *LSE, int64_t G, int64_t S, int64_t D, int causal, float *dQ,
                                 float *dK, float *dV, float *dS, const AttnBwdWs &w, hipStream_t s) {
-  const dim3 tg((unsigned)((S + 63) / 64), (unsigned)((D + 63) / 64), (unsigned)G);
-  transpose_bf16_kernel<<<tg, 256, 0, s>>>(dO, S, D, w.doutt);
   const int64_t rows = G * S;
   const unsigned dgrid = (unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)));
   if (D == 128) attention_delta_kernel<128><<<dgrid, 256, 0, s>>>(dO, O, rows, w.delta);
@@ -1066,7 +1071,7 @@ fs4_status launch_attention_bwd(const fs4_nvfp4 &Qr, const fs4_nvfp4 &Kr, const 
   AttnBwdArgs a;
   a.q_codes = Qr.codes; a.q_scales = Qr.scales; a.k_codes = Kr.codes; a.k_scales = Kr.scales;
   a.q_ts = Qr.tscale; a.k_ts = Kr.tscale;
-  a.v = V; a.dout = dO; a.doutt = w.doutt; a.lse = LSE; a.delta = w.delta;
+  a.v = V; a.dout = dO; a.lse = LSE; a.delta = w.delta;
   a.ds = dS; a.dv = dV; a.amax = w.amax;
   a.G = G; a.S = S;
   a.scale = scale;

@@ -129,16 +129,16 @@ fs4_status launch_abs_quantile(const void *x, fs4_dtype dt, int64_t n, double q,
                                hipStream_t s);
 
 // NVFP4 mixed-precision attention forward: Q, K row-wise views of [G*S, D],
-// V bf16 [G][S][D]; V^T [G][D][S] is written to Vt (caller's or workspace)
+// V bf16 [G][S][D]; Vt (nullable) receives V^T [G][D][S] as a side output;
+// no workspace (attention_fwd_ws_bytes is 0)
 size_t attention_fwd_ws_bytes(int64_t G, int64_t S, int64_t D);
 fs4_status launch_attention_fwd(const fs4_nvfp4 &Q, const fs4_nvfp4 &K, const uint16_t *V, int64_t G, int64_t S,
                                 int64_t D, int causal, float *O, float *LSE, uint16_t *Vt, hipStream_t s);
 
-// Its backward.  Workspace: dO^T, Delta, one amax partial per softmax-gradient
+// Its backward.  Workspace: Delta, one amax partial per softmax-gradient
 // workgroup and dS's two NVFP4 views (row-wise [G*S][S], column-wise
 // [S][G*S]).
 struct AttnBwdWs {
-  uint16_t *doutt;
   float *delta;
   uint32_t *amax;
   int64_t nwg;

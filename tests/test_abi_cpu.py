@@ -421,7 +421,7 @@ def test_attention_bwd_validation():
     assert abwd(dS=A16 + 8) == ALIGN
     assert abwd(wsb=1024) == WORKSPACE
     need = lib.fs4_attention_bwd_workspace_bytes(2, 64, 128)
-    assert need >= 2 * 64 * 128 * 2 + 2 * (2 * 64 * 64 * 9 // 16)   # dO^T and dS's two NVFP4 views
+    assert need >= 2 * (2 * 64 * 64 * 9 // 16)   # at least dS's two NVFP4 views
     assert abwd(wsb=need - 1) == WORKSPACE
     assert lib.fs4_attention_bwd_workspace_bytes(2, 64, 96) == 0
     assert lib.fs4_attention_bwd_workspace_bytes(1 << 12, 1 << 10, 128) == 0
