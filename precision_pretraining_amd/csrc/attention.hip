@@ -894,13 +894,19 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void attention_ds_gemm_kernel(DsGemmArgs p) {
   constexpr int TN = D / 32;
   constexpr int TM = 2;
-  constexpr int kH = kDsKC + 8;                 // FP16 per LDS row
-  constexpr int A_BYTES = kDsBM * kH * 2, B_BYTES = D * kH * 2;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int APER = kDsBM * (kDsKC / 16) / 256;   // 16-element units per thread
-  constexpr int BPER = D * (kDsKC / 16) / 256;
-  static_assert(APER == 4 && BPER >= 1, "staging");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[STAGE];   // one stage: two workgroups fit a CU
+  // An LDS stage holds a chunk's codes and scales as they sit in memory (4
+  // bits per element); each wave expands the fragments it multiplies in
+  // registers, so the LDS traffic per MFMA is a quarter of FP16 staging.
+  constexpr int kCS = kDsKC / 2 + 8;            // code bytes per LDS row (40: 2-way conflicts at most)
+  constexpr int kSB = kDsKC / 16;               // scale bytes per row and chunk
+  constexpr int A_C = kDsBM * kCS, B_C = D * kCS, A_S = kDsBM * kSB, B_S = D * kSB;
+  constexpr int STAGE = A_C + B_C + A_S + B_S;
+  // staging unit: one 16-element block of a row (8 code bytes, 1 scale byte)
+  constexpr int AU = kDsBM * kSB, BU = D * kSB;
+  constexpr int APER = AU / 256, BPER = (BU + 255) / 256;
+  static_assert(AU % 256 == 0 && kSB == 4, "staging");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  __shared__ uint2 lut[128];   // E4M3 byte -> {2^E as fp32 bits, F as two FP16}
 
   const int z = blockIdx.y;
   const DsOperand A = p.a[z], B = p.b[z];
@@ -918,48 +924,59 @@ __global__ __launch_bounds__(256, 2) void attention_ds_gemm_kernel(DsGemmArgs p)
   const uint8_t *bc = B.codes + g * B.gs, *bs = B.scales + g * (B.gs / 8);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
 
+  for (int b = tid; b < 128; b += 256) {
+    const ScalePair sp = split_scale((uint32_t)b);
+    lut[b] = make_uint2(__builtin_bit_cast(uint32_t, sp.pow2), __builtin_bit_cast(uint32_t, sp.mant));
+  }
+
+  // A block is zero, and masked to zero (codes and scale) where it is stored,
+  // when it lies past S or k_hi or wholly above a causal diagonal: dQ (rows
+  // are queries) past the row, dK (rows are keys) before it.  The loads read
+  // clamped, in-range blocks, so that none sits in a branch.
+  auto a_blk_ok = [&](int64_t rg, int64_t kg) {
+    const bool above = (mode == 1 && kg > rg) || (mode == 2 && kg + 15 < rg);
+    return rg < S && kg < k_hi && !above;
+  };
   uint2 ra[APER], rbv[BPER];
-  uint32_t ras = 0, rbs = 0;   // one scale byte per unit
+  uint8_t rsa[APER], rsb[BPER];
   auto load = [&](int kc) {
     const int64_t kk0 = k_lo + (int64_t)kc * kDsKC;
-    ras = 0;
-    rbs = 0;
 #pragma unroll
     for (int i = 0; i < APER; ++i) {
-      const int u = tid + i * 256, row = u >> 2, blk = u & 3;
-      const int64_t rg = r0 + row, kg = kk0 + 16 * blk;
-      // blocks wholly above a causal diagonal are zero and are not read:
-      // dQ (rows are queries) past the row, dK (rows are keys) before it
-      const bool above = (mode == 1 && kg > rg) || (mode == 2 && kg + 15 < rg);
-      const bool ok = rg < S && kg < k_hi && !above;
-      ra[i] = ok ? *(const uint2 *)(ac + rg * A.ld + kg / 2) : make_uint2(0, 0);
-      ras |= (ok ? (uint32_t)as[rg * (A.ld / 8) + kg / 16] : 0u) << (8 * i);
+      const int u = tid + i * 256, row = u / kSB, blk = u % kSB;
+      int64_t rg = r0 + row, kg = kk0 + 16 * blk;
+      rg = rg < S ? rg : S - 1;
+      kg = kg < k_hi ? kg : k_hi - 16;
+      ra[i] = *(const uint2 *)(ac + rg * A.ld + kg / 2);
+      rsa[i] = as[rg * (A.ld / 8) + kg / 16];
     }
 #pragma unroll
     for (int i = 0; i < BPER; ++i) {
-      const int u = tid + i * 256, row = u >> 2, blk = u & 3;
-      const int64_t kg = kk0 + 16 * blk;
-      const bool ok = kg < k_hi;
-      rbv[i] = ok ? *(const uint2 *)(bc + row * B.ld + kg / 2) : make_uint2(0, 0);
-      rbs |= (ok ? (uint32_t)bs[row * (B.ld / 8) + kg / 16] : 0u) << (8 * i);
+      const int u = tid + i * 256, row = (u < BU ? u : 0) / kSB, blk = u % kSB;
+      int64_t kg = kk0 + 16 * blk;
+      kg = kg < k_hi ? kg : k_hi - 16;
+      rbv[i] = *(const uint2 *)(bc + row * B.ld + kg / 2);
+      rsb[i] = bs[row * (B.ld / 8) + kg / 16];
     }
   };
-  auto store = [&](int st) {
-    _Float16 *ah = (_Float16 *)(lds + st * STAGE);
-    _Float16 *bh = (_Float16 *)(lds + st * STAGE + A_BYTES);
+  auto store = [&](int st, int kc) {
+    const int64_t kk0 = k_lo + (int64_t)kc * kDsKC;
+    uint8_t *base = lds + st * STAGE;
 #pragma unroll
     for (int i = 0; i < APER; ++i) {
-      const int u = tid + i * 256, row = u >> 2, blk = u & 3;
-      const ScalePair sp = split_scale((ras >> (8 * i)) & 0xFFu);
-      *(f16x8_t *)(ah + row * kH + 16 * blk) = expand8(ra[i].x, sp);
-      *(f16x8_t *)(ah + row * kH + 16 * blk + 8) = expand8(ra[i].y, sp);
+      const int u = tid + i * 256, row = u / kSB, blk = u % kSB;
+      const uint32_t m = a_blk_ok(r0 + row, kk0 + 16 * blk) ? 0xFFFFFFFFu : 0u;
+      *(uint2 *)(base + row * kCS + 8 * blk) = make_uint2(ra[i].x & m, ra[i].y & m);
+      base[A_C + B_C + row * kSB + blk] = (uint8_t)(rsa[i] & m);
     }
 #pragma unroll
     for (int i = 0; i < BPER; ++i) {
-      const int u = tid + i * 256, row = u >> 2, blk = u & 3;
-      const ScalePair sp = split_scale((rbs >> (8 * i)) & 0xFFu);
-      *(f16x8_t *)(bh + row * kH + 16 * blk) = expand8(rbv[i].x, sp);
-      *(f16x8_t *)(bh + row * kH + 16 * blk + 8) = expand8(rbv[i].y, sp);
+      const int u = tid + i * 256, row = u / kSB, blk = u % kSB;
+      if (u < BU) {
+        const uint32_t m = kk0 + 16 * blk < k_hi ? 0xFFFFFFFFu : 0u;
+        *(uint2 *)(base + A_C + row * kCS + 8 * blk) = make_uint2(rbv[i].x & m, rbv[i].y & m);
+        base[A_C + B_C + A_S + row * kSB + blk] = (uint8_t)(rsb[i] & m);
+      }
     }
   };
 
@@ -971,31 +988,42 @@ __global__ __launch_bounds__(256, 2) void attention_ds_gemm_kernel(DsGemmArgs p)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  auto lut_pair = [&](uint32_t byte) {
+    const uint2 v = lut[byte & 0x7Fu];
+    ScalePair sp;
+    sp.pow2 = __builtin_bit_cast(float, v.x);
+    sp.mant = __builtin_bit_cast(f16x2_t, v.y);
+    return sp;
+  };
   if (nkc > 0) {
     load(0);
-    store(0);
-    __syncthreads();
+    store(0, 0);
   }
+  __syncthreads();   // the table and the first chunk
   for (int kc = 0; kc < nkc; ++kc) {
     if (kc + 1 < nkc) load(kc + 1);
-    const _Float16 *ah = (const _Float16 *)lds;
-    const _Float16 *bh = (const _Float16 *)(lds + A_BYTES);
+    const uint8_t *base = lds + (kc & 1) * STAGE;
+    const uint8_t *a_rows = base + (64 * w + l32) * kCS, *b_rows = base + A_C + l32 * kCS;
+    uint32_t sa[TM], sb[TN];   // the chunk's four scale bytes of each fragment row
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = *(const uint32_t *)(base + A_C + B_C + (64 * w + 32 * i + l32) * kSB);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] = *(const uint32_t *)(base + A_C + B_C + A_S + (32 * j + l32) * kSB);
 #pragma unroll
     for (int ks = 0; ks < kDsKC / 16; ++ks) {
       f16x8_t af[TM], bf[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *(const f16x8_t *)(ah + (64 * w + 32 * i + l32) * kH + 16 * ks + 8 * h);
+      for (int i = 0; i < TM; ++i)
+        af[i] = expand8(*(const uint32_t *)(a_rows + 32 * i * kCS + 8 * ks + 4 * h), lut_pair(sa[i] >> (8 * ks)));
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bf[j] = *(const f16x8_t *)(bh + (32 * j + l32) * kH + 16 * ks + 8 * h);
+      for (int j = 0; j < TN; ++j)
+        bf[j] = expand8(*(const uint32_t *)(b_rows + 32 * j * kCS + 8 * ks + 4 * h), lut_pair(sb[j] >> (8 * ks)));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (kc + 1 < nkc) {
-      __syncthreads();
-      store(0);
-    }
+    if (kc + 1 < nkc) store((kc + 1) & 1, kc + 1);   // that stage was last read in chunk kc - 1
     __syncthreads();
   }
 
