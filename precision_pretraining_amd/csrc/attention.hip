@@ -346,13 +346,9 @@ constexpr int kBwdQ = 64;       // queries per step: two 32-query tiles
 struct AttnBwdArgs {
   const uint8_t *q_codes, *q_scales, *k_codes, *k_scales;
   const float *q_ts, *k_ts;
-  const uint16_t *v;      // bf16 [G][S][D]
   const uint16_t *dout;   // bf16 [G][S][D]
   const float *lse;       // [G][S], natural log
-  const float *delta;     // [G][S]
-  float *ds;              // fp32 [G*S][S], nullable: dS for the caller
   float *dv;              // fp32 [G][S][D]
-  uint32_t *amax;         // one max |dS| per workgroup (fp32 bits)
   int64_t G, S;
   float scale;
   int causal;
@@ -361,17 +357,14 @@ struct AttnBwdArgs {
 template <int D>
 struct BwdLds {
   static constexpr int kQh = D + 8;       // FP16 per row of the expanded Q block
-  static constexpr int kDo = D + 8;       // BF16 per row of the dO block
   static constexpr int kDt = kBwdQ + 8;   // BF16 per row of dO^T
   static constexpr int kQhOff = 0;
-  static constexpr int kDoOff = kQhOff + kBwdQ * kQh * 2;
-  static constexpr int kDtOff = kDoOff + kBwdQ * kDo * 2;
+  static constexpr int kDtOff = kQhOff + kBwdQ * kQh * 2;
   static constexpr int kLseOff = kDtOff + D * kDt * 2;
-  static constexpr int kDeltaOff = kLseOff + kBwdQ * 4;
-  static constexpr int kStage = kDeltaOff + kBwdQ * 4;
+  static constexpr int kStage = kLseOff + kBwdQ * 4;
   static constexpr int kEpt = kBwdQ * D / kAttnThreads;                // Q elements a thread expands
   // dO words (8 dims of a query) in pairs of consecutive queries: each pair
-  // is stored as two rows of dO and, transposed, as 32-bit words of dO^T
+  // is stored, transposed, as 32-bit words of dO^T
   static constexpr int kDoPairs = (kBwdQ / 2) * (D / 8) / kAttnThreads;   // 2 for D = 128, 1 for D = 64
   static_assert((kBwdQ / 2) * (D / 8) % kAttnThreads == 0, "dO staging");
   static_assert(D / kEpt == 4 && kEpt % 16 == 0, "Q staging: four threads per row, whole scale blocks");
@@ -379,12 +372,11 @@ struct BwdLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void attention_bwd_kernel(AttnBwdArgs a) {
   using L = BwdLds<D>;
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::kStage];
-  __shared__ uint32_t red[kAttnThreads / 64];
 
   const int64_t G = a.G, S = a.S;
   const int64_t g = blockIdx.x % G;
@@ -397,27 +389,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
   const bool key_ok = key < S;
   const int64_t keyc = key_ok ? key : S - 1;
 
-  // ---- this wave's keys: K expanded to FP16 and V, both B operands --------
+  // ---- this wave's keys: K expanded to FP16, the B operand of S ------------
   f16x8_t kf[KSTEPS];
-  bf16x8_t vf[KSTEPS];
   {
     const uint8_t *krow = a.k_codes + (g * S + keyc) * (D / 2);
     const uint8_t *ksc = a.k_scales + (g * S + keyc) * (D / 16);
-    const uint16_t *vrow = a.v + (g * S + keyc) * D;
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
+    for (int t = 0; t < KSTEPS; ++t)
       kf[t] = expand8(*(const uint32_t *)(krow + 8 * t + 4 * h), split_scale(ksc[t]));   // d = 16t + 8h .. +8
-      vf[t] = *(const bf16x8_t *)(vrow + 16 * t + 8 * h);
-    }
-  }
-
-  // ---- under a causal mask, dS is zero for the queries before this block ---
-  if (a.ds && a.causal && k0 > 0) {
-    const int64_t n4 = (kend - k0) / 4;
-    for (int64_t i = tid; i < k0 * n4; i += kAttnThreads) {
-      const int64_t row = i / n4, c = i % n4;
-      *(float4 *)(a.ds + (g * S + row) * S + k0 + 4 * c) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
   }
 
   // ---- query-block staging: global -> registers -> LDS ---------------------
@@ -454,9 +433,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
         rdo[2 * j + b] = *(const uint4 *)(a.dout + (g * S + qq) * D + dg * 8);
       }
     }
-    if (tid < 2 * kBwdQ) {
-      const int64_t qq = q0 + (tid & (kBwdQ - 1));
-      rls = qq < S ? (tid < kBwdQ ? a.lse[g * S + qq] * kLog2e : a.delta[g * S + qq]) : 0.0f;
+    if (tid < kBwdQ) {
+      const int64_t qq = q0 + tid;
+      rls = qq < S ? a.lse[g * S + qq] * kLog2e : 0.0f;
     }
   };
   auto store_block = [&](int st, int64_t q0) {
@@ -474,8 +453,6 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
       const uint4 w0 = make_uint4(rdo[2 * j].x & m0, rdo[2 * j].y & m0, rdo[2 * j].z & m0, rdo[2 * j].w & m0);
       const uint4 w1 = make_uint4(rdo[2 * j + 1].x & m1, rdo[2 * j + 1].y & m1, rdo[2 * j + 1].z & m1,
                                   rdo[2 * j + 1].w & m1);
-      *(uint4 *)(base + L::kDoOff + ((2 * qp) * L::kDo + dg * 8) * 2) = w0;
-      *(uint4 *)(base + L::kDoOff + ((2 * qp + 1) * L::kDo + dg * 8) * 2) = w1;
       // dO^T rows [d][queries]: dims 2c, 2c + 1 of the pair become two 32-bit
       // words (query 2 qp in the low half, 2 qp + 1 in the high half)
       const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w}, a1[4] = {w1.x, w1.y, w1.z, w1.w};
@@ -486,7 +463,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
         *(uint32_t *)(col + (2 * c + 1) * L::kDt * 2) = __builtin_amdgcn_perm(a1[c], a0[c], 0x07060302u);
       }
     }
-    if (tid < 2 * kBwdQ) ((float *)(base + L::kLseOff))[tid] = rls;   // lse2 then delta, adjacent
+    if (tid < kBwdQ) ((float *)(base + L::kLseOff))[tid] = rls;   // LSE in log2 units
   };
 
   const float c_log2 = (*a.q_ts) * (*a.k_ts) * a.scale * kLog2e;   // S in log2 units
@@ -495,7 +472,6 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dvt[i][e] = 0.0f;
-  float amax = 0.0f;
 
   const int64_t nqb = (S + kBwdQ - 1) / kBwdQ;
   const int64_t qb0 = a.causal ? k0 / kBwdQ : 0;
@@ -508,10 +484,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
     const int st = (int)((qb - qb0) & 1);
     const uint8_t *base = lds + st * L::kStage;
     const _Float16 *qh = (const _Float16 *)(base + L::kQhOff);
-    const uint16_t *dor = (const uint16_t *)(base + L::kDoOff);
     const uint8_t *dtr = base + L::kDtOff;
     const float *lse2 = (const float *)(base + L::kLseOff);
-    const float *dlt = (const float *)(base + L::kDeltaOff);
     const int64_t q0 = qb * kBwdQ;
     bf16x8_t pb[2][2];
     bool live[2];
@@ -520,40 +494,29 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
       const int64_t qt0 = q0 + 32 * qt;
       // some query of this tile sees some key of this wave (wave-uniform)
       live[qt] = qt0 < S && (!a.causal || qt0 + 31 >= kw0);
-      floatx16_t sacc, dp;
+      floatx16_t sacc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sacc[e] = 0.0f;
-        dp[e] = 0.0f;
-      }
+      for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
       if (live[qt]) {
         const int r = 32 * qt + l32;
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t)
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8_t *)(qh + r * L::kQh + 16 * t + 8 * h), kf[t],
                                                          sacc, 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t)
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(dor + r * L::kDo + 16 * t + 8 * h), vf[t],
-                                                        dp, 0, 0, 0);
       }
       // register e holds query q0 + 32 qt + 8 (e/4) + 4 h + e%4 of key `key`
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int qi = 32 * qt + 8 * c + 4 * h;
         const float4 l4 = *(const float4 *)(lse2 + qi);
-        const float4 d4 = *(const float4 *)(dlt + qi);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = 4 * c + r;
           const int64_t query = q0 + qi + r;
           const bool valid = key_ok && query < S && (!a.causal || key <= query);
           const float p = valid ? __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[r]) : 0.0f;
-          const float dsv = valid ? p * (dp[e] - dv[r]) : 0.0f;
           pb[qt][e >> 3][e & 7] = (__bf16)p;
-          amax = fmaxf(amax, fabsf(dsv));
-          if (a.ds && key_ok && query < S) a.ds[(g * S + query) * S + key] = dsv;
         }
       }
     }
@@ -582,7 +545,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
     __syncthreads();
   }
 
-  // ---- dV, and this workgroup's max |dS| -----------------------------------
+  // ---- dV -------------------------------------------------------------------
   if (key_ok) {
     float *vrow = a.dv + (g * S + key) * D;
 #pragma unroll
@@ -592,6 +555,189 @@ __global__ __launch_bounds__(kAttnThreads) void attention_bwd_kernel(AttnBwdArgs
         *(float4 *)(vrow + dt * 32 + 8 * c + 4 * h) =
             make_float4(dvt[dt][4 * c], dvt[dt][4 * c + 1], dvt[dt][4 * c + 2], dvt[dt][4 * c + 3]);
   }
+}
+
+// ---- the amax of dS ------------------------------------------------------------
+// dS's tensor scale needs max |dS| over all of it before any block is encoded.
+// This pass forms S, P, dP and dS query-major, as the forward walks the keys:
+// a workgroup takes 128 queries (32 per wave) and walks 64-key blocks, with
+// each block's K expanded to FP16 and its V rows staged in LDS, and keeps only
+// the maximum (and dS itself when the caller asks for it).  Every product
+// takes the same operands in the same roles and order as the key-major
+// passes (A = Q or dO, B = K or V, k-steps over D in order), so its dS values
+// are bit for bit the ones the second pass encodes.
+struct AttnAmaxArgs {
+  const uint8_t *q_codes, *q_scales, *k_codes, *k_scales;
+  const float *q_ts, *k_ts;
+  const uint16_t *v;      // bf16 [G][S][D]
+  const uint16_t *dout;   // bf16 [G][S][D]
+  const float *lse;       // [G][S], natural log
+  const float *delta;     // [G][S]
+  float *ds;              // fp32 [G*S][S], nullable: dS for the caller
+  uint32_t *amax;         // one max |dS| per workgroup (fp32 bits)
+  int64_t G, S;
+  float scale;
+  int causal;
+};
+
+constexpr int kAmK = 32;   // keys per block of the amax pass (one MFMA tile)
+
+template <int D>
+struct AmaxLds {
+  static constexpr int kKh = D + 8;   // FP16 per row of the expanded K block
+  static constexpr int kVr = D + 8;   // BF16 per row of the V block
+  static constexpr int kKhBytes = kAmK * kKh * 2, kVBytes = kAmK * kVr * 2;
+  static constexpr int kStage = kKhBytes + kVBytes;
+  static constexpr int kEpt = kAmK * D / kAttnThreads;           // K elements a thread expands (16 or 8)
+  static constexpr int kTpr = D / kEpt;                          // threads per K row (8)
+  static constexpr int kVPer = kAmK * D * 2 / 16 / kAttnThreads;  // 16-byte words of V per thread
+  static_assert(kEpt % 8 == 0 && kVPer >= 1, "staging");
+};
+
+// KEEP: write dS too (the caller asked for it; every key block is walked so
+// that its zeros above a causal diagonal are written as well)
+template <int D, bool KEEP>
+__global__ __launch_bounds__(kAttnThreads, 2) void attention_amax_kernel(AttnAmaxArgs a) {
+  using L = AmaxLds<D>;
+  constexpr int KSTEPS = D / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::kStage];
+  __shared__ __attribute__((aligned(16))) float qv[2][kBQ];   // LSE (log2 units) and Delta of the queries
+  __shared__ uint32_t red[kAttnThreads / 64];
+
+  const int64_t G = a.G, S = a.S;
+  const int64_t nqb = (S + kBQ - 1) / kBQ;
+  const int64_t g = blockIdx.x % G;
+  const int64_t qb = a.causal ? nqb - 1 - (int64_t)blockIdx.x / G : (int64_t)blockIdx.x / G;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int64_t q0 = qb * kBQ;
+  const int64_t qw0 = q0 + w * 32;
+  const int64_t qc = qw0 + l32 < S ? qw0 + l32 : S - 1;   // this lane's A-operand row, clamped
+
+  // ---- the wave's Q (FP16) and dO fragments, A operands -------------------
+  f16x8_t qf[KSTEPS];
+  bf16x8_t df[KSTEPS];
+  {
+    const uint8_t *qrow = a.q_codes + (g * S + qc) * (D / 2);
+    const uint8_t *qsc = a.q_scales + (g * S + qc) * (D / 16);
+    const uint16_t *drow = a.dout + (g * S + qc) * D;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      qf[t] = expand8(*(const uint32_t *)(qrow + 8 * t + 4 * h), split_scale(qsc[t]));   // d = 16t + 8h .. +8
+      df[t] = *(const bf16x8_t *)(drow + 16 * t + 8 * h);
+    }
+  }
+  if (tid < kBQ) {
+    const int64_t qq = q0 + tid;
+    qv[0][tid] = qq < S ? a.lse[g * S + qq] * kLog2e : 0.0f;
+    qv[1][tid] = qq < S ? a.delta[g * S + qq] : 0.0f;
+  }
+  const float c_log2 = (*a.q_ts) * (*a.k_ts) * a.scale * kLog2e;   // S in log2 units
+
+  // ---- key-block staging: K expanded to FP16, V rows as they are -----------
+  uint4 rk = make_uint4(0, 0, 0, 0), rv[L::kVPer];
+  uint32_t rks = 0;
+  const int krow_s = tid / L::kTpr, kc0 = (tid % L::kTpr) * L::kEpt;
+  auto load_block = [&](int64_t kb) {
+    const int64_t k0 = kb * kAmK;
+    {
+      int64_t key = k0 + krow_s;
+      key = key < S ? key : S - 1;
+      const uint8_t *cp = a.k_codes + (g * S + key) * (D / 2) + kc0 / 2;
+      const uint8_t *sp = a.k_scales + (g * S + key) * (D / 16) + kc0 / 16;
+      if constexpr (L::kEpt == 16) {
+        const uint2 t = *(const uint2 *)cp;
+        rk = make_uint4(t.x, t.y, 0u, 0u);
+        rks = *sp;
+      } else {
+        rk = make_uint4(*(const uint32_t *)cp, 0u, 0u, 0u);   // half of a scale block
+        rks = *sp;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < L::kVPer; ++i) {
+      const int idx = tid + i * kAttnThreads;
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      int64_t key = k0 + row;
+      key = key < S ? key : S - 1;   // rows past S are never visible
+      rv[i] = *(const uint4 *)(a.v + (g * S + key) * D + ch * 8);
+    }
+  };
+  auto store_block = [&](int st) {
+    uint8_t *base = lds + st * L::kStage;
+    _Float16 *kh = (_Float16 *)base + krow_s * L::kKh + kc0;
+    const uint32_t cw[4] = {rk.x, rk.y, rk.z, rk.w};
+#pragma unroll
+    for (int j = 0; j < L::kEpt / 8; ++j)
+      *(f16x8_t *)(kh + 8 * j) = expand8(cw[j], split_scale(rks & 0xFFu));   // one scale block
+#pragma unroll
+    for (int i = 0; i < L::kVPer; ++i) {
+      const int idx = tid + i * kAttnThreads;
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      *(uint4 *)(base + L::kKhBytes + (row * L::kVr + ch * 8) * 2) = rv[i];
+    }
+  };
+
+  const int64_t nkb_all = (S + kAmK - 1) / kAmK;
+  const int64_t nkb = (a.causal && !KEEP) ? ((q0 + kBQ < S ? q0 + kBQ : S) + kAmK - 1) / kAmK : nkb_all;
+  float amax = 0.0f;
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) load_block(kb + 1);
+    const int64_t k0 = kb * kAmK;
+    const bool live = !a.causal || k0 <= qw0 + 31 || KEEP;   // wave-uniform
+    if (live) {
+      const uint8_t *base = lds + (int)(kb & 1) * L::kStage;
+      const _Float16 *kh = (const _Float16 *)base;
+      const uint16_t *vr = (const uint16_t *)(base + L::kKhBytes);
+#pragma unroll
+      for (int kt = 0; kt < kAmK / 32; ++kt) {
+        floatx16_t sacc, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sacc[e] = 0.0f;
+          dp[e] = 0.0f;
+        }
+        const int kr = kt * 32 + l32;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[t], *(const f16x8_t *)(kh + kr * L::kKh + 16 * t + 8 * h),
+                                                         sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // (the fragments of one product at a time in registers)
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df[t], *(const bf16x8_t *)(vr + kr * L::kVr + 16 * t + 8 * h),
+                                                        dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // register e holds query qw0 + 8 (e/4) + 4 h + e%4 of key `key`
+        const int64_t key = k0 + kr;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int qi = 32 * w + 8 * c + 4 * h;
+          const float4 l4 = *(const float4 *)(&qv[0][qi]);
+          const float4 d4 = *(const float4 *)(&qv[1][qi]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * c + r;
+            const int64_t query = qw0 + 8 * c + 4 * h + r;
+            const bool valid = key < S && query < S && (!a.causal || key <= query);
+            const float p = valid ? __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[r]) : 0.0f;
+            const float dsv = valid ? p * (dp[e] - dl[r]) : 0.0f;
+            amax = fmaxf(amax, fabsf(dsv));
+            if constexpr (KEEP) {
+              if (key < S && query < S) a.ds[(g * S + query) * S + key] = dsv;
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one 32-key tile at a time
+      }
+    }
+    if (kb + 1 < nkb) store_block((int)((kb + 1) & 1));
+    __syncthreads();
+  }
+
   uint32_t m = __builtin_bit_cast(uint32_t, amax);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -1077,6 +1223,7 @@ size_t attention_bwd_ws_bytes(int64_t G, int64_t S, int64_t D) {
 AttnBwdWs attention_bwd_carve(Carver &c, int64_t G, int64_t S, int64_t D) {
   AttnBwdWs w;
   w.delta = (float *)c.take((size_t)(G * S) * 4);
+  static_assert(kBwdKeys == kBQ, "one amax partial per 128 queries and per 128 keys alike");
   w.nwg = G * ((S + kBwdKeys - 1) / kBwdKeys);
   w.amax = (uint32_t *)c.take((size_t)w.nwg * 4);
   w.ds_row = carve_view(c, G * S, S);
@@ -1095,12 +1242,30 @@ fs4_status launch_attention_bwd(const fs4_nvfp4 &Qr, const fs4_nvfp4 &Kr, const 
   if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
 
   const float scale = (float)(1.0 / __builtin_sqrt((double)D));
-  // first pass over the keys: dV, the amax of dS (and dS when asked for)
+  // the amax of dS (and dS when asked for), query-major
+  AttnAmaxArgs x;
+  x.q_codes = Qr.codes; x.q_scales = Qr.scales; x.k_codes = Kr.codes; x.k_scales = Kr.scales;
+  x.q_ts = Qr.tscale; x.k_ts = Kr.tscale;
+  x.v = V; x.dout = dO; x.lse = LSE; x.delta = w.delta;
+  x.ds = dS; x.amax = w.amax;
+  x.G = G; x.S = S;
+  x.scale = scale;
+  x.causal = causal;
+  const unsigned xgrid = (unsigned)(G * ((S + kBQ - 1) / kBQ));   // == w.nwg (128 rows either way)
+  if (dS) {
+    if (D == 128) attention_amax_kernel<128, true><<<xgrid, kAttnThreads, 0, s>>>(x);
+    else attention_amax_kernel<64, true><<<xgrid, kAttnThreads, 0, s>>>(x);
+  } else {
+    if (D == 128) attention_amax_kernel<128, false><<<xgrid, kAttnThreads, 0, s>>>(x);
+    else attention_amax_kernel<64, false><<<xgrid, kAttnThreads, 0, s>>>(x);
+  }
+  if (hipGetLastError() != hipSuccess) return FS4_ERR_HIP;
+
+  // first pass over the keys: dV = P^T dO
   AttnBwdArgs a;
   a.q_codes = Qr.codes; a.q_scales = Qr.scales; a.k_codes = Kr.codes; a.k_scales = Kr.scales;
   a.q_ts = Qr.tscale; a.k_ts = Kr.tscale;
-  a.v = V; a.dout = dO; a.lse = LSE; a.delta = w.delta;
-  a.ds = dS; a.dv = dV; a.amax = w.amax;
+  a.dout = dO; a.lse = LSE; a.dv = dV;
   a.G = G; a.S = S;
   a.scale = scale;
   a.causal = causal;
