@@ -411,15 +411,17 @@ fs4_status fs4_linear_bwd(const void *dY, int64_t M, int64_t N, int64_t K, const
     // run along n); this pass reads all of dY, so it also yields dY's amax
     // partials for the quantizer when they fit.  With dual, the same pass
     // forms dU[n][j] = beta sum_m dY[m][n] T[m][j].
-    FS4_TRY(launch_transpose_rank((const uint16_t *)U, N, r, w.Ut, s));
     const int64_t nwg = dual ? dualred_workgroups(M, N) : rowred_workgroups(M, N);
     const bool fuse = nwg <= kAmaxPartials;
-    if (dual)
-      FS4_TRY(launch_dualred((const uint16_t *)dY, w.Ut, T, M, N, r, 1.0f, w.P, beta, dU,
-                             w.partials, w.bt, fuse ? w.qws : nullptr, s));
-    else
+    if (dual) {
+      // (its last launch leaves P's BF16 split in w.bt for the dV pass)
+      FS4_TRY(launch_dualred((const uint16_t *)dY, (const uint16_t *)U, w.Ut, T, M, N, r, 1.0f, w.P, beta, dU,
+                             w.partials, w.bt, fuse ? w.qws : nullptr, dV ? w.bt : nullptr, s));
+    } else {
+      FS4_TRY(launch_transpose_rank((const uint16_t *)U, N, r, w.Ut, s));
       FS4_TRY(launch_rowred((const uint16_t *)dY, w.Ut, M, r, N, 1.0f, w.P, w.partials,
                             fuse ? w.qws : nullptr, s));
+    }
     if (fuse)
       FS4_TRY(launch_quantize_encode(dY, FS4_BF16, M, N, &w.dy_row, &w.dy_col, w.qws, (int)nwg, s));
     else
@@ -442,7 +444,7 @@ fs4_status fs4_linear_bwd(const void *dY, int64_t M, int64_t N, int64_t K, const
   }
   if (r > 0 && dV) {
     // dV[j][k] = beta sum_m P[m][j] X[m][k]
-    FS4_TRY(launch_colred((const uint16_t *)X, w.P, M, K, r, beta, dV, true, w.partials, w.bt, s));
+    FS4_TRY(launch_colred((const uint16_t *)X, w.P, M, K, r, beta, dV, true, w.partials, w.bt, s, dual));
   }
   return FS4_OK;
 }

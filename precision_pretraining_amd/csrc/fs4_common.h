@@ -213,18 +213,23 @@ fs4_status launch_rowred(const uint16_t *A, const uint16_t *B, int64_t Na, int r
 size_t colred_partials_bytes(int64_t M, int64_t C, int r);
 fs4_status launch_colred(const uint16_t *A, const float *Bm, int64_t M, int64_t C, int r,
                          float scale, float *out, bool transpose_out, float *partials,
-                         uint16_t *bt, hipStream_t s);
+                         uint16_t *bt, hipStream_t s, bool presplit = false);
+//           (presplit: bt already holds Bm's split, as launch_dualred's
+//           p_split leaves it; Bm is not read)
 //   dualred: both of A's rank-r contractions in one read of A bf16 [M][N]
-//           (r <= 32; M, N % 8 == 0; M N, M r < 2^30): P[m][j] = p_scale sum_n A[m][n] B[j][n]
-//           with B bf16 [r][N], and Q[n][j] = q_scale sum_m A[m][n] Bm[m][j]
-//           with Bm fp32 [M][r]; `partials` needs dualred_partials_bytes,
-//           `bt` 2 * M * r BF16; optional amax partials of A
-//           (dualred_workgroups of them).
+//           (r <= 32; M, N % 8 == 0; M N, M r < 2^30): P[m][j] = p_scale sum_n A[m][n] U[n][j]
+//           with U bf16 [N][r] (transposed into Ut, N r BF16 of scratch),
+//           and Q[n][j] = q_scale sum_m A[m][n] Bm[m][j] with Bm fp32 [M][r];
+//           `partials` needs dualred_partials_bytes, `bt` 2 * M * r BF16;
+//           optional amax partials of A (dualred_workgroups of them);
+//           p_split (nullable, 2 * M * r BF16, may be bt) receives P's
+//           transposed BF16 hi/lo split for launch_colred(presplit).
 size_t dualred_partials_bytes(int64_t M, int64_t N, int r);
 int64_t dualred_workgroups(int64_t M, int64_t N);
-fs4_status launch_dualred(const uint16_t *A, const uint16_t *B, const float *Bm, int64_t M,
+fs4_status launch_dualred(const uint16_t *A, const uint16_t *U, uint16_t *Ut, const float *Bm, int64_t M,
                           int64_t N, int r, float p_scale, float *P, float q_scale, float *Q,
-                          float *partials, uint16_t *bt, uint32_t *amax_parts, hipStream_t s);
+                          float *partials, uint16_t *bt, uint32_t *amax_parts, uint16_t *p_split,
+                          hipStream_t s);
 fs4_status launch_transpose_rank(const uint16_t *U, int64_t N, int r, uint16_t *Ut, hipStream_t s);
 // Frobenius normalisation X = G / (||G||_F + eps), fp64 accumulation
 size_t normalize_ws_bytes();

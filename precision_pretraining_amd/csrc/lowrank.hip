@@ -171,13 +171,9 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallGemm g, uint32_t *
   }
 }
 
-__global__ void reduce_partials_kernel(const float *__restrict__ partials, int S, int64_t Na,
-                                       int64_t Nb, float scale, float *__restrict__ out,
-                                       bool transpose_out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= Na * Nb) return;
-  // (unrolled so that eight loads are in flight; the sum order stays p = 0, 1, ..)
-  const int64_t stride = Na * Nb;
+// sum over p = 0, 1, .., S - 1 (in that order) of partials[p * stride + i],
+// unrolled so that eight loads are in flight
+__device__ inline float sum_slots(const float *__restrict__ partials, int S, int64_t stride, int64_t i) {
   float s = 0.0f;
   int p = 0;
   for (; p + 8 <= S; p += 8) {
@@ -188,8 +184,24 @@ __global__ void reduce_partials_kernel(const float *__restrict__ partials, int S
     for (int q = 0; q < 8; ++q) s += v[q];
   }
   for (; p < S; ++p) s += partials[(int64_t)p * stride + i];
+  return s;
+}
+
+__global__ void reduce_partials_kernel(const float *__restrict__ partials, int S, int64_t Na,
+                                       int64_t Nb, float scale, float *__restrict__ out,
+                                       bool transpose_out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Na * Nb) return;
+  const float s = sum_slots(partials, S, Na * Nb, i);
   const int64_t ra = i / Nb, cb = i % Nb;
   out[transpose_out ? cb * Na + ra : i] = scale * s;
+}
+
+// x = hi + lo as BF16 parts (x - hi rounded to BF16; |lo| <= 2^-9 |x|)
+__device__ inline void split_bf16(float x, uint16_t *hi, uint16_t *lo) {
+  const uint32_t hb = float_to_bf16_rne_bits(x);
+  *hi = (uint16_t)hb;
+  *lo = (uint16_t)float_to_bf16_rne_bits(x - bf16_bits_to_float(hb));
 }
 
 constexpr int64_t kChunkMin = 64;
@@ -464,10 +476,7 @@ __global__ void split_transpose_kernel(const float *__restrict__ Bm, int64_t M, 
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= M * r) return;
   const int64_t j = i / M, m = i % M;
-  const float x = Bm[m * r + j];
-  const uint32_t hb = float_to_bf16_rne_bits(x);
-  hi[i] = (uint16_t)hb;
-  lo[i] = (uint16_t)float_to_bf16_rne_bits(x - bf16_bits_to_float(hb));
+  split_bf16(Bm[m * r + j], hi + i, lo + i);
 }
 
 // U [N][r] -> U^T [r][N] (bf16)
@@ -477,6 +486,48 @@ __global__ void transpose_rank_kernel(const uint16_t *__restrict__ U, int64_t N,
   if (i >= N * r) return;
   const int64_t j = i / N, n = i % N;
   Ut[i] = U[n * r + j];
+}
+
+// The operand preparation of the dual pass in one launch: U [N][r] -> U^T
+// [r][N] (bf16, the first N r threads) and Bm fp32 [M][r] -> its transposed
+// BF16 hi/lo split [r][M] (the next M r).
+__global__ void rank_prep_kernel(const uint16_t *__restrict__ U, int64_t N, int r, uint16_t *__restrict__ Ut,
+                                 const float *__restrict__ Bm, int64_t M, uint16_t *__restrict__ hi,
+                                 uint16_t *__restrict__ lo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nu = N * r;
+  if (i < nu) {
+    const int64_t j = i / N, n = i % N;
+    Ut[i] = U[n * r + j];
+    return;
+  }
+  const int64_t k = i - nu;
+  if (k >= M * r) return;
+  const int64_t j = k / M, m = k % M;
+  split_bf16(Bm[m * r + j], hi + k, lo + k);
+}
+
+// Both reductions of the dual pass in one launch, each in slot order:
+// P[m][j] = p_scale sum over its cb slots (the first M r threads), with
+// P's transposed BF16 hi/lo split [r][M] when p_hi is given (the operand of
+// the later column pass over X), and Q[n][j] = q_scale sum over its rb
+// slots (the next N r).
+__global__ void dual_reduce_kernel(const float *__restrict__ ppart, int cb, int64_t M, float p_scale,
+                                   float *__restrict__ P, uint16_t *__restrict__ p_hi, uint16_t *__restrict__ p_lo,
+                                   const float *__restrict__ qpart, int rb, int64_t N, float q_scale,
+                                   float *__restrict__ Q, int r) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, np = M * r;
+  if (i < np) {
+    const float v = p_scale * sum_slots(ppart, cb, np, i);
+    P[i] = v;
+    if (p_hi) {
+      const int64_t m = i / r, j = i % r;
+      split_bf16(v, p_hi + j * M + m, p_lo + j * M + m);
+    }
+    return;
+  }
+  const int64_t k = i - np;
+  if (k >= N * r) return;
+  Q[k] = q_scale * sum_slots(qpart, rb, N * r, k);
 }
 
 // dualred: both rank-r contractions of one bf16 matrix A [M][N] in a single
@@ -730,11 +781,11 @@ size_t colred_partials_bytes(int64_t M, int64_t C, int r) {
 }
 fs4_status launch_colred(const uint16_t *A, const float *Bm, int64_t M, int64_t C, int r,
                          float scale, float *out, bool transpose_out, float *partials,
-                         uint16_t *bt, hipStream_t s) {
+                         uint16_t *bt, hipStream_t s, bool presplit) {
   if (C == 0 || r == 0) return FS4_OK;
   uint16_t *bt_hi = bt, *bt_lo = bt + M * r;
   const int64_t nb = M * r;
-  split_transpose_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, s>>>(Bm, M, r, bt_hi, bt_lo);
+  if (!presplit) split_transpose_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, s>>>(Bm, M, r, bt_hi, bt_lo);
   int64_t mc;
   const int64_t S = colred_splits(M, C, &mc);
   dim3 grid((unsigned)((C + kColBlock - 1) / kColBlock), (unsigned)S);
@@ -752,23 +803,24 @@ size_t dualred_partials_bytes(int64_t M, int64_t N, int r) {
 int64_t dualred_workgroups(int64_t M, int64_t N) {
   return ((N + kDrCols - 1) / kDrCols) * ((M + kDrRows - 1) / kDrRows);
 }
-fs4_status launch_dualred(const uint16_t *A, const uint16_t *B, const float *Bm, int64_t M,
+fs4_status launch_dualred(const uint16_t *A, const uint16_t *U, uint16_t *Ut, const float *Bm, int64_t M,
                           int64_t N, int r, float p_scale, float *P, float q_scale, float *Q,
-                          float *partials, uint16_t *bt, uint32_t *amax_parts, hipStream_t s) {
+                          float *partials, uint16_t *bt, uint32_t *amax_parts, uint16_t *p_split,
+                          hipStream_t s) {
   if (M == 0 || N == 0 || r == 0) return FS4_OK;
   if (r > 32) return FS4_ERR_RANK;
   if (M * N >= ((int64_t)1 << 30) || M * r >= ((int64_t)1 << 30)) return FS4_ERR_SHAPE;   // 32-bit buffer offsets
   uint16_t *bt_hi = bt, *bt_lo = bt + M * r;
-  const int64_t nb = M * r;
-  split_transpose_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, s>>>(Bm, M, r, bt_hi, bt_lo);
+  const int64_t nprep = (N + M) * r;
+  rank_prep_kernel<<<(unsigned)((nprep + 255) / 256), 256, 0, s>>>(U, N, r, Ut, Bm, M, bt_hi, bt_lo);
   const int64_t cb = (N + kDrCols - 1) / kDrCols, rb = (M + kDrRows - 1) / kDrRows;
   float *ppart = partials, *qpart = partials + cb * M * r;
-  dualred_kernel<<<dim3((unsigned)cb, (unsigned)rb), kDrThreads, 0, s>>>(A, B, bt_hi, bt_lo, M, N, r,
+  dualred_kernel<<<dim3((unsigned)cb, (unsigned)rb), kDrThreads, 0, s>>>(A, Ut, bt_hi, bt_lo, M, N, r,
                                                                        ppart, qpart, amax_parts);
-  reduce_partials_kernel<<<(unsigned)((M * r + 255) / 256), 256, 0, s>>>(ppart, (int)cb, M, r,
-                                                                          p_scale, P, false);
-  reduce_partials_kernel<<<(unsigned)((N * r + 255) / 256), 256, 0, s>>>(qpart, (int)rb, N, r,
-                                                                          q_scale, Q, false);
+  // (the dual pass has read bt; p_split may be the same buffer)
+  const int64_t nred = (M + N) * r;
+  dual_reduce_kernel<<<(unsigned)((nred + 255) / 256), 256, 0, s>>>(
+      ppart, (int)cb, M, p_scale, P, p_split, p_split ? p_split + M * r : nullptr, qpart, (int)rb, N, q_scale, Q, r);
   return hipGetLastError() == hipSuccess ? FS4_OK : FS4_ERR_HIP;
 }
 fs4_status launch_transpose_rank(const uint16_t *U, int64_t N, int r, uint16_t *Ut, hipStream_t s) {
