@@ -547,12 +547,17 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
     } else {
       FS4_TRY(quantize(cur, n, m, &w.x_col, &w.x_row));
     }
+    // Unless traced, A and B keep only their upper triangle's tiles: the
+    // quantizer reads those and writes each lower block from its mirror
+    // image, and the A^2 product reads its bA term where it stores.
     FS4_TRY(launch_gemm_nt(w.x_row, w.x_row, 1.0f, nullptr, 0.0f, A, LowRankEpilogue(), s, w.amax, &np, true,
-                           w.split, w.split_floats));
-    FS4_TRY(quantize(A, m, m, &w.a_row, nullptr));
+                           w.split, w.split_floats, trace_A != nullptr));
+    if (trace_A) FS4_TRY(quantize(A, m, m, &w.a_row, nullptr));
+    else FS4_TRY(launch_quantize_encode(A, FS4_FP32, m, m, &w.a_row, nullptr, w.amax, np, s, nullptr, true));
     FS4_TRY(launch_gemm_nt(w.a_row, w.a_row, c, A, b, B, LowRankEpilogue(), s, w.amax, &np, true, w.split,
-                           w.split_floats));
-    FS4_TRY(quantize(B, m, m, &w.b_row, nullptr));
+                           w.split_floats, trace_B != nullptr));
+    if (trace_B) FS4_TRY(quantize(B, m, m, &w.b_row, nullptr));
+    else FS4_TRY(launch_quantize_encode(B, FS4_FP32, m, m, &w.b_row, nullptr, w.amax, np, s, nullptr, true));
     FS4_TRY(launch_gemm_nt(w.x_col, w.b_row, 1.0f, cur, a, next, LowRankEpilogue(), s, w.amax, &np, false,
                            w.split, w.split_floats));
     cur = next;

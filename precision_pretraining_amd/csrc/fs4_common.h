@@ -103,11 +103,15 @@ fs4_status launch_quantize(const void *x, fs4_dtype dt, int64_t rows, int64_t co
 // The encode pass alone, for a caller whose earlier kernel already wrote npart
 // (npart >= 1) partial maxima of |x| (fp32 bits) that cover all of x.  With
 // clip (a device scalar p >= 0), x is clipped to magnitude p first and p is
-// its amax (the partials are not read).
+// its amax (the partials are not read).  upper_only: x is square and
+// symmetric and only its 64 x 64 tiles on or above the diagonal hold values
+// (the others are not read); the row-wise view alone is produced, the lower
+// tiles' blocks from their mirror images (identical values, so identical
+// codes).
 fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                                   const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                                   const uint32_t *partials, int npart, hipStream_t s,
-                                  const float *clip = nullptr);
+                                  const float *clip = nullptr, bool upper_only = false);
 // *out = the k-th smallest |x| of x[0..n) (bf16 or fp32), k = ceil(q n) in
 // fp64 clamped to [1, n], by exact radix selection; ws needs
 // abs_quantile_ws_bytes().  n >= 1.
@@ -181,7 +185,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, bool can_split, in
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
                           float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
                           uint32_t *amax_parts = nullptr, int *nwg = nullptr, bool sym = false,
-                          float *split_ws = nullptr, int64_t split_floats = 0);
+                          float *split_ws = nullptr, int64_t split_floats = 0, bool mirror = true);
+// (mirror = false with sym: the tiles below the diagonal are not stored; C
+// holds the upper triangle's tiles only)
 // one round of 256 workgroups of split partials, 256 x 256 floats each
 constexpr int64_t kGemmSplitFloats = int64_t(256) * 256 * 256;
 inline int64_t gemm_max_workgroups(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }

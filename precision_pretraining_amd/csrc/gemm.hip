@@ -74,6 +74,7 @@ struct GemmArgs {
   // sym: C is symmetric (A and B the same view): only tiles with
   // tile_m <= tile_n are computed, each stored at both positions.
   int sym;
+  int mirror;   // with sym: store each tile at its mirrored position too
   // Split-k: tiles [0, t_full) run whole, one workgroup each; every later
   // tile runs as s_tail workgroups over consecutive ranges of whole k-tiles,
   // which store their raw fp32 accumulators to `part` (slot (tile - t_full)
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
           }
         }
       }
-      if (g.sym && tile_m != tile_n) {
+      if (g.sym && g.mirror && tile_m != tile_n) {
         // C[n][m] = C[m][n]: this lane's column n becomes a row, its rows m
         // (four runs of four) become 16-byte pieces of that row
         const int64_t n = n0 + brow;
@@ -807,7 +808,7 @@ __global__ __launch_bounds__(kSplitReduceThreads) void split_reduce_kernel(GemmA
           amax = fmaxf(amax, fabsf(v[c]));
         }
     }
-    if (g.sym && tile_m != tile_n) {
+    if (g.sym && g.mirror && tile_m != tile_n) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         if (n + c < g.M && m < g.N) g.C[(n + c) * g.N + m] = v[c];
@@ -913,8 +914,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, bool can_split, in
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
                           float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
                           uint32_t *amax_parts, int *nwg, bool sym, float *split_ws,
-                          int64_t split_floats) {
+                          int64_t split_floats, bool mirror) {
   GemmArgs g;
+  g.mirror = mirror ? 1 : 0;
   g.t_full = 0;
   g.s_tail = 1;
   g.part = split_ws;

@@ -181,7 +181,9 @@ struct TileOrder {
   int tiles_r, tiles_c, sct, n_st;   // tile grid, super-tile columns and count
   int sub_r, sub_c;                  // this workgroup's tile inside a super-tile
   int d_r, d_c;                      // per-step advance in super-tile rows / columns
-  __device__ TileOrder(int64_t rows, int64_t cols) {
+  int upper;                         // only tiles on or above the diagonal
+  __device__ TileOrder(int64_t rows, int64_t cols, int upper_only) {
+    upper = upper_only;
     tiles_r = (int)((rows + kTile - 1) / kTile);
     tiles_c = (int)((cols + kTile - 1) / kTile);
     sct = (tiles_c + 3) / 4;
@@ -197,7 +199,8 @@ struct TileOrder {
   // (sr, sc) forward to the first super-tile whose sub-tile lies inside.
   __device__ bool seek(int &sr, int &sc) const {
     while (sr * sct + sc < n_st) {
-      if (sr * 4 + sub_r < tiles_r && sc * 4 + sub_c < tiles_c) return true;
+      if (sr * 4 + sub_r < tiles_r && sc * 4 + sub_c < tiles_c && (!upper || sr * 4 + sub_r <= sc * 4 + sub_c))
+        return true;
       advance(sr, sc);
     }
     return false;
@@ -221,13 +224,16 @@ struct TileOrder {
 };
 
 // With CLIP, *clip replaces the tensor amax and every element is clipped to
-// magnitude *clip before it is encoded (the partials are not read).
+// magnitude *clip before it is encoded (the partials are not read).  With
+// upper_only (a symmetric square x, cv the same view as rv), only the tiles
+// on or above the diagonal are read: a tile's column blocks are the row
+// blocks of its mirror image, and go there.
 template <bool BF16, bool ROW, bool COL, bool CLIP = false>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restrict__ x, int64_t rows,
                                                             int64_t cols,
                                                             const uint32_t *__restrict__ partials,
                                                             int npart, fs4_nvfp4 rv, fs4_nvfp4 cv,
-                                                            const float *clip = nullptr) {
+                                                            const float *clip = nullptr, int upper_only = 0) {
   __shared__ float tile[kTile][kTile + 1];
   __shared__ Tables tab;
   __shared__ uint32_t red[kThreads / 64];
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
     if (COL) *cv.tscale = s_t;
   }
   // the first two tiles' loads overlap the table construction
-  const TileOrder order(rows, cols);
+  const TileOrder order(rows, cols, upper_only);
   int sr, sc;
   order.start(sr, sc);
   int have = order.seek(sr, sc) ? 1 : 0;   // int flags stay in scalar registers
@@ -328,10 +334,13 @@ size_t quantize_ws_bytes() { return kAmaxPartials * sizeof(uint32_t); }
 fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int64_t cols,
                                   const fs4_nvfp4 *rowwise, const fs4_nvfp4 *colwise,
                                   const uint32_t *partials, int npart, hipStream_t s,
-                                  const float *clip) {
+                                  const float *clip, bool upper_only) {
   const fs4_nvfp4 none = {nullptr, nullptr, nullptr, 0, 0};
+  if (upper_only && (rows != cols || !rowwise || colwise || clip)) return FS4_ERR_ARG;
   const fs4_nvfp4 rv = rowwise ? *rowwise : none;
-  const fs4_nvfp4 cv = colwise ? *colwise : none;
+  // a square view's column blocks land at its mirrored row blocks: the same
+  // addresses as in a column-wise view of the same shape
+  const fs4_nvfp4 cv = upper_only ? *rowwise : (colwise ? *colwise : none);
   const bool bf16 = dt == FS4_BF16;
   // one workgroup per tile slot (4 x 4 tiles per super-tile), at most the cap
   const int64_t slots = ((rows + 4 * kTile - 1) / (4 * kTile)) * ((cols + 4 * kTile - 1) / (4 * kTile)) * 16;
@@ -345,7 +354,8 @@ fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int
     if (clip)                                                                                      \
       quantize_kernel<B, R, C, true><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv, clip); \
     else                                                                                           \
-      quantize_kernel<B, R, C><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv);  \
+      quantize_kernel<B, R, C><<<grid, kThreads, 0, s>>>(x, rows, cols, partials, npart, rv, cv, nullptr, \
+                                                          upper_only ? 1 : 0);                     \
   } while (0)
   if (bf16) {
     if (row && col) FS4_QK(true, true, true);

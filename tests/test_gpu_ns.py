@@ -98,3 +98,20 @@ def test_full_size_first_product_sampled():
         assert abs(A0[i, j].item() - ref) <= TOL * den
     assert torch.equal(X, tX[5])
     assert torch.isfinite(X).all()
+
+
+@pytest.mark.parametrize("m,n,clip", [(208, 512, 0.0), (768, 2048, 0.0), (3072, 8192, 0.0), (208, 512, 0.99)])
+def test_upper_triangle_path_equals_traced_path(m, n, clip):
+    """Untraced, A and B keep only their upper triangle's tiles and the
+    quantizer writes each lower block from its mirror image; traced, both
+    are stored whole and quantized whole.  A and B are exactly symmetric, so
+    the codes, and every iterate, must agree bit for bit (208 leaves partial
+    64 x 64 and 128 x 128 tiles on the diagonal)."""
+    fs4 = need_gpu()
+    print_case(test="ns_upper_vs_traced", m=m, n=n, clip=clip)
+    G = dev_bf16(synth.ns_input(seed=9, m=m, n=n))
+    X1 = fs4.newton_schulz(G, steps=5, clip_q=clip).cpu().numpy()
+    X2, tX, tA, tB = fs4.newton_schulz(G, steps=5, trace=True, clip_q=clip)
+    assert np.array_equal(X1.view(np.uint32), X2.cpu().numpy().view(np.uint32))
+    A = tA.cpu().numpy()
+    assert np.array_equal(A, np.transpose(A, (0, 2, 1)))
