@@ -504,21 +504,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_bwd_kernel(AttnBwdA
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8_t *)(qh + r * L::kQh + 16 * t + 8 * h), kf[t],
                                                          sacc, 0, 0, 0);
       }
-      // register e holds query q0 + 32 qt + 8 (e/4) + 4 h + e%4 of key `key`
+      // register e holds query q0 + 32 qt + 8 (e/4) + 4 h + e%4 of key `key`;
+      // a tile wholly in range and below a causal diagonal needs no masks
+      auto form_p = [&](auto masked) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int qi = 32 * qt + 8 * c + 4 * h;
-        const float4 l4 = *(const float4 *)(lse2 + qi);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        for (int c = 0; c < 4; ++c) {
+          const int qi = 32 * qt + 8 * c + 4 * h;
+          const float4 l4 = *(const float4 *)(lse2 + qi);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * c + r;
-          const int64_t query = q0 + qi + r;
-          const bool valid = key_ok && query < S && (!a.causal || key <= query);
-          const float p = valid ? __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[r]) : 0.0f;
-          pb[qt][e >> 3][e & 7] = (__bf16)p;
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * c + r;
+            float p = __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[r]);
+            if constexpr (decltype(masked)::value) {
+              const int64_t query = q0 + qi + r;
+              const bool valid = key_ok && query < S && (!a.causal || key <= query);
+              p = valid ? p : 0.0f;
+            }
+            pb[qt][e >> 3][e & 7] = (__bf16)p;
+          }
         }
-      }
+      };
+      if (qt0 + 31 < S && kw0 + 31 < S && (!a.causal || kw0 + 31 <= qt0)) form_p(std::false_type{});
+      else form_p(std::true_type{});
     }
     // ---- dV^T += dO^T P, queries in the registers' order ---------------------
 #pragma unroll
@@ -710,27 +718,36 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_amax_kernel(AttnAma
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df[t], *(const bf16x8_t *)(vr + kr * L::kVr + 16 * t + 8 * h),
                                                         dp, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // register e holds query qw0 + 8 (e/4) + 4 h + e%4 of key `key`
+        // register e holds query qw0 + 8 (e/4) + 4 h + e%4 of key `key`; a
+        // tile wholly in range and below a causal diagonal needs no masks
         const int64_t key = k0 + kr;
+        auto form_ds = [&](auto masked) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int qi = 32 * w + 8 * c + 4 * h;
-          const float4 l4 = *(const float4 *)(&qv[0][qi]);
-          const float4 d4 = *(const float4 *)(&qv[1][qi]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+          for (int c = 0; c < 4; ++c) {
+            const int qi = 32 * w + 8 * c + 4 * h;
+            const float4 l4 = *(const float4 *)(&qv[0][qi]);
+            const float4 d4 = *(const float4 *)(&qv[1][qi]);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 4 * c + r;
-            const int64_t query = qw0 + 8 * c + 4 * h + r;
-            const bool valid = key < S && query < S && (!a.causal || key <= query);
-            const float p = valid ? __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[r]) : 0.0f;
-            const float dsv = valid ? p * (dp[e] - dl[r]) : 0.0f;
-            amax = fmaxf(amax, fabsf(dsv));
-            if constexpr (KEEP) {
-              if (key < S && query < S) a.ds[(g * S + query) * S + key] = dsv;
+            for (int r = 0; r < 4; ++r) {
+              const int e = 4 * c + r;
+              const int64_t query = qw0 + 8 * c + 4 * h + r;
+              const float p = __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[r]);
+              float dsv = p * (dp[e] - dl[r]);
+              if constexpr (decltype(masked)::value) {
+                const bool valid = key < S && query < S && (!a.causal || key <= query);
+                dsv = valid ? dsv : 0.0f;
+              }
+              amax = fmaxf(amax, fabsf(dsv));
+              if constexpr (KEEP) {
+                if (key < S && query < S) a.ds[(g * S + query) * S + key] = dsv;
+              }
             }
           }
-        }
+        };
+        const int64_t kt0 = k0 + kt * 32;
+        if (!KEEP && qw0 + 31 < S && kt0 + 31 < S && (!a.causal || kt0 + 31 <= qw0)) form_ds(std::false_type{});
+        else form_ds(std::true_type{});
         __builtin_amdgcn_sched_barrier(0);   // one 32-key tile at a time
       }
     }
@@ -938,22 +955,31 @@ __global__ __launch_bounds__(kAttnThreads) void attention_dsq_kernel(AttnDsqArgs
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(dor + r * L::kDo + 16 * t + 8 * h), vf[t],
                                                       dp, 0, 0, 0);
       // dS exactly as the first pass forms it; the tile goes to the scratch
-      // as [key][query]
+      // as [key][query].  A tile with every (key, query) in range and, when
+      // causal, wholly below the diagonal needs no masks (wave-uniform).
+      auto form_ds = [&](auto masked) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int qi = 32 * qt + 8 * c + 4 * h;
-        const float4 l4 = *(const float4 *)(lse2 + qi);
-        const float4 d4 = *(const float4 *)(dlt + qi);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int c = 0; c < 4; ++c) {
+          const int qi = 32 * qt + 8 * c + 4 * h;
+          const float4 l4 = *(const float4 *)(lse2 + qi);
+          const float4 d4 = *(const float4 *)(dlt + qi);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int e = 4 * c + rr;
-          const int64_t query = q0 + qi + rr;
-          const bool valid = key_ok && query < S && (!a.causal || key <= query);
-          const float p = valid ? __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[rr]) : 0.0f;
-          sc[l32 * L::kT + 8 * c + 4 * h + rr] = valid ? p * (dp[e] - dv[rr]) : 0.0f;
+          for (int rr = 0; rr < 4; ++rr) {
+            const int e = 4 * c + rr;
+            const float p = __builtin_amdgcn_exp2f(sacc[e] * c_log2 - lv[rr]);
+            float ds = p * (dp[e] - dv[rr]);
+            if constexpr (decltype(masked)::value) {
+              const int64_t query = q0 + qi + rr;
+              const bool valid = key_ok && query < S && (!a.causal || key <= query);
+              ds = valid ? ds : 0.0f;
+            }
+            sc[l32 * L::kT + 8 * c + 4 * h + rr] = ds;
+          }
         }
-      }
+      };
+      if (qt0 + 31 < S && kw0 + 31 < S && (!a.causal || kw0 + 31 <= qt0)) form_ds(std::false_type{});
+      else form_ds(std::true_type{});
       __builtin_amdgcn_wave_barrier();
       // row-wise view: query bi of the tile, keys 16 bh .. 16 bh + 15
       {
