@@ -516,7 +516,11 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
   // the chip better than the m x n one.  Iterate k lives in w.X or X_out,
   // alternating so that the last one is in w.X; X_out and each trace_X[k]
   // get it transposed back.
-  auto slot = [&](int k) -> float * { return ((steps - k) % 2 == 0) ? w.X : X_out; };
+  // Untraced, the last update stores X_steps straight into X_out transposed,
+  // so X_{steps-1} must not live there: iterates then alternate so that
+  // X_{steps-1} is in w.X.
+  const bool direct = steps > 0 && !trace_X;
+  auto slot = [&](int k) -> float * { return ((steps - k - (direct ? 1 : 0)) % 2 == 0) ? w.X : X_out; };
   float *cur = slot(0);
   // Each producer (normalisation, GEMM epilogue) leaves per-workgroup amax
   // partials of its output in w.amax, so each quantization is one encode
@@ -558,6 +562,9 @@ fs4_status fs4_newton_schulz(const void *G, fs4_dtype dt, int64_t m, int64_t n, 
                            w.split_floats, trace_B != nullptr));
     if (trace_B) FS4_TRY(quantize(B, m, m, &w.b_row, nullptr));
     else FS4_TRY(launch_quantize_encode(B, FS4_FP32, m, m, &w.b_row, nullptr, w.amax, np, s, nullptr, true));
+    if (direct && k + 1 == steps)
+      return launch_gemm_nt(w.x_col, w.b_row, 1.0f, cur, a, nullptr, LowRankEpilogue(), s, nullptr, nullptr, false,
+                            nullptr, 0, true, X_out);
     FS4_TRY(launch_gemm_nt(w.x_col, w.b_row, 1.0f, cur, a, next, LowRankEpilogue(), s, w.amax, &np, false,
                            w.split, w.split_floats));
     cur = next;

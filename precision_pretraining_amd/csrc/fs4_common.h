@@ -185,9 +185,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, bool can_split, in
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
                           float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
                           uint32_t *amax_parts = nullptr, int *nwg = nullptr, bool sym = false,
-                          float *split_ws = nullptr, int64_t split_floats = 0, bool mirror = true);
+                          float *split_ws = nullptr, int64_t split_floats = 0, bool mirror = true,
+                          float *Ct = nullptr);
 // (mirror = false with sym: the tiles below the diagonal are not stored; C
-// holds the upper triangle's tiles only)
+// holds the upper triangle's tiles only.  Ct, for a product that is not
+// symmetric and has M % 4 == 0: C is stored transposed there, Ct[n][m], and
+// not at C; the tiles run whole.)
 // one round of 256 workgroups of split partials, 256 x 256 floats each
 constexpr int64_t kGemmSplitFloats = int64_t(256) * 256 * 256;
 inline int64_t gemm_max_workgroups(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }

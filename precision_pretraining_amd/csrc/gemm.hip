@@ -75,6 +75,7 @@ struct GemmArgs {
   // tile_m <= tile_n are computed, each stored at both positions.
   int sym;
   int mirror;   // with sym: store each tile at its mirrored position too
+  float *Ct;    // nullable: C is stored transposed, Ct[n][m] (leading dimension M), instead
   // Split-k: tiles [0, t_full) run whole, one workgroup each; every later
   // tile runs as s_tail workgroups over consecutive ranges of whole k-tiles,
   // which store their raw fp32 accumulators to `part` (slot (tile - t_full)
@@ -688,7 +689,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
         // register e in a scalar register and this lane's offset (rows 4h..,
         // column l32) in a vector register: no per-element address work.
         const int64_t base = (m0 + wm_u * TM * 32 + i * 32) * g.N + n0;
-        const int nrec = (int)((g.M * g.N - base) * 4 < 0x7FFFFFFF ? (g.M * g.N - base) * 4 : 0x7FFFFFFF);
+        // (with Ct the record count is 0: the hardware drops these stores)
+        const int nrec = g.Ct ? 0 : (int)((g.M * g.N - base) * 4 < 0x7FFFFFFF ? (g.M * g.N - base) * 4 : 0x7FFFFFFF);
         const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(g.C + base, 0, nrec, kBufferWord3);
         const int loff = (4 * h * (int)g.N + wn * TN * 32 + j * 32 + l32) * 4;
 #pragma unroll
@@ -709,21 +711,24 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
           if (m < g.M && n < g.N) {
             float v = t[e];
             if (g.E) v += g.beta_e * g.E[m * g.N + n];
-            g.C[m * g.N + n] = v;
+            if (!g.Ct) g.C[m * g.N + n] = v;   // (non-interior tiles only)
             if (g.amax_parts) amax = fmaxf(amax, fabsf(v));
             vv[e] = v;
           }
         }
       }
-      if (g.sym && g.mirror && tile_m != tile_n) {
-        // C[n][m] = C[m][n]: this lane's column n becomes a row, its rows m
-        // (four runs of four) become 16-byte pieces of that row
+      // The transposed store: C^T into Ct, or a symmetric C's mirror image.
+      // This lane's column n becomes a row, its rows m (four runs of four)
+      // become 16-byte pieces of that row (M % 4 == 0; a symmetric C is
+      // square).
+      float *ct = g.Ct ? g.Ct : ((g.sym && g.mirror && tile_m != tile_n) ? g.C : nullptr);
+      if (ct) {
         const int64_t n = n0 + brow;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t m = m0 + wm * TM * 32 + i * 32 + 8 * q + 4 * h;
-          if (n < g.M && m < g.N)
-            *(float4 *)(g.C + n * g.N + m) = make_float4(vv[4 * q], vv[4 * q + 1], vv[4 * q + 2], vv[4 * q + 3]);
+          if (n < g.N && m < g.M)
+            *(float4 *)(ct + n * g.M + m) = make_float4(vv[4 * q], vv[4 * q + 1], vv[4 * q + 2], vv[4 * q + 3]);
         }
       }
     }
@@ -914,9 +919,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, bool can_split, in
 fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, const float *E,
                           float beta_e, float *C, const LowRankEpilogue &lr, hipStream_t s,
                           uint32_t *amax_parts, int *nwg, bool sym, float *split_ws,
-                          int64_t split_floats, bool mirror) {
+                          int64_t split_floats, bool mirror, float *Ct) {
   GemmArgs g;
   g.mirror = mirror ? 1 : 0;
+  g.Ct = Ct;
   g.t_full = 0;
   g.s_tail = 1;
   g.part = split_ws;
@@ -932,7 +938,8 @@ fs4_status launch_gemm_nt(const fs4_nvfp4 &A, const fs4_nvfp4 &B, float alpha, c
   // triangle's tiles, each at both positions; not with a rank-r term
   g.sym = sym && A.codes == B.codes && A.scales == B.scales && g.M == g.N && g.r == 0 ? 1 : 0;
   if (g.M == 0 || g.N == 0) return FS4_OK;
-  const GemmPlan best = plan_gemm(g.M, g.N, g.K, g.sym != 0, split_ws && g.r == 0, split_floats);
+  if (Ct && (g.sym || g.M % 4)) return FS4_ERR_ARG;
+  const GemmPlan best = plan_gemm(g.M, g.N, g.K, g.sym != 0, split_ws && g.r == 0 && !Ct, split_floats);
   if (best.cfg == 0) return launch_cfg<2, 4, 4, 2>(g, best.tiles, best.t_full, best.s_tail, s, nwg);
   if (best.cfg == 1) return launch_cfg<2, 2, 4, 3>(g, best.tiles, best.t_full, best.s_tail, s, nwg);
   return launch_cfg<2, 2, 2, 2>(g, best.tiles, best.t_full, best.s_tail, s, nwg);
