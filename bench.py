@@ -241,7 +241,9 @@ def main():
             fs4.quantize(copies[j % len(copies)], out_row=qrow, out_col=qcol)
             qe[j][1].record(stream)
         torch.cuda.synchronize()
-        q_ms = float(np.mean([s.elapsed_time(e) for s, e in qe]))
+        # median of the per-call intervals: a host stall longer than the
+        # queue-holding spin would otherwise put idle time into one interval
+        q_ms = float(np.median([s.elapsed_time(e) for s, e in qe]))
         q_gbs = quantizer_bytes(rows_q, cols_q) / (q_ms * 1e-3) / 1e9
         hold_queue()
         for j in range(qreps):
@@ -249,7 +251,7 @@ def main():
             fs4.quantize(copies[j % len(copies)], colwise=False, out_row=qrow)
             qe[j][1].record(stream)
         torch.cuda.synchronize()
-        r_ms = float(np.mean([s.elapsed_time(e) for s, e in qe]))
+        r_ms = float(np.median([s.elapsed_time(e) for s, e in qe]))
         r_bytes = quantizer_bytes(rows_q, cols_q, layouts=1)
         return {"workload": "4096x4096 bf16 ~N(0,1), 0.1% x50; row+col layouts",
                 "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
