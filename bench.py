@@ -207,16 +207,17 @@ def main():
         for (A, B), C in zip(shapes, Cs):
             fs4.gemm_nt(A, B, out=C)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * 3)]
-        i = 0
+        # one pair of events around all the launches: an event recorded
+        # between two launches adds a few microseconds of its own to the
+        # interval; the average still holds the gaps between launches
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         for _ in range(reps):
             for (A, B), C in zip(shapes, Cs):
-                ev[i][0].record(stream)
                 fs4.gemm_nt(A, B, out=C)
-                ev[i][1].record(stream)
-                i += 1
+        e1.record(stream)
         torch.cuda.synchronize()
-        gemm_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+        gemm_ms = e0.elapsed_time(e1) / (reps * 3)
         gemm_flop = 2.0 * M * N * K
         ach = gemm_flop / (gemm_ms * 1e-3) / 1e12
         return {"bound": "mfma", "kernel": "gemm_nt_kernel (block-scaled NVFP4 NT GEMM)",
@@ -225,7 +226,24 @@ def main():
                 "per_launch": "8192x8192x3072 = %.1f GFLOP" % (gemm_flop / 1e9),
                 "avg_launch_ms": round(gemm_ms, 4)}
 
-    def quantizer_leg(qreps=48):
+    def grouped_ms(call, groups=8, per_group=6):
+        # events around groups of back-to-back calls, median of the group
+        # means: an event between every two calls adds a few microseconds of
+        # its own per call, and a host stall longer than the queue-holding
+        # spin puts idle time into one group only
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(groups)]
+        hold_queue()
+        j = 0
+        for g in range(groups):
+            ev[g][0].record(stream)
+            for _ in range(per_group):
+                call(j)
+                j += 1
+            ev[g][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([s.elapsed_time(e) / per_group for s, e in ev]))
+
+    def quantizer_leg():
         qb = synth.quantizer_input()
         copies = [to_bf16(qb) for _ in range(12)]
         rows_q, cols_q = qb.shape
@@ -234,24 +252,9 @@ def main():
         for c in copies[:3]:
             fs4.quantize(c, out_row=qrow, out_col=qcol)
         torch.cuda.synchronize()
-        qe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(qreps)]
-        hold_queue()
-        for j in range(qreps):
-            qe[j][0].record(stream)
-            fs4.quantize(copies[j % len(copies)], out_row=qrow, out_col=qcol)
-            qe[j][1].record(stream)
-        torch.cuda.synchronize()
-        # median of the per-call intervals: a host stall longer than the
-        # queue-holding spin would otherwise put idle time into one interval
-        q_ms = float(np.median([s.elapsed_time(e) for s, e in qe]))
+        q_ms = grouped_ms(lambda j: fs4.quantize(copies[j % len(copies)], out_row=qrow, out_col=qcol))
         q_gbs = quantizer_bytes(rows_q, cols_q) / (q_ms * 1e-3) / 1e9
-        hold_queue()
-        for j in range(qreps):
-            qe[j][0].record(stream)
-            fs4.quantize(copies[j % len(copies)], colwise=False, out_row=qrow)
-            qe[j][1].record(stream)
-        torch.cuda.synchronize()
-        r_ms = float(np.median([s.elapsed_time(e) for s, e in qe]))
+        r_ms = grouped_ms(lambda j: fs4.quantize(copies[j % len(copies)], colwise=False, out_row=qrow))
         r_bytes = quantizer_bytes(rows_q, cols_q, layouts=1)
         return {"workload": "4096x4096 bf16 ~N(0,1), 0.1% x50; row+col layouts",
                 "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
