@@ -237,23 +237,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
   __shared__ float tile[kTile][kTile + 1];
   __shared__ Tables tab;
   __shared__ uint32_t red[kThreads / 64];
-  // tensor scale from the amax partials (every workgroup reduces them itself)
-  float amax, clipv = 0.0f;
+  // The amax partials (every workgroup reduces them itself) are loaded first
+  // and the first two tiles' loads are issued behind them, so one memory round
+  // trip covers both; the tables are built while the tiles are in flight.
+  constexpr int kPrePart = 4;
+  uint32_t pm[kPrePart] = {};
+  float clipv = 0.0f;
   if constexpr (CLIP) {
     clipv = *clip;
-    amax = clipv;
   } else {
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < npart; i += kThreads) m = m > partials[i] ? m : partials[i];
-    m = block_max_u32(m, red);
-    amax = __builtin_bit_cast(float, m);
+#pragma unroll
+    for (int u = 0; u < kPrePart; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      pm[u] = partials[i < npart ? i : npart - 1];   // npart >= 1; a repeat leaves the max unchanged
+    }
   }
-  const float s_t = (float)((double)amax / kTensorDiv);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (ROW) *rv.tscale = s_t;
-    if (COL) *cv.tscale = s_t;
-  }
-  // the first two tiles' loads overlap the table construction
   const TileOrder order(rows, cols, upper_only);
   int sr, sc;
   order.start(sr, sc);
@@ -264,6 +262,23 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void *__restri
   TileRegs<BF16> g0, g1;
   tile_gload<BF16>(x, rows, cols, order.r0(sr), order.c0(sc), have != 0, g0);
   tile_gload<BF16>(x, rows, cols, order.r0(sr1), order.c0(sc1), have1 != 0, g1);
+  float amax;
+  if constexpr (CLIP) {
+    amax = clipv;
+  } else {
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < kPrePart; ++u) m = m > pm[u] ? m : pm[u];
+    for (int i = threadIdx.x + kPrePart * kThreads; i < npart; i += kThreads)
+      m = m > partials[i] ? m : partials[i];
+    m = block_max_u32(m, red);
+    amax = __builtin_bit_cast(float, m);
+  }
+  const float s_t = (float)((double)amax / kTensorDiv);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (ROW) *rv.tscale = s_t;
+    if (COL) *cv.tscale = s_t;
+  }
   build_tables_n<kThreads>(tab, s_t);
   // 1/(6 s_t) only seeds the scale-code estimate; the tables make it exact
   const float inv6st = s_t > 0.0f ? (float)(1.0 / (6.0 * (double)s_t)) : 0.0f;   // may be inf
@@ -337,6 +352,7 @@ fs4_status launch_quantize_encode(const void *x, fs4_dtype dt, int64_t rows, int
                                   const float *clip, bool upper_only) {
   const fs4_nvfp4 none = {nullptr, nullptr, nullptr, 0, 0};
   if (upper_only && (rows != cols || !rowwise || colwise || clip)) return FS4_ERR_ARG;
+  if (!clip && (!partials || npart < 1)) return FS4_ERR_ARG;
   const fs4_nvfp4 rv = rowwise ? *rowwise : none;
   // a square view's column blocks land at its mirrored row blocks: the same
   // addresses as in a column-wise view of the same shape
