@@ -161,6 +161,8 @@ __device__ inline void static_for(F &&f) {
 
 // Word 3 of a raw buffer resource: 32-bit data format (untyped dword access).
 constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer store: the non-temporal (streaming) bit.
+constexpr int kStoreNT = 2;
 
 // Direct global->LDS loads (gfx950 global_load_lds): lane l's 16 (or 4)
 // bytes from `src` land at LDS byte address `lds_dst + 16 l` (or + 4 l);
@@ -689,7 +691,10 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
         // register e in a scalar register and this lane's offset (rows 4h..,
         // column l32) in a vector register: no per-element address work.
         const int64_t base = (m0 + wm_u * TM * 32 + i * 32) * g.N + n0;
-        // (with Ct the record count is 0: the hardware drops these stores)
+        // (with Ct the record count is 0: the hardware drops these stores).
+        // C goes out with the non-temporal policy: an output of 100-268 MB
+        // would otherwise displace the operands that the kernels after it
+        // read from the caches.
         const int nrec = g.Ct ? 0 : (int)((g.M * g.N - base) * 4 < 0x7FFFFFFF ? (g.M * g.N - base) * 4 : 0x7FFFFFFF);
         const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(g.C + base, 0, nrec, kBufferWord3);
         const int loff = (4 * h * (int)g.N + wn * TN * 32 + j * 32 + l32) * 4;
@@ -699,7 +704,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_nt_kernel(GemmArgs g) {
           if (e_pipe) t[e] += g.beta_e * ebuf[q & 1][e];
           const float v = t[e];
           if (g.amax_parts) amax = fmaxf(amax, fabsf(v));
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, loff, soff, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, loff, soff, kStoreNT);
           vv[e] = v;
         }
       } else {
